@@ -1,0 +1,213 @@
+"""Plain fp64 definitions of the attention path (test infrastructure only).
+
+Every input is upcast exactly to fp64 (bf16 and fp32 values are representable)
+and every step is the textbook definition, written out:
+
+1. RoPE ("Llama 3.1 Architecture: Dense Scaling to 405B and 128K Context",
+   "Context Expansion ... RoPE Frequency Scaling", "1. High Base Frequency",
+   the theta_k equation): theta_k = base^(-2k/D) for k = 0 .. D/2-1, d being the
+   head dimension because the rotation acts on each head's vector. Each pair of
+   channels (2k, 2k+1) of a query or key at position m is rotated by the angle
+   m * theta_k. The pairing of adjacent channels follows RoFormer (Su et al.,
+   in the same page's references). Values are not rotated.
+2. Scores ("The Llama 3 Herd of Models", "A Deliberately Standard Dense
+   Transformer"): s_ij = <q_i, k_j> * scale with scale = 1/sqrt(D) unless given;
+   query head h reads KV head floor(h / g), g = Hq / Hkv (contiguous groups of
+   query heads share a KV head: "How Meta's Llama 3.1 405B Architecture
+   Actually Works", GQA paragraph).
+3. Mask: key j is visible to query i iff j <= i (decoder-only, causal) and both
+   lie in the same document, documents being the contiguous segments
+   [cu_docs[d], cu_docs[d+1]) of the packed sequence (the cross-document mask
+   of the same "Deliberately Standard Dense Transformer" entry).
+4. Exact softmax per row: m_i = max_j s_ij, p_ij = exp(s_ij - m_i) / l_i with
+   l_i = sum_j exp(s_ij - m_i); O_i = sum_j p_ij v_j, LSE_i = m_i + ln l_i.
+
+Rows are processed in blocks only to bound memory; each row's softmax is
+computed in one pass over all of its keys, and keys outside the union of the
+block's visible windows (which contribute exactly zero) are not materialised.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    """Exact upcast to a float64 numpy array (torch tensors or array-likes)."""
+    if hasattr(x, "detach"):  # torch.Tensor, without importing torch here
+        import torch
+        return x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def rope_frequencies(D: int, base: float = 500000.0) -> np.ndarray:
+    """theta_k = base^(-2k/D), k = 0 .. D/2-1, in fp64."""
+    k = np.arange(D // 2, dtype=np.float64)
+    return np.power(np.float64(base), -2.0 * k / np.float64(D))
+
+
+def rope(x, positions, base: float = 500000.0) -> np.ndarray:
+    """Rotate channel pairs (2k, 2k+1) of x [..., S, H, D] by positions * theta_k.
+
+    ``positions`` has the shape of x's leading dims up to S (e.g. [B, S]);
+    returns fp64 of x's shape.
+    """
+    x = _f64(x)
+    D = x.shape[-1]
+    pos = np.asarray(positions, dtype=np.float64)
+    angle = pos[..., None] * rope_frequencies(D, base)        # [..., S, D/2]
+    c = np.cos(angle)[..., None, :]                            # broadcast over H
+    s = np.sin(angle)[..., None, :]
+    even, odd = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = even * c - odd * s
+    out[..., 1::2] = even * s + odd * c
+    return out
+
+
+def document_of(cu_docs, S: int) -> np.ndarray:
+    """Document index of every token 0..S-1 for offsets cu_docs [n+1]."""
+    cu = np.asarray(cu_docs, dtype=np.int64)
+    return np.searchsorted(cu, np.arange(S), side="right") - 1
+
+
+def attention(qr, kr, v, cu_docs=None, scale: Optional[float] = None,
+              rows: Optional[Sequence[int]] = None,
+              block: int = 256) -> Tuple[np.ndarray, np.ndarray]:
+    """Masked GQA softmax attention on already-rotated queries and keys.
+
+    qr [B,S,Hq,D], kr and v [B,S,Hkv,D]. Returns O [B,R,Hq,D] and LSE [B,Hq,R]
+    in fp64, R = S or len(rows) (the query rows asked for, in that order).
+    """
+    qr, kr, v = _f64(qr), _f64(kr), _f64(v)
+    B, S, Hq, D = qr.shape
+    Hkv = kr.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    cu = np.asarray([0, S] if cu_docs is None else cu_docs, dtype=np.int64)
+    doc = document_of(cu, S)
+    start = cu[doc]                                            # first key of each row's document
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.size
+    O = np.zeros((B, R, Hq, D))
+    LSE = np.zeros((B, Hq, R))
+    for b in range(B):
+        for r0 in range(0, R, block):
+            ri = rows[r0:r0 + block]
+            lo, hi = int(start[ri].min()), int(ri.max()) + 1   # keys any of these rows may see
+            j = np.arange(lo, hi)
+            visible = (j[None, :] <= ri[:, None]) & (doc[j][None, :] == doc[ri][:, None])
+            for kv in range(Hkv):
+                heads = slice(kv * g, (kv + 1) * g)
+                q = qr[b, ri, heads, :]                        # [r, g, D]
+                n = q.shape[0]
+                s = (q.reshape(n * g, D) @ kr[b, lo:hi, kv, :].T).reshape(n, g, hi - lo) * scale
+                s = np.where(visible[:, None, :], s, -np.inf)
+                m = s.max(axis=2, keepdims=True)               # every row sees itself: finite
+                e = np.exp(s - m)
+                l = e.sum(axis=2, keepdims=True)
+                pv = (e.reshape(n * g, hi - lo) @ v[b, lo:hi, kv, :]).reshape(n, g, D)
+                O[b, r0:r0 + n, heads, :] = pv / l
+                LSE[b, heads, r0:r0 + n] = (m + np.log(l))[:, :, 0].T
+    return O, LSE
+
+
+def rope_attention(q, k, v, cu_docs=None, base: float = 500000.0, positions=None,
+                   scale: Optional[float] = None, rows=None) -> Tuple[np.ndarray, np.ndarray]:
+    """The whole prefill path: RoPE on Q and K at ``positions`` (default: the
+    token index), then masked GQA attention. Shapes as in ``attention``."""
+    q = _f64(q)
+    B, S = q.shape[:2]
+    if positions is None:
+        positions = np.broadcast_to(np.arange(S), (B, S))
+    return attention(rope(q, positions, base), rope(k, positions, base), v,
+                     cu_docs, scale, rows)
+
+
+def _decode_scores(qb, kb, scale):
+    # qb [g, D] (the g query heads of one KV head), kb [L, D] -> [g, L]
+    return (qb @ kb.T) * scale
+
+
+def decode(q_rot, k_cache, v_cache, seq_lens, scale: Optional[float] = None
+           ) -> Tuple[np.ndarray, np.ndarray]:
+    """One new token per sequence attending to its whole cache.
+
+    q_rot [B,Hq,D] is the new token's query, already rotated at position
+    L_b - 1; k_cache[b] / v_cache[b] are [Hkv, >= L_b, D] with rotated keys in
+    slots 0..L_b-1. Every cached token is visible (causal: all are earlier or
+    the token itself). Returns O [B,Hq,D] and LSE [B,Hq].
+    """
+    q_rot = _f64(q_rot)
+    B, Hq, D = q_rot.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    O = np.zeros((B, Hq, D))
+    LSE = np.zeros((B, Hq))
+    for b in range(B):
+        L = int(seq_lens[b])
+        kb, vb = _f64(k_cache[b]), _f64(v_cache[b])
+        Hkv = kb.shape[0]
+        g = Hq // Hkv
+        for kv in range(Hkv):
+            heads = slice(kv * g, (kv + 1) * g)
+            s = _decode_scores(q_rot[b, heads], kb[kv, :L], scale)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            l = e.sum(axis=1, keepdims=True)
+            O[b, heads] = (e @ vb[kv, :L]) / l
+            LSE[b, heads] = (m + np.log(l))[:, 0]
+    return O, LSE
+
+
+def decode_partials(q_rot, k_cache, v_cache, seq_lens, kv_chunk: int, max_splits: int,
+                    scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of each new token restricted to each chunk of its cache.
+
+    Split s of sequence b covers keys [s*kv_chunk, min((s+1)*kv_chunk, L_b)).
+    o_part [B,Hq,max_splits,D] is the softmax-weighted mean of V over the
+    split's keys and lse_part [B,Hq,max_splits] the log of the split's sum of
+    exp(scores). A split with no keys has o = 0 and lse = -inf.
+    """
+    q_rot = _f64(q_rot)
+    B, Hq, D = q_rot.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o_part = np.zeros((B, Hq, max_splits, D))
+    lse_part = np.full((B, Hq, max_splits), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        kb, vb = _f64(k_cache[b]), _f64(v_cache[b])
+        Hkv = kb.shape[0]
+        g = Hq // Hkv
+        for s_i in range(max_splits):
+            a, e_ = s_i * kv_chunk, min((s_i + 1) * kv_chunk, L)
+            if a >= e_:
+                continue
+            for kv in range(Hkv):
+                heads = slice(kv * g, (kv + 1) * g)
+                s = _decode_scores(q_rot[b, heads], kb[kv, a:e_], scale)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                l = e.sum(axis=1, keepdims=True)
+                o_part[b, heads, s_i] = (e @ vb[kv, a:e_]) / l
+                lse_part[b, heads, s_i] = (m + np.log(l))[:, 0]
+    return o_part, lse_part
+
+
+def combine(o_part, lse_part) -> Tuple[np.ndarray, np.ndarray]:
+    """Merge per-split results by their log-sum-exp weights.
+
+    With M = max_s lse_s and w_s = exp(lse_s - M) (w_s = 0 where lse_s = -inf),
+    O = sum_s w_s o_s / sum_s w_s and LSE = M + ln sum_s w_s. Inputs
+    [..., n_splits, D] and [..., n_splits]; at least one split must be finite.
+    """
+    o_part, lse_part = _f64(o_part), _f64(lse_part)
+    M = lse_part.max(axis=-1, keepdims=True)
+    w = np.exp(lse_part - M)                                   # exp(-inf) = 0
+    W = w.sum(axis=-1, keepdims=True)
+    O = (w[..., None] * o_part).sum(axis=-2) / W
+    return O, (M + np.log(W))[..., 0]

@@ -1,0 +1,107 @@
+"""Planted slips in the oracle (on the CPU) must each fail at least one pin.
+
+Each mutation swaps one function of ``oracle.reference`` for a plausibly wrong
+variant; the pin tests of ``test_oracle_pins`` are then run against it and at
+least one must raise. This shows the pins are tight enough to catch the slips
+they are meant for.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.reference as orc
+import test_oracle_pins as pins
+
+_real_attention = orc.attention
+_real_rope = orc.rope
+_real_freq = orc.rope_frequencies
+
+
+def _attention_variant(kv_map=None, strict=False, leak=False, scale_one=False, lse_no_max=False):
+    """A copy of the oracle's attention with one deliberate slip switched on."""
+    def attention(qr, kr, v, cu_docs=None, scale=None, rows=None, block=256):
+        qr, kr, v = orc._f64(qr), orc._f64(kr), orc._f64(v)
+        B, S, Hq, D = qr.shape
+        Hkv = kr.shape[2]
+        g = Hq // Hkv
+        sc = 1.0 if scale_one else (1.0 / math.sqrt(D) if scale is None else scale)
+        cu = np.asarray([0, S] if cu_docs is None else cu_docs)
+        doc = np.zeros(S, dtype=np.int64) if leak else orc.document_of(cu, S)
+        rows = np.arange(S) if rows is None else np.asarray(rows)
+        O = np.zeros((B, rows.size, Hq, D))
+        L = np.zeros((B, Hq, rows.size))
+        j = np.arange(S)
+        for b in range(B):
+            for n, i in enumerate(rows):
+                vis = ((j < i) if strict else (j <= i)) & (doc == doc[i])
+                for h in range(Hq):
+                    kv = kv_map(h, g, Hkv) if kv_map else h // g
+                    s = np.where(vis, kr[b, :, kv] @ qr[b, i, h] * sc, -np.inf)
+                    m = s.max()
+                    e = np.exp(s - m)
+                    O[b, n, h] = e @ v[b, :, kv] / e.sum()
+                    L[b, h, n] = (0.0 if lse_no_max else m) + np.log(e.sum())
+        return O, L
+    return attention
+
+
+def _rope_half_split(x, positions, base=500000.0):
+    x = orc._f64(x)
+    D = x.shape[-1]
+    ang = np.asarray(positions, dtype=np.float64)[..., None] * orc.rope_frequencies(D, base)
+    c, s = np.cos(ang)[..., None, :], np.sin(ang)[..., None, :]
+    a, b = x[..., :D // 2], x[..., D // 2:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def _rope_wrong_sign(x, positions, base=500000.0):
+    return _real_rope(x, -np.asarray(positions), base)
+
+
+MUTATIONS = {
+    "kv head h % Hkv": ("attention", _attention_variant(kv_map=lambda h, g, Hkv: h % Hkv)),
+    "strict causal j < i": ("attention", _attention_variant(strict=True)),
+    "mask leaks across documents": ("attention", _attention_variant(leak=True)),
+    "softmax scale dropped": ("attention", _attention_variant(scale_one=True)),
+    "LSE without the max": ("attention", _attention_variant(lse_no_max=True)),
+    "RoPE half-split pairs": ("rope", _rope_half_split),
+    "RoPE rotates backwards": ("rope", _rope_wrong_sign),
+    "theta uses k/D": ("rope_frequencies", lambda D, base=500000.0: _real_freq(2 * D, base)),
+    "theta uses d_model": ("rope_frequencies", lambda D, base=500000.0: _real_freq(128 * D, base)),
+}
+
+PIN_CALLS = [
+    lambda: pins.test_brute_force_equals_oracle(0, 13, 4, 2, 8, 3, False),
+    lambda: pins.test_brute_force_equals_oracle(3, 11, 6, 2, 8, 4, True),
+    lambda: pins.test_sdpa_library_route(4, 40, 8, 2, 16, 3),
+    pins.test_gqa_equals_mha_with_repeated_kv,
+    pins.test_document_mask_equals_separate_documents,
+    pins.test_scores_depend_only_on_offset,
+    pins.test_rope_unit_vectors_show_pairing_and_direction,
+    pins.test_rope_frequency_closed_forms,
+    pins.test_zero_query_gives_mean_of_visible_values_and_log_count,
+    pins.test_first_token_of_each_document_returns_its_value_row,
+    pins.test_two_key_document_is_a_logistic_mix,
+]
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_slip_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    caught = 0
+    for call in PIN_CALLS:
+        try:
+            call()
+        except (AssertionError, ValueError, FloatingPointError):
+            caught += 1
+    assert caught >= 1, f"no pin catches the slip: {name}"
+
+
+def test_unmutated_oracle_passes_every_pin_call():
+    assert orc.attention is _real_attention
+    for call in PIN_CALLS:
+        call()

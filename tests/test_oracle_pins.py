@@ -1,0 +1,255 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each check ties the oracle to brute force, to a library routine, or to an
+invariant / closed form the method fixes, so that a plausible slip (a dropped
+scale, a wrong sign in the rotation, the wrong channel pairing, h % Hkv instead
+of h // g, a strict instead of non-strict causal test, a mask leaking across
+documents, d_model instead of head_dim in theta_k) fails at least one of them.
+``test_oracle_mutations.py`` plants those slips and checks that they do.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute, reference as orc
+from workloads import draw_cu_docs, draw_positions, draw_prefill_inputs
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _tiny(seed=0, B=2, S=13, Hq=4, Hkv=2, D=8, dtype="fp32"):
+    q, k, v = draw_prefill_inputs(B, S, Hq, Hkv, D, dtype, seed)
+    return q, k, v
+
+
+# ---------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("seed,S,Hq,Hkv,D,ndocs,pos", [
+    (0, 13, 4, 2, 8, 3, False),
+    (1, 9, 4, 1, 6, 1, False),
+    (2, 16, 4, 4, 4, 2, True),
+    (3, 11, 6, 2, 8, 4, True),
+])
+def test_brute_force_equals_oracle(seed, S, Hq, Hkv, D, ndocs, pos):
+    q, k, v = _tiny(seed, 2, S, Hq, Hkv, D, "bf16")
+    cu = draw_cu_docs(S, seed, n_docs=ndocs)
+    positions = draw_positions(2, S, 131071, seed) if pos else None
+    O, L = orc.rope_attention(q, k, v, cu, 500000.0, positions)
+    qb, kb, vb = (x.double().numpy().tolist() for x in (q, k, v))
+    Ob, Lb = brute.brute_rope_attention(qb, kb, vb, cu.tolist(), 500000.0,
+                                        None if positions is None else positions.tolist())
+    np.testing.assert_allclose(O, np.array(Ob), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, np.array(Lb), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------- library routine
+
+def _torch_rope_complex(x, positions, base):
+    """RoPE as complex multiplication: (x_2k + i x_2k+1) * e^{i m theta_k}."""
+    x = x.double()
+    D = x.shape[-1]
+    inv_freq = 1.0 / (base ** (torch.arange(0, D, 2, dtype=torch.float64) / D))
+    ang = torch.as_tensor(positions, dtype=torch.float64)[..., None] * inv_freq
+    rot = torch.polar(torch.ones_like(ang), ang)[:, :, None, :]
+    xc = torch.view_as_complex(x.reshape(*x.shape[:-1], D // 2, 2).contiguous())
+    return torch.view_as_real(xc * rot).reshape(x.shape)
+
+
+@pytest.mark.parametrize("seed,S,Hq,Hkv,D,ndocs", [(4, 40, 8, 2, 16, 3), (5, 33, 16, 1, 32, 1),
+                                                    (6, 64, 4, 4, 64, 5)])
+def test_sdpa_library_route(seed, S, Hq, Hkv, D, ndocs):
+    B = 2
+    q, k, v = _tiny(seed, B, S, Hq, Hkv, D, "bf16")
+    cu = draw_cu_docs(S, seed, n_docs=ndocs)
+    positions = draw_positions(B, S, 100000, seed)
+    O, _ = orc.rope_attention(q, k, v, cu, 500000.0, positions)
+    g = Hq // Hkv
+    qr = _torch_rope_complex(q, positions, 500000.0).transpose(1, 2)            # [B,H,S,D]
+    kr = _torch_rope_complex(k, positions, 500000.0).repeat_interleave(g, dim=2).transpose(1, 2)
+    vv = v.double().repeat_interleave(g, dim=2).transpose(1, 2)
+    doc = torch.bucketize(torch.arange(S), torch.as_tensor(cu[1:-1]), right=True)
+    i = torch.arange(S)
+    mask = (i[None, :] <= i[:, None]) & (doc[None, :] == doc[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qr.contiguous(), kr.contiguous(), vv.contiguous(), attn_mask=mask)
+    np.testing.assert_allclose(O, ref.transpose(1, 2).numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_gqa_equals_mha_with_repeated_kv():
+    q, k, v = _tiny(7, 1, 24, 8, 2, 16, "bf16")
+    cu = np.array([0, 10, 24], dtype=np.int32)
+    O1, L1 = orc.rope_attention(q, k, v, cu)
+    O2, L2 = orc.rope_attention(q, k.repeat_interleave(4, dim=2), v.repeat_interleave(4, dim=2), cu)
+    np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(L1, L2, rtol=0, atol=1e-13)
+
+
+def test_document_mask_equals_separate_documents():
+    S = 50
+    q, k, v = _tiny(8, 1, S, 8, 2, 16, "bf16")
+    cu = np.array([0, 1, 17, 18, 41, 50], dtype=np.int32)     # includes length-1 documents
+    O, L = orc.rope_attention(q, k, v, cu)
+    for a, b in zip(cu[:-1], cu[1:]):
+        # each document alone, positions restarted at 0 (relative-offset property)
+        Od, Ld = orc.rope_attention(q[:, a:b], k[:, a:b], v[:, a:b])
+        np.testing.assert_allclose(O[:, a:b], Od, rtol=0, atol=1e-10)
+        np.testing.assert_allclose(L[:, :, a:b], Ld, rtol=0, atol=1e-10)
+
+
+def test_scores_depend_only_on_offset():
+    q, k, v = _tiny(9, 1, 20, 4, 2, 32, "fp32")
+    base_pos = np.arange(20)[None, :]
+    O0, L0 = orc.rope_attention(q, k, v, None, 500000.0, base_pos)
+    for shift in (1, 777, 123456):
+        O1, L1 = orc.rope_attention(q, k, v, None, 500000.0, base_pos + shift)
+        np.testing.assert_allclose(O1, O0, rtol=0, atol=1e-10)
+        np.testing.assert_allclose(L1, L0, rtol=0, atol=1e-10)
+
+
+def test_rope_position_zero_is_identity_and_norms_preserved():
+    x = torch.randn(1, 5, 3, 16, generator=torch.Generator().manual_seed(3), dtype=torch.float64)
+    r0 = orc.rope(x, np.zeros((1, 5)), 500000.0)
+    assert np.array_equal(r0, x.numpy())
+    r = orc.rope(x, np.array([[1, 10, 1000, 65536, 131071]]), 500000.0)
+    pairs = lambda a: np.hypot(a[..., 0::2], a[..., 1::2])
+    np.testing.assert_allclose(pairs(r), pairs(x.numpy()), rtol=1e-14, atol=0)
+
+
+def test_rope_unit_vectors_show_pairing_and_direction():
+    """e_{2k} at position m rotates to (cos m theta_k, sin m theta_k) in channels
+    (2k, 2k+1); e_{2k+1} to (-sin, cos). Channels of other pairs stay 0."""
+    D, m = 8, 3
+    theta = [1.0, 500000.0 ** -0.25, 500000.0 ** -0.5, 500000.0 ** -0.75]  # base^(-2k/8)
+    for kk in range(D // 2):
+        for which in (0, 1):
+            x = np.zeros((1, 1, 1, D))
+            x[..., 2 * kk + which] = 1.0
+            r = orc.rope(x, np.array([[m]]), 500000.0)[0, 0, 0]
+            c, s = math.cos(m * theta[kk]), math.sin(m * theta[kk])
+            want = np.zeros(D)
+            want[2 * kk], want[2 * kk + 1] = (c, s) if which == 0 else (-s, c)
+            np.testing.assert_allclose(r, want, rtol=0, atol=1e-15)
+
+
+def test_rope_frequency_closed_forms():
+    for D in (64, 128):
+        th = orc.rope_frequencies(D, 500000.0)
+        assert th.shape == (D // 2,)
+        assert th[0] == 1.0
+        assert th[D // 4] == pytest.approx(1.0 / math.sqrt(500000.0), rel=1e-15)
+        ratios = th[1:] / th[:-1]                                # geometric progression
+        np.testing.assert_allclose(ratios, 500000.0 ** (-2.0 / D), rtol=1e-14)
+        # slowest band, against the same power written as exp(-(D-2)/D * ln base)
+        assert th[-1] == pytest.approx(math.exp(-(D - 2) / D * math.log(500000.0)), rel=1e-14)
+
+
+# -------------------------------------------------------------- closed forms
+
+def test_zero_query_gives_mean_of_visible_values_and_log_count():
+    S = 30
+    _, k, v = _tiny(10, 1, S, 4, 2, 8, "bf16")
+    q = torch.zeros(1, S, 4, 8)
+    cu = np.array([0, 7, 8, 30], dtype=np.int32)
+    O, L = orc.rope_attention(q, k, v, cu)
+    vv = v.double().numpy()
+    for i in range(S):
+        a = cu[np.searchsorted(cu, i, side="right") - 1]
+        n = i - a + 1
+        for h in range(4):
+            np.testing.assert_allclose(O[0, i, h], vv[0, a:i + 1, h // 2].mean(axis=0), atol=1e-14)
+            assert L[0, h, i] == pytest.approx(math.log(n), abs=1e-14)
+
+
+def test_first_token_of_each_document_returns_its_value_row():
+    q, k, v = _tiny(11, 1, 40, 8, 2, 16, "bf16")
+    cu = np.array([0, 5, 6, 23, 40], dtype=np.int32)
+    O, _ = orc.rope_attention(q, k, v, cu)
+    for a in cu[:-1]:
+        for h in range(8):
+            assert np.array_equal(O[0, a, h], v[0, a, h // 4].double().numpy())
+
+
+def test_constant_values_give_constant_output():
+    q, k, _ = _tiny(12, 1, 25, 4, 1, 8, "bf16")
+    v = torch.full((1, 25, 1, 8), 0.375)
+    O, _ = orc.rope_attention(q, k, v, np.array([0, 12, 25]))
+    np.testing.assert_allclose(O, 0.375, rtol=0, atol=1e-15)
+
+
+def test_two_key_document_is_a_logistic_mix():
+    """Row 1 of a 2-token document: O = (v0 + e^{s1-s0} v1) / (1 + e^{s1-s0})."""
+    D = 2
+    q = torch.tensor([[[[0.3, -0.2]], [[0.7, 0.4]]]], dtype=torch.float64)
+    k = torch.tensor([[[[1.1, 0.5]], [[-0.6, 0.9]]]], dtype=torch.float64)
+    v = torch.tensor([[[[2.0, -1.0]], [[0.5, 3.0]]]], dtype=torch.float64)
+    O, L = orc.rope_attention(q, k, v, None, 500000.0)
+    # D = 2: one band, theta_0 = 1; position 0 unrotated, position 1 rotated by 1 rad
+    c, s = math.cos(1.0), math.sin(1.0)
+    q1 = (0.7 * c - 0.4 * s, 0.7 * s + 0.4 * c)
+    k1 = (-0.6 * c - 0.9 * s, -0.6 * s + 0.9 * c)
+    s0 = (q1[0] * 1.1 + q1[1] * 0.5) / math.sqrt(D)
+    s1 = (q1[0] * k1[0] + q1[1] * k1[1]) / math.sqrt(D)
+    w = 1.0 / (1.0 + math.exp(s0 - s1))                          # weight of key 1
+    np.testing.assert_allclose(O[0, 1, 0], [(1 - w) * 2.0 + w * 0.5, (1 - w) * -1.0 + w * 3.0],
+                               atol=1e-15)
+    assert L[0, 0, 1] == pytest.approx(math.log(math.exp(s0) + math.exp(s1)), abs=1e-14)
+
+
+# -------------------------------------------------------------------- decode
+
+def _decode_case(seed, B=3, Hq=8, Hkv=2, D=16, lens=(5, 17, 40)):
+    gen = torch.Generator().manual_seed(seed)
+    lens = np.array(lens, dtype=np.int32)
+    k_raw = [torch.randn(Hkv, L, D, generator=gen).bfloat16() for L in lens]
+    v = [torch.randn(Hkv, L, D, generator=gen).bfloat16() for L in lens]
+    q_raw = torch.randn(B, Hq, D, generator=gen).bfloat16()
+    return q_raw, k_raw, v, lens
+
+
+def test_decode_equals_last_row_of_prefill():
+    q_raw, k_raw, v, lens = _decode_case(13)
+    B, Hq, D = q_raw.shape
+    k_rot = [orc.rope(kb.transpose(0, 1)[None], np.arange(kb.shape[1])[None])[0].transpose(1, 0, 2)
+             for kb in k_raw]
+    q_rot = np.stack([orc.rope(q_raw[b][None, None], np.array([[lens[b] - 1]]))[0, 0] for b in range(B)])
+    O, L = orc.decode(q_rot, k_rot, v, lens)
+    for b in range(B):
+        n = int(lens[b])
+        # a prefill of n tokens whose last query is the new token
+        qp = torch.zeros(1, n, Hq, D, dtype=torch.float64)
+        qp[0, -1] = q_raw[b].double()
+        kp = k_raw[b].transpose(0, 1)[None].double()
+        vp = v[b].transpose(0, 1)[None].double()
+        Op, Lp = orc.rope_attention(qp, kp, vp, None, 500000.0, rows=[n - 1])
+        np.testing.assert_allclose(O[b], Op[0, 0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L[b], Lp[0, :, 0], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("chunk,max_splits", [(1, 40), (4, 12), (7, 6), (16, 8), (40, 1), (64, 3)])
+def test_split_partials_combine_to_unsplit_result(chunk, max_splits):
+    q_raw, k_raw, v, lens = _decode_case(14)
+    q = q_raw.double().numpy()
+    O, L = orc.decode(q, k_raw, v, lens)
+    op, lp = orc.decode_partials(q, k_raw, v, lens, chunk, max_splits)
+    # empty trailing splits are -inf / 0
+    for b, n in enumerate(lens):
+        used = -(-int(n) // chunk)
+        assert np.all(np.isneginf(lp[b, :, used:])) and np.all(op[b, :, used:] == 0)
+        assert np.all(np.isfinite(lp[b, :, :used]))
+    Oc, Lc = orc.combine(op, lp)
+    np.testing.assert_allclose(Oc, O, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(Lc, L, rtol=0, atol=1e-12)
+
+
+def test_single_split_partial_equals_decode():
+    q_raw, k_raw, v, lens = _decode_case(15)
+    q = q_raw.double().numpy()
+    O, L = orc.decode(q, k_raw, v, lens)
+    op, lp = orc.decode_partials(q, k_raw, v, lens, 64, 1)
+    np.testing.assert_allclose(op[:, :, 0], O, atol=1e-13)
+    np.testing.assert_allclose(lp[:, :, 0], L, atol=1e-13)

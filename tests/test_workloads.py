@@ -1,0 +1,62 @@
+"""The seeded input rules (CPU only)."""
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import (CONFIGS, draw_cu_docs, draw_decode_inputs, draw_prefill_inputs,
+                       draw_seq_lens, sample_rows)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama8b", "llama405b", "long128k"])
+def test_document_offsets_are_valid_and_seeded(name):
+    w = CONFIGS[name]
+    cu = draw_cu_docs(w.S, w.seed, w.n_docs, w.n_docs_max)
+    assert cu.dtype == np.int32 and cu[0] == 0 and cu[-1] == w.S
+    assert np.all(np.diff(cu) >= 1)
+    n = cu.size - 1
+    if w.n_docs is not None:
+        assert n == w.n_docs
+    else:
+        assert 1 <= n <= w.n_docs_max
+    assert np.array_equal(cu, draw_cu_docs(w.S, w.seed, w.n_docs, w.n_docs_max))
+
+
+def test_document_count_draw_covers_its_range():
+    counts = {draw_cu_docs(1000, s, None, 8).size - 1 for s in range(200)}
+    assert counts == set(range(1, 9))
+
+
+def test_seq_lens_inclusive_range():
+    w = CONFIGS["decode405b"]
+    L = draw_seq_lens(w.B, w.len_lo, w.len_hi, w.seed)
+    assert L.shape == (16,) and L.dtype == np.int32
+    assert L.min() >= 4096 and L.max() <= 131072
+    many = draw_seq_lens(100000, 3, 5, 0)
+    assert set(np.unique(many)) == {3, 4, 5}
+
+
+def test_prefill_draws_are_seeded_normal_and_cast():
+    q, k, v = draw_prefill_inputs(1, 64, 8, 2, 64, "bf16", 3)
+    assert q.dtype == torch.bfloat16 and k.shape == (1, 64, 2, 64)
+    q2, _, _ = draw_prefill_inputs(1, 64, 8, 2, 64, "bf16", 3)
+    assert torch.equal(q, q2)
+    x = torch.cat([q.flatten(), k.flatten(), v.flatten()]).float()
+    assert abs(x.mean().item()) < 0.05 and abs(x.std().item() - 1) < 0.05
+    qf, _, _ = draw_prefill_inputs(1, 64, 8, 2, 64, "fp32", 3)
+    assert torch.equal(qf.bfloat16(), q)        # bf16 is the RNE cast of the same draws
+
+
+def test_decode_draws():
+    L = np.array([3, 7], dtype=np.int32)
+    q, ks, vs = draw_decode_inputs(2, 8, 2, 16, L, "bf16", 1)
+    assert q.shape == (2, 8, 16) and [x.shape for x in ks] == [(2, 3, 16), (2, 7, 16)]
+    assert [x.shape for x in vs] == [(2, 3, 16), (2, 7, 16)]
+
+
+def test_sample_rows_contains_document_edges():
+    cu = np.array([0, 5, 300, 1000])
+    r = sample_rows(1000, cu, 0, n_random=50, tile=64)
+    for x in (0, 4, 5, 299, 300, 999, 63, 64, 127, 128):
+        assert x in r
+    assert np.all(np.diff(r) > 0) and r.min() >= 0 and r.max() < 1000
