@@ -1,0 +1,160 @@
+"""Python binding of the gfx950 GQA + RoPE attention library.
+
+The four calls mirror the C ABI in ``include/llama_attn.h`` one to one and only
+marshal arguments: tensor pointers, element strides, sizes and the current HIP
+stream. Every step of the computation runs in the library's HIP kernels;
+PyTorch provides device memory and streams. Tensors must live on the GPU.
+
+Shapes (strides are taken from the tensors; the last dimension must be
+contiguous):
+
+* ``rope_qk(q_in, q_out, k_in, k_out, positions=None, rope_base=500000.0)``:
+  q [B,S,Hq,D], k [B,S,Hkv,D] (either pair may be None); positions int32 [B,S].
+* ``gqa_prefill(q, k, v, o, lse=None, cu_docs=None, softmax_scale=0.0)``:
+  q/o [B,S,Hq,D], k/v [B,S,Hkv,D], cu_docs int32 [B, n_docs+1], lse fp32 [B,Hq,S].
+* ``gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk, o_part, lse_part,
+  softmax_scale=0.0)``: q [B,Hq,D], caches [B,Hkv,Lmax,D], seq_lens int32 [B],
+  o_part fp32 [B,Hq,max_splits,D], lse_part fp32 [B,Hq,max_splits].
+* ``gqa_decode_combine(o_part, lse_part, seq_lens, kv_chunk, o, lse=None)``:
+  o [B,Hq,D] (bf16 or fp32), lse fp32 [B,Hq].
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+__all__ = ["LlamaAttnError", "rope_qk", "gqa_prefill", "gqa_decode", "gqa_decode_combine",
+           "version", "LA_BF16", "LA_FP32"]
+
+LA_BF16, LA_FP32 = 0, 1
+_DT = {torch.bfloat16: LA_BF16, torch.float32: LA_FP32}
+
+
+class LlamaAttnError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        msg = _lib.load().la_status_str(status).decode()
+        super().__init__(f"{call}: {msg} (status {status})")
+
+
+def version() -> int:
+    return _lib.load().la_version()
+
+
+def _check(status: int, call: str) -> None:
+    if status != 0:
+        raise LlamaAttnError(status, call)
+
+
+def _dev(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("llama_attn tensors must be torch tensors on the GPU")
+    return t.data_ptr()
+
+
+def _i32(t):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError("index tensors (positions, cu_docs, seq_lens) must be contiguous int32")
+    return _dev(t)
+
+
+def _f32c(t):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError("lse / split workspaces must be contiguous float32")
+    return _dev(t)
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype(t) -> int:
+    if t.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _strides(t, n):
+    if t is None:
+        return None
+    if t.stride(-1) != 1:
+        raise ValueError("the last (head_dim) dimension must be contiguous")
+    return _lib.i64_array(t.stride()[:n])
+
+
+def _same_shape(call, *pairs):
+    for a, b in pairs:
+        if a is not None and b is not None and tuple(a.shape) != tuple(b.shape):
+            raise ValueError(f"{call}: shape mismatch {tuple(a.shape)} vs {tuple(b.shape)}")
+
+
+def rope_qk(q_in, q_out, k_in=None, k_out=None, positions=None, rope_base: float = 500000.0):
+    ref = q_in if q_in is not None else k_in
+    B, S, _, D = ref.shape
+    Hq = q_in.shape[2] if q_in is not None else 0
+    Hkv = k_in.shape[2] if k_in is not None else 0
+    _same_shape("rope_qk", (q_in, q_out), (k_in, k_out))
+    if q_in is not None and k_in is not None and (k_in.shape[:2] != q_in.shape[:2] or k_in.shape[3] != D):
+        raise ValueError("rope_qk: q and k must share B, S and D")
+    if positions is not None and tuple(positions.shape) != (B, S):
+        raise ValueError("rope_qk: positions must be [B, S]")
+    st = _lib.load().rope_qk(
+        _dev(q_in), _dev(q_out), _strides(q_in, 3), _strides(q_out, 3),
+        _dev(k_in), _dev(k_out), _strides(k_in, 3), _strides(k_out, 3),
+        _dtype(ref), B, S, Hq, Hkv, D, _i32(positions), float(rope_base), _stream())
+    _check(st, "rope_qk")
+
+
+def gqa_prefill(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float = 0.0):
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    n_docs = cu_docs.shape[-1] - 1 if cu_docs is not None else 1
+    _same_shape("gqa_prefill", (q, o), (k, v))
+    if tuple(k.shape) != (B, S, Hkv, D):
+        raise ValueError("gqa_prefill: k/v must be [B, S, Hkv, D]")
+    if lse is not None and tuple(lse.shape) != (B, Hq, S):
+        raise ValueError("gqa_prefill: lse must be [B, Hq, S]")
+    if cu_docs is not None and (cu_docs.dim() != 2 or cu_docs.shape[0] != B):
+        raise ValueError("gqa_prefill: cu_docs must be [B, n_docs + 1]")
+    st = _lib.load().gqa_prefill(
+        _dev(q), _dev(k), _dev(v), _dev(o), _f32c(lse), _dtype(q), B, S, Hq, Hkv, D,
+        _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
+        _i32(cu_docs), n_docs, float(softmax_scale), _stream())
+    _check(st, "gqa_prefill")
+
+
+def gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk: int, o_part, lse_part,
+               softmax_scale: float = 0.0):
+    B, Hq, D = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must share strides")
+    max_splits = o_part.shape[2]
+    _same_shape("gqa_decode", (k_cache, v_cache))
+    if k_cache.shape[0] != B or k_cache.shape[3] != D or tuple(o_part.shape) != (B, Hq, max_splits, D) \
+            or tuple(lse_part.shape) != (B, Hq, max_splits) or tuple(seq_lens.shape) != (B,):
+        raise ValueError("gqa_decode: inconsistent shapes")
+    st = _lib.load().gqa_decode(
+        _dev(q), _strides(q, 2), _dev(k_cache), _dev(v_cache), _strides(k_cache, 3),
+        _i32(seq_lens), B, Hq, Hkv, D, Lmax, int(kv_chunk), max_splits, float(softmax_scale),
+        _f32c(o_part), _f32c(lse_part), _stream())
+    _check(st, "gqa_decode")
+
+
+def gqa_decode_combine(o_part, lse_part, seq_lens, kv_chunk: int, o, lse=None):
+    B, Hq, max_splits, D = o_part.shape
+    if tuple(lse_part.shape) != (B, Hq, max_splits) or tuple(o.shape) != (B, Hq, D) \
+            or tuple(seq_lens.shape) != (B,) or (lse is not None and tuple(lse.shape) != (B, Hq)):
+        raise ValueError("gqa_decode_combine: inconsistent shapes")
+    st = _lib.load().gqa_decode_combine(
+        _f32c(o_part), _f32c(lse_part), _i32(seq_lens), B, Hq, D, int(kv_chunk), max_splits,
+        _dev(o), _strides(o, 2), _f32c(lse), _dtype(o), _stream())
+    _check(st, "gqa_decode_combine")

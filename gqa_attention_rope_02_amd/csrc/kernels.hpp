@@ -1,0 +1,72 @@
+// Internal interface between the C-ABI host code and the kernel translation
+// units: argument blocks and launchers. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+struct RopeArgs {
+  const void* in;
+  void* out;
+  int64_t is_b, is_s, is_h;   // input strides (elements)
+  int64_t os_b, os_s, os_h;   // output strides
+  int H;                      // heads of this tensor
+  const int32_t* positions;   // [B, S] or null
+  int B, S;
+  double base;
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;                 // [B, Hq, S] or null
+  int64_t qs_b, qs_s, qs_h;
+  int64_t ks_b, ks_s, ks_h;
+  int64_t vs_b, vs_s, vs_h;
+  int64_t os_b, os_s, os_h;
+  const int32_t* cu_docs;     // [B, n_docs + 1] or null
+  int n_docs;
+  int B, S, Hq, Hkv;
+  int n_qtiles;               // ceil(S / tokens per workgroup)
+  float scale_log2;           // softmax scale * log2(e)
+  float scale;                // softmax scale
+};
+
+struct DecodeArgs {
+  const void* q;
+  int64_t qs_b, qs_h;
+  const void* k;
+  const void* v;
+  int64_t cs_b, cs_h, cs_l;
+  const int32_t* seq_lens;
+  int B, Hq, Hkv, Lmax, kv_chunk, max_splits;
+  float scale_log2;
+  float scale;
+  float* o_part;              // [B, Hq, max_splits, D]
+  float* lse_part;            // [B, Hq, max_splits]
+};
+
+struct CombineArgs {
+  const float* o_part;
+  const float* lse_part;
+  const int32_t* seq_lens;
+  int B, Hq, kv_chunk, max_splits;
+  void* o;
+  int64_t os_b, os_h;
+  float* lse;                 // [B, Hq] or null
+};
+
+// Launchers: return hipSuccess or the launch error. dt: 0 = bf16, 1 = fp32.
+hipError_t launch_rope_pair(const RopeArgs& q, const RopeArgs& k, int D, int dt, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, int D, int G, int dt, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int D, int G, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& a, int D, int dt, hipStream_t st);
+
+// Tokens of one sequence handled by one prefill workgroup for group size G.
+constexpr int prefill_tokens_per_block(int G) { return 256 / G; }
+
+}  // namespace la

@@ -1,0 +1,174 @@
+// Host side of the C ABI declared in include/llama_attn.h: argument checks
+// (all made before anything is enqueued), variant selection, and launches on
+// the caller's stream. The library allocates nothing and keeps no state.
+#include "llama_attn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool supported_d(int D) { return D == 64 || D == 128; }
+bool supported_g(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
+int elem_size(la_dtype dt) { return dt == LA_BF16 ? 2 : 4; }
+bool known_dtype(la_dtype dt) { return dt == LA_BF16 || dt == LA_FP32; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Strides must be non-negative multiples of 16 bytes' worth of elements.
+bool strides_ok(const int64_t* s, int n, int esize) {
+  if (s == nullptr) return false;
+  const int64_t q = 16 / esize;
+  for (int i = 0; i < n; ++i)
+    if (s[i] < 0 || s[i] % q != 0) return false;
+  return true;
+}
+
+la_status launched(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* la_status_str(la_status s) {
+  switch (s) {
+    case LA_OK: return "ok";
+    case LA_ERR_INVALID_ARG: return "invalid argument";
+    case LA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case LA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int la_version(void) { return kVersion; }
+
+la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
+                  const int64_t q_out_strides[3], const void* k_in, void* k_out,
+                  const int64_t k_in_strides[3], const int64_t k_out_strides[3], la_dtype dt,
+                  int B, int S, int Hq, int Hkv, int D, const int32_t* positions,
+                  double rope_base, hipStream_t stream) {
+  if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
+  const bool has_q = q_in != nullptr || q_out != nullptr;
+  const bool has_k = k_in != nullptr || k_out != nullptr;
+  if (!has_q && !has_k) return LA_ERR_INVALID_ARG;
+  if (has_q && (q_in == nullptr || q_out == nullptr)) return LA_ERR_INVALID_ARG;
+  if (has_k && (k_in == nullptr || k_out == nullptr)) return LA_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || (has_q && Hq < 1) || (has_k && Hkv < 1)) return LA_ERR_INVALID_ARG;
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
+  if ((long long)B * S > 0x7fffffffLL) return LA_ERR_INVALID_ARG;
+  if (!supported_d(D)) return LA_ERR_UNSUPPORTED;
+  const int es = elem_size(dt);
+  if (has_q && (!aligned16(q_in) || !aligned16(q_out) || !strides_ok(q_in_strides, 3, es) ||
+                !strides_ok(q_out_strides, 3, es)))
+    return LA_ERR_INVALID_ARG;
+  if (has_k && (!aligned16(k_in) || !aligned16(k_out) || !strides_ok(k_in_strides, 3, es) ||
+                !strides_ok(k_out_strides, 3, es)))
+    return LA_ERR_INVALID_ARG;
+
+  la::RopeArgs qa{}, ka{};
+  if (has_q) {
+    qa = la::RopeArgs{q_in, q_out, q_in_strides[0], q_in_strides[1], q_in_strides[2],
+                      q_out_strides[0], q_out_strides[1], q_out_strides[2], Hq, positions, B, S,
+                      rope_base};
+  }
+  if (has_k) {
+    ka = la::RopeArgs{k_in, k_out, k_in_strides[0], k_in_strides[1], k_in_strides[2],
+                      k_out_strides[0], k_out_strides[1], k_out_strides[2], Hkv, positions, B, S,
+                      rope_base};
+  }
+  return launched(la::launch_rope_pair(qa, ka, D, dt == LA_BF16 ? 0 : 1, stream));
+}
+
+la_status gqa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                      la_dtype dt, int B, int S, int Hq, int Hkv, int D,
+                      const int64_t q_strides[3], const int64_t k_strides[3],
+                      const int64_t v_strides[3], const int64_t o_strides[3],
+                      const int32_t* cu_docs, int n_docs, float softmax_scale,
+                      hipStream_t stream) {
+  if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o) return LA_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return LA_ERR_INVALID_ARG;
+  if (cu_docs && n_docs < 1) return LA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return LA_ERR_INVALID_ARG;
+  if (!supported_d(D) || !supported_g(Hq / Hkv)) return LA_ERR_UNSUPPORTED;
+  const int es = elem_size(dt);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_INVALID_ARG;
+  if (!strides_ok(q_strides, 3, es) || !strides_ok(k_strides, 3, es) ||
+      !strides_ok(v_strides, 3, es) || !strides_ok(o_strides, 3, es))
+    return LA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return LA_ERR_INVALID_ARG;
+  const int G = Hq / Hkv;
+  const int tq = la::prefill_tokens_per_block(G);
+  const long long n_qtiles = (S + tq - 1) / tq;
+  if ((long long)B * Hkv * n_qtiles > 0x7fffffffLL) return LA_ERR_INVALID_ARG;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+
+  la::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.qs_b = q_strides[0]; a.qs_s = q_strides[1]; a.qs_h = q_strides[2];
+  a.ks_b = k_strides[0]; a.ks_s = k_strides[1]; a.ks_h = k_strides[2];
+  a.vs_b = v_strides[0]; a.vs_s = v_strides[1]; a.vs_h = v_strides[2];
+  a.os_b = o_strides[0]; a.os_s = o_strides[1]; a.os_h = o_strides[2];
+  a.cu_docs = cu_docs; a.n_docs = cu_docs ? n_docs : 1;
+  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv;
+  a.n_qtiles = (int)n_qtiles;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launched(la::launch_prefill(a, D, G, dt == LA_BF16 ? 0 : 1, stream));
+}
+
+la_status gqa_decode(const void* q, const int64_t q_strides[2], const void* k_cache,
+                     const void* v_cache, const int64_t cache_strides[3],
+                     const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int Lmax,
+                     int kv_chunk, int max_splits, float softmax_scale, float* o_part,
+                     float* lse_part, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !o_part || !lse_part) return LA_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lmax < 1 || max_splits < 1) return LA_ERR_INVALID_ARG;
+  if (kv_chunk < 64 || kv_chunk % 64 != 0) return LA_ERR_INVALID_ARG;
+  if ((long long)max_splits * kv_chunk < Lmax) return LA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return LA_ERR_INVALID_ARG;
+  if (!supported_d(D) || !supported_g(Hq / Hkv)) return LA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part))
+    return LA_ERR_INVALID_ARG;
+  if (!strides_ok(q_strides, 2, 2) || !strides_ok(cache_strides, 3, 2)) return LA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return LA_ERR_INVALID_ARG;
+  if ((long long)B * Hkv * max_splits > 0x7fffffffLL) return LA_ERR_INVALID_ARG;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+
+  la::DecodeArgs a{};
+  a.q = q; a.qs_b = q_strides[0]; a.qs_h = q_strides[1];
+  a.k = k_cache; a.v = v_cache;
+  a.cs_b = cache_strides[0]; a.cs_h = cache_strides[1]; a.cs_l = cache_strides[2];
+  a.seq_lens = seq_lens;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lmax = Lmax; a.kv_chunk = kv_chunk; a.max_splits = max_splits;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o_part = o_part; a.lse_part = lse_part;
+  return launched(la::launch_decode(a, D, Hq / Hkv, stream));
+}
+
+la_status gqa_decode_combine(const float* o_part, const float* lse_part, const int32_t* seq_lens,
+                             int B, int Hq, int D, int kv_chunk, int max_splits, void* o,
+                             const int64_t o_strides[2], float* lse, la_dtype dt,
+                             hipStream_t stream) {
+  if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
+  if (!o_part || !lse_part || !seq_lens || !o) return LA_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || max_splits < 1) return LA_ERR_INVALID_ARG;
+  if (kv_chunk < 64 || kv_chunk % 64 != 0) return LA_ERR_INVALID_ARG;
+  if (!supported_d(D)) return LA_ERR_UNSUPPORTED;
+  if (!o_strides || o_strides[0] < 0 || o_strides[1] < 0) return LA_ERR_INVALID_ARG;
+  if ((long long)B * Hq > 0x7fffffffLL - 3) return LA_ERR_INVALID_ARG;
+
+  la::CombineArgs a{};
+  a.o_part = o_part; a.lse_part = lse_part; a.seq_lens = seq_lens;
+  a.B = B; a.Hq = Hq; a.kv_chunk = kv_chunk; a.max_splits = max_splits;
+  a.o = o; a.os_b = o_strides[0]; a.os_h = o_strides[1];
+  a.lse = lse;
+  return launched(la::launch_combine(a, D, dt == LA_BF16 ? 0 : 1, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,163 @@
+/*
+ * llama_attn.h — C ABI of a gfx950 (MI355X) library for the attention step of
+ * the Llama 3.1 dense decoder: rotary position embeddings on queries and keys,
+ * then grouped-query causal self-attention under the cross-document mask, for
+ * prefill (many tokens) and for decode over a KV cache.
+ *
+ * What the calls compute comes from these web pages:
+ *   [P1] "Llama 3.1 Architecture: Dense Scaling to 405B and 128K Context",
+ *        section "Context Expansion: From 8K to 128K via RoPE Frequency
+ *        Scaling", subsection "1. High Base Frequency" (the theta_k equation),
+ *        and the "Architectural Deep Dive" flowchart (128 query heads on 8 KV
+ *        heads, 16:1);
+ *   [P2] "How Meta's Llama 3.1 405B Architecture Actually Works", the GQA
+ *        paragraph (query heads grouped onto a shared key/value head, which
+ *        shrinks the KV cache during decoding);
+ *   [P4] "The Llama 3 Herd of Models", Chapter Roadmap entry "A Deliberately
+ *        Standard Dense Transformer" (GQA with 8 KV heads, RoPE base 500,000,
+ *        cross-document attention mask).
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer on the current HIP device; the
+ *     caller allocates and frees all memory (including the decode workspace).
+ *     The library allocates nothing and keeps no pointer after returning.
+ *   - Strides are in ELEMENTS. The innermost (head_dim) stride is always 1.
+ *     Base pointers must be 16-byte aligned and every stride a multiple of
+ *     16 bytes' worth of elements (8 for bf16, 4 for fp32).
+ *   - All work is enqueued on `stream` (0 = the null stream) and is
+ *     asynchronous: no call synchronises.
+ *   - All argument checks are made on the host before anything is enqueued;
+ *     on any error nothing is launched. Device-resident CONTENTS (document
+ *     offsets, sequence lengths, positions) are the caller's contract and are
+ *     not read on the host.
+ *   - Head mapping: query head h reads KV head h / (Hq / Hkv) (contiguous
+ *     groups) [P2, P4].
+ *   - RoPE pairs adjacent channels (2k, 2k+1) and rotates them by the angle
+ *     position * theta_k, theta_k = rope_base^(-2k/D), k = 0..D/2-1 [P1].
+ *   - Supported: D in {64, 128}; Hq / Hkv in {1, 2, 4, 8, 16}.
+ */
+#ifndef LLAMA_ATTN_H
+#define LLAMA_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, stride or alignment */
+  LA_ERR_UNSUPPORTED = 2,   /* a shape or dtype this library has no kernel for */
+  LA_ERR_LAUNCH = 3         /* the HIP runtime refused the launch */
+} la_status;
+
+typedef enum { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* la_status_str(la_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int la_version(void);
+
+/*
+ * rope_qk — rotary position embedding of queries and keys [P1].
+ *
+ * q_in/q_out: [B, S, Hq, D] with strides q_in_strides / q_out_strides = (b, s, h);
+ * k_in/k_out: [B, S, Hkv, D] with strides k_in_strides / k_out_strides.
+ * Element type `dt` for inputs and outputs (bf16 results are rounded to
+ * nearest even from an fp32 rotation; the angle position*theta_k is formed and
+ * reduced modulo 2*pi in fp64). Values are not rotated.
+ * positions: int32 [B, S] (row-major, position of token s of sequence b), or
+ * NULL for position = s. k_in/k_out may be NULL together (queries only) and
+ * so may q_in/q_out (keys only); at least one pair must be given.
+ * In place is allowed (q_out == q_in, k_out == k_in); other overlap is not.
+ * Errors: INVALID_ARG for B, S, H < 1, rope_base <= 0, bad strides or
+ * alignment; UNSUPPORTED for D not in {64, 128} or an unknown dtype.
+ */
+la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
+                  const int64_t q_out_strides[3],
+                  const void* k_in, void* k_out, const int64_t k_in_strides[3],
+                  const int64_t k_out_strides[3],
+                  la_dtype dt, int B, int S, int Hq, int Hkv, int D,
+                  const int32_t* positions, double rope_base, hipStream_t stream);
+
+/*
+ * gqa_prefill — grouped-query causal attention with the cross-document mask,
+ * on queries and keys that are ALREADY ROTATED (see rope_qk) [P2, P4].
+ *
+ * q: [B, S, Hq, D], k and v: [B, S, Hkv, D], o: [B, S, Hq, D], all of type
+ * `dt`, strides (b, s, h) in q_strides, k_strides, v_strides, o_strides.
+ * cu_docs: int32 [B, n_docs + 1], row b non-decreasing from 0 to S: document
+ *   d of sequence b is the token range [cu_docs[b][d], cu_docs[b][d+1])
+ *   (empty documents are allowed and hold no token). NULL means one document
+ *   per sequence (n_docs is then ignored).
+ * Key j is visible to query i iff j <= i and both lie in the same document.
+ * Scores are (q_i . k_j) * softmax_scale (softmax_scale <= 0 means 1/sqrt(D));
+ * o_i is the softmax-weighted sum of the visible v_j.
+ * lse: optional fp32 [B, Hq, S] (contiguous): natural-log log-sum-exp of each
+ *   row's visible scores; NULL to skip.
+ * Arithmetic: bf16 MFMA products with fp32 accumulation, fp32 softmax
+ * statistics, probabilities rounded to bf16 before the PV product. For
+ * dt = LA_FP32 the operands are rounded to bf16 on load and o is fp32.
+ * Errors: INVALID_ARG for null q/k/v/o, B, S, Hq, Hkv < 1, n_docs < 1 with
+ * cu_docs given, Hq % Hkv != 0, bad strides or alignment; UNSUPPORTED for D or
+ * group size outside the supported set.
+ */
+la_status gqa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                      la_dtype dt, int B, int S, int Hq, int Hkv, int D,
+                      const int64_t q_strides[3], const int64_t k_strides[3],
+                      const int64_t v_strides[3], const int64_t o_strides[3],
+                      const int32_t* cu_docs, int n_docs, float softmax_scale,
+                      hipStream_t stream);
+
+/*
+ * gqa_decode — split-KV attention of one new token per sequence over its KV
+ * cache; writes per-split partial results for gqa_decode_combine [P2].
+ *
+ * q: bf16 [B, Hq, D], strides q_strides = (b, h), already rotated at position
+ *   seq_lens[b] - 1.
+ * k_cache, v_cache: bf16 [B, Hkv, Lmax, D] with strides cache_strides =
+ *   (b, h, l) shared by both; slots 0..seq_lens[b]-1 hold the rotated keys and
+ *   the values of every token of sequence b, the new token included.
+ * seq_lens: int32 [B] on the device, 1 <= seq_lens[b] <= Lmax.
+ * Split s of sequence b covers cache slots [s*kv_chunk, min((s+1)*kv_chunk,
+ *   seq_lens[b])); every slot of the cache window is visible.
+ * o_part: fp32 [B, Hq, max_splits, D], lse_part: fp32 [B, Hq, max_splits]
+ *   (contiguous, caller-owned workspace of B*Hq*max_splits*(D+1)*4 bytes):
+ *   the split's softmax-normalised output and natural-log log-sum-exp; a
+ *   split with no slots gets o = 0 and lse = -inf.
+ * Requirements: kv_chunk a positive multiple of 64; max_splits >=
+ *   ceil(Lmax / kv_chunk); dt of q and caches is bf16 only.
+ * Errors: INVALID_ARG for null pointers, sizes < 1, kv_chunk not a multiple
+ * of 64, max_splits too small, bad strides or alignment; UNSUPPORTED for D
+ * or group size outside the supported set.
+ */
+la_status gqa_decode(const void* q, const int64_t q_strides[2],
+                     const void* k_cache, const void* v_cache, const int64_t cache_strides[3],
+                     const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int Lmax,
+                     int kv_chunk, int max_splits, float softmax_scale,
+                     float* o_part, float* lse_part, hipStream_t stream);
+
+/*
+ * gqa_decode_combine — merge the split partials of gqa_decode by their
+ * log-sum-exp weights: with M = max_s lse_s and w_s = exp(lse_s - M),
+ * o = sum_s w_s o_s / sum_s w_s and lse = M + ln(sum_s w_s), over the splits
+ * s < ceil(seq_lens[b] / kv_chunk).
+ * o: [B, Hq, D] of type dt (bf16 or fp32) with strides o_strides = (b, h);
+ * lse: optional fp32 [B, Hq] (contiguous), NULL to skip.
+ * Errors: as gqa_decode for the shared arguments; UNSUPPORTED for D not in
+ * {64, 128}.
+ */
+la_status gqa_decode_combine(const float* o_part, const float* lse_part,
+                             const int32_t* seq_lens, int B, int Hq, int D,
+                             int kv_chunk, int max_splits,
+                             void* o, const int64_t o_strides[2], float* lse,
+                             la_dtype dt, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLAMA_ATTN_H */

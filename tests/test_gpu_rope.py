@@ -1,0 +1,81 @@
+"""rope_qk on the GPU against the fp64 oracle rotation."""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_helpers as H
+from oracle import reference as orc
+from workloads import draw_positions, draw_prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _rope_gpu(q, k, positions=None, base=500000.0, inplace=False):
+    import gqa_attention_rope_02_amd as la
+    qd, kd = q.cuda(), k.cuda()
+    pos = None if positions is None else torch.as_tensor(positions, dtype=torch.int32).cuda()
+    if inplace:
+        la.rope_qk(qd, qd, kd, kd, positions=pos, rope_base=base)
+        qo, ko = qd, kd
+    else:
+        qo, ko = torch.full_like(qd, float("nan")), torch.full_like(kd, float("nan"))
+        la.rope_qk(qd, qo, kd, ko, positions=pos, rope_base=base)
+    torch.cuda.synchronize()
+    return qo.cpu(), ko.cpu()
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,maxpos", [(1, 200, 16, 2, 128, None), (2, 77, 8, 8, 64, 131071),
+                                                 (1, 64, 128, 8, 128, 131071)])
+def test_rope_bf16_within_one_ulp(B, S, Hq, Hkv, D, maxpos):
+    H.say("rope bf16", B, S, Hq, Hkv, D, maxpos)
+    q, k, _ = draw_prefill_inputs(B, S, Hq, Hkv, D, "bf16", 21)
+    positions = None if maxpos is None else draw_positions(B, S, maxpos, 21)
+    pos = np.broadcast_to(np.arange(S), (B, S)) if positions is None else positions
+    qo, ko = _rope_gpu(q, k, positions)
+    for got, x in ((qo, q), (ko, k)):
+        want = orc.rope(x, pos, 500000.0)
+        err = np.abs(got.double().numpy() - want)
+        assert np.all(err <= H.bf16_ulp(want)), f"max err/ulp {np.max(err / H.bf16_ulp(want)):.3f}"
+
+
+def test_rope_fp32_tiny_config():
+    H.say("rope fp32 tiny")
+    q, k, _ = draw_prefill_inputs(1, 128, 8, 2, 64, "fp32", 1)
+    qo, ko = _rope_gpu(q, k)
+    pos = np.arange(128)[None]
+    for got, x in ((qo, q), (ko, k)):
+        want = orc.rope(x, pos, 500000.0)
+        err = np.abs(got.double().numpy() - want)
+        assert np.all(err <= 8 * H.fp32_ulp(np.abs(x.double().numpy()).max()) + 1e-7)
+
+
+def test_rope_position_zero_is_exact_and_inplace_matches():
+    H.say("rope pos0 / inplace")
+    q, k, _ = draw_prefill_inputs(1, 40, 8, 2, 128, "bf16", 22)
+    zero = np.zeros((1, 40), dtype=np.int32)
+    qo, ko = _rope_gpu(q, k, zero)
+    assert torch.equal(qo, q) and torch.equal(ko, k)
+    a = _rope_gpu(q, k, draw_positions(1, 40, 9999, 22))
+    b = _rope_gpu(q, k, draw_positions(1, 40, 9999, 22), inplace=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_rope_strided_views_of_packed_qkv():
+    """Q and K as head-slices of one packed [B, S, Hq + 2Hkv, D] projection output."""
+    H.say("rope packed views")
+    B, S, Hq, Hkv, D = 2, 50, 8, 2, 128
+    gen = torch.Generator().manual_seed(5)
+    qkv = torch.randn(B, S, Hq + 2 * Hkv, D, generator=gen).bfloat16()
+    dev = qkv.cuda()
+    out = torch.full_like(dev, float("nan"))
+    import gqa_attention_rope_02_amd as la
+    la.rope_qk(dev[:, :, :Hq], out[:, :, :Hq], dev[:, :, Hq:Hq + Hkv], out[:, :, Hq:Hq + Hkv])
+    torch.cuda.synchronize()
+    out = out.cpu()
+    pos = np.broadcast_to(np.arange(S), (B, S))
+    want_q = orc.rope(qkv[:, :, :Hq], pos)
+    want_k = orc.rope(qkv[:, :, Hq:Hq + Hkv], pos)
+    assert np.all(np.abs(out[:, :, :Hq].double().numpy() - want_q) <= H.bf16_ulp(want_q))
+    assert np.all(np.abs(out[:, :, Hq:Hq + Hkv].double().numpy() - want_k) <= H.bf16_ulp(want_k))
+    assert torch.isnan(out[:, :, Hq + Hkv:].float()).all()     # V slot untouched
