@@ -1,0 +1,320 @@
+"""Throughput of the GQA + RoPE attention path on one MI355X.
+
+One step = one pass of the prefill path (rope_qk on Q and K, then gqa_prefill
+with the causal + cross-document mask, writing O and the log-sum-exp) over
+one batch of seeded synthetic input of the Llama-3.1-8B layer shape
+(S=8192, 32 query heads on 8 KV heads, head_dim 128, bf16, 1-8 documents).
+Inputs are resident in HBM before the timed region starts.
+
+The JSON line also carries the 405B-shape prefill (S=32768, 128/8 heads) and
+the 405B-shape split-KV decode (16 sequences, cache lengths U[4096, 131072],
+measured as cache-read GB/s), each against its own roofline, plus the fp64
+oracle timed on a bounded row sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--only prefill|decode] [--with-128k]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "GQA prefill TFLOP/s (% MFMA peak) + decode KV-read GB/s (% HBM peak), 1 GPU"
+KV_CHUNK = 2048
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def allowed_pairs(cu_docs: np.ndarray) -> int:
+    """Visible (query, key) pairs of one sequence under causal + document mask."""
+    n = np.diff(np.asarray(cu_docs, dtype=np.int64))
+    return int(np.sum(n * (n + 1) // 2))
+
+
+def kernel_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gqa_attention_rope_02_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = table.get(f"{kernel}/{workload}")
+    if not e or e.get("source_hash") != src_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------- prefill
+
+def setup_prefill(name: str):
+    import torch
+    from workloads import CONFIGS, draw_cu_docs, draw_prefill_inputs
+    w = CONFIGS[name]
+    t = time.time()
+    q, k, v = draw_prefill_inputs(w.B, w.S, w.Hq, w.Hkv, w.D, w.dtype, w.seed)
+    cu = draw_cu_docs(w.S, w.seed, w.n_docs, w.n_docs_max)
+    dev = torch.device("cuda")
+    st = dict(w=w, cu=cu, q=q.to(dev), k=k.to(dev), v=v.to(dev),
+              cu_d=torch.as_tensor(cu, dtype=torch.int32).reshape(1, -1).to(dev))
+    st["qr"] = torch.empty_like(st["q"])
+    st["kr"] = torch.empty_like(st["k"])
+    st["o"] = torch.empty_like(st["q"])
+    st["lse"] = torch.empty(w.B, w.Hq, w.S, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"{name}: inputs ready in {time.time() - t:.1f}s, documents {np.diff(cu).tolist()}")
+    return st, (q, k, v)
+
+
+def time_prefill(st, steps: int, warmup: int):
+    import torch
+    import gqa_attention_rope_02_amd as la
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        la.rope_qk(st["q"], st["qr"], st["k"], st["kr"])
+        if evs:
+            evs[1].record()
+        la.gqa_prefill(st["qr"], st["kr"], st["v"], st["o"], st["lse"], st["cu_d"])
+        if evs:
+            evs[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rope_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    gpu_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    return dict(wall_ms_per_step=1e3 * wall / steps, rope_ms=float(np.mean(rope_ms)),
+                prefill_ms=float(np.mean(attn_ms)), gpu_ms_per_step=float(np.mean(gpu_ms)),
+                prefill_ms_median=float(np.median(attn_ms)))
+
+
+def prefill_flops(w, cu) -> float:
+    return 4.0 * w.D * w.Hq * w.B * allowed_pairs(cu)
+
+
+# ---------------------------------------------------------------------- decode
+
+def setup_decode():
+    import torch
+    from workloads import CONFIGS, draw_seq_lens
+    w = CONFIGS["decode405b"]
+    lens = draw_seq_lens(w.B, w.len_lo, w.len_hi, w.seed)
+    Lmax = w.len_hi
+    dev = torch.device("cuda")
+    t = time.time()
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    kc = torch.empty(w.B, w.Hkv, Lmax, w.D, dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    for b in range(w.B):     # random cache contents (keys as if already rotated)
+        kc[b].normal_(generator=g)
+        vc[b].normal_(generator=g)
+    q = torch.randn(w.B, w.Hq, w.D, generator=g, device=dev).bfloat16()
+    max_splits = -(-Lmax // KV_CHUNK)
+    st = dict(w=w, lens=lens, q=q, kc=kc, vc=vc, Lmax=Lmax, max_splits=max_splits,
+              sl=torch.as_tensor(lens, dtype=torch.int32).to(dev),
+              op=torch.empty(w.B, w.Hq, max_splits, w.D, dtype=torch.float32, device=dev),
+              lp=torch.empty(w.B, w.Hq, max_splits, dtype=torch.float32, device=dev),
+              o=torch.empty(w.B, w.Hq, w.D, dtype=torch.bfloat16, device=dev))
+    torch.cuda.synchronize()
+    log(f"decode405b: cache ready in {time.time() - t:.1f}s, lengths {lens.tolist()}")
+    return st
+
+
+def time_decode(st, steps: int, warmup: int):
+    import torch
+    import gqa_attention_rope_02_amd as la
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        la.gqa_decode(st["q"], st["kc"], st["vc"], st["sl"], KV_CHUNK, st["op"], st["lp"])
+        if evs:
+            evs[1].record()
+        la.gqa_decode_combine(st["op"], st["lp"], st["sl"], KV_CHUNK, st["o"])
+        if evs:
+            evs[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    dec = [e[0].elapsed_time(e[1]) for e in evs]
+    comb = [e[1].elapsed_time(e[2]) for e in evs]
+    tot = [e[0].elapsed_time(e[2]) for e in evs]
+    return dict(decode_ms=float(np.mean(dec)), combine_ms=float(np.mean(comb)),
+                ms_per_step=float(np.mean(tot)), decode_ms_median=float(np.median(dec)))
+
+
+def decode_bytes(st) -> float:
+    w = st["w"]
+    return float(np.sum(st["lens"].astype(np.int64))) * w.Hkv * w.D * 2 * 2
+
+
+# ----------------------------------------------------------------- cpu oracle
+
+def cpu_baseline(host_inputs, w, cu, budget_s: float = 20.0):
+    """The fp64 oracle on a row sample of the same workload, as TFLOP/s."""
+    from oracle import reference as orc
+    from workloads import sample_rows
+    q, k, v = host_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    rows_all = sample_rows(w.S, cu, w.seed, n_random=4096, tile=64, n_edges=0)
+    rng = np.random.default_rng(w.seed + 7)
+    rows_all = rng.permutation(rows_all)
+    doc = orc.document_of(cu, w.S)
+    start = np.asarray(cu)[doc]
+    done, flops, t_used = 0, 0.0, 0.0
+    t0 = time.perf_counter()
+    chunk = 256
+    while done < rows_all.size and t_used < budget_s:
+        rows = np.sort(rows_all[done:done + chunk])
+        orc.rope_attention(q, k, v, cu, w.rope_base, None, None, rows)
+        done += rows.size
+        flops += 4.0 * w.D * w.Hq * float(np.sum(rows - start[rows] + 1))
+        t_used = time.perf_counter() - t0
+    return dict(value=flops / t_used / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"{done} query rows x all {w.Hq} heads of the {w.name} prefill "
+                       f"(fp64 NumPy oracle incl. RoPE), {t_used:.1f}s")
+
+
+# ------------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--with-128k", action="store_true", help="also time the S=131072 prefill")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention path here runs unsharded on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import gqa_attention_rope_02_amd  # noqa: F401  (fails loudly without the HIP library)
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) Q/K/V, seeded document cuts)"}
+    phash = kernel_hash("gqa_prefill.hip")
+
+    if args.only in (None, "prefill"):
+        st, host = setup_prefill("llama8b")
+        w, cu = st["w"], st["cu"]
+        t = time_prefill(st, args.steps, args.warmup)
+        fl = prefill_flops(w, cu)
+        value = fl / (t["gpu_ms_per_step"] * 1e-3) / 1e12
+        achieved = fl / (t["prefill_ms"] * 1e-3) / 1e12
+        out.update(value=round(value, 2), unit="TFLOP/s", ms_per_step=round(t["gpu_ms_per_step"], 4))
+        out["config"] = {"workload": "llama-3.1-8b attention layer prefill: rope_qk + gqa_prefill, "
+                                     "causal + cross-document mask",
+                         "batch": w.B, "seq_len": w.S, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                         "head_dim": w.D, "rope_base": w.rope_base, "documents": int(cu.size - 1),
+                         "allowed_pairs": allowed_pairs(cu), "flops_per_step": fl,
+                         "parallelism": "none (1 GPU)"}
+        out["roofline"] = {"kernel": "gqa_prefill", "bound": "mfma", "achieved": round(achieved, 2),
+                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                           "traffic": measured_traffic("gqa_prefill", "llama8b", phash),
+                           "launch_ms": round(t["prefill_ms"], 4)}
+        out["timing"] = {k: round(x, 4) for k, x in t.items()}
+        if not args.no_cpu_baseline:
+            log("timing the fp64 oracle on a row sample ...")
+            out["cpu_baseline"] = cpu_baseline(host, w, cu)
+        del st
+
+        st3, _ = setup_prefill("llama405b")
+        t3 = time_prefill(st3, max(3, args.steps // 2), args.warmup)
+        fl3 = prefill_flops(st3["w"], st3["cu"])
+        out["prefill_405b"] = {
+            "workload": "llama-3.1-405b attention layer prefill S=32768, 128 q / 8 kv heads",
+            "documents": int(st3["cu"].size - 1),
+            "tflops_path": round(fl3 / (t3["gpu_ms_per_step"] * 1e-3) / 1e12, 2),
+            "tflops_kernel": round(fl3 / (t3["prefill_ms"] * 1e-3) / 1e12, 2),
+            "frac_kernel": round(fl3 / (t3["prefill_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "ms_per_step": round(t3["gpu_ms_per_step"], 4), "prefill_ms": round(t3["prefill_ms"], 4),
+            "rope_ms": round(t3["rope_ms"], 4), "traffic": measured_traffic("gqa_prefill", "llama405b", phash)}
+        del st3
+        if args.with_128k:
+            st5, _ = setup_prefill("long128k")
+            t5 = time_prefill(st5, 3, 1)
+            fl5 = prefill_flops(st5["w"], st5["cu"])
+            out["prefill_128k"] = {
+                "workload": "405b-shape long-context prefill S=131072, 4 documents",
+                "tflops_kernel": round(fl5 / (t5["prefill_ms"] * 1e-3) / 1e12, 2),
+                "frac_kernel": round(fl5 / (t5["prefill_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "prefill_ms": round(t5["prefill_ms"], 3), "rope_ms": round(t5["rope_ms"], 3)}
+            del st5
+        torch.cuda.empty_cache()
+
+    if args.only in (None, "decode"):
+        sd = setup_decode()
+        td = time_decode(sd, args.steps, args.warmup)
+        nbytes = decode_bytes(sd)
+        gbs = nbytes / (td["decode_ms"] * 1e-3) / 1e9
+        dhash = kernel_hash("gqa_decode.hip")
+        out["decode_405b"] = {
+            "workload": "405b-shape decode: 16 sequences x 1 token, 128 q / 8 kv heads, "
+                        "cache lengths U[4096,131072]", "kv_chunk": KV_CHUNK,
+            "kv_bytes": nbytes, "gbs_path": round(nbytes / (td["ms_per_step"] * 1e-3) / 1e9, 1),
+            "ms_per_step": round(td["ms_per_step"], 4),
+            "roofline": {"kernel": "gqa_decode", "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("gqa_decode", "decode405b", dhash),
+                         "launch_ms": round(td["decode_ms"], 4)},
+            "combine_ms": round(td["combine_ms"], 4)}
+        if args.only == "decode":
+            out.update(value=round(gbs, 1), unit="GB/s", ms_per_step=round(td["ms_per_step"], 4),
+                       config={"workload": out["decode_405b"]["workload"]},
+                       roofline=out["decode_405b"]["roofline"])
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
