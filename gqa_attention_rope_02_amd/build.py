@@ -33,13 +33,26 @@ def _flags():
             "-Wno-unused-result"]
 
 
+# Per-source extra flags (none at present).
+EXTRA = {}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
+
+
+def _check_kernel_stubs(path: str) -> None:
+    """Fail if a kernel's host launch stub is missing from the library (the host
+    pass of hipcc can drop a kernel template whose body it cannot compile)."""
+    r = subprocess.run(["nm", "-D", "--undefined-only", path], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from the library: " + ", ".join(missing[:4]))
 
 
 def build(verbose: bool = True) -> str:
@@ -51,6 +64,7 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    _check_kernel_stubs(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -12,45 +12,91 @@
 // * One workgroup = one (sequence, KV head, tile of 256/g tokens): its 256
 //   "columns" are the (token, query head) pairs of the g heads sharing the KV
 //   head, so each K/V byte staged in LDS feeds 256 query rows. Four waves own
-//   64 columns each.
+//   64 columns each (one wave per SIMD; 64 columns per wave keep the LDS
+//   operand traffic at half of what the LDS delivers at full MFMA rate).
 // * The contractions run transposed on the 32x32x16 bf16 MFMA: S^T = K Q^T
 //   (keys on M, columns on N) and O^T = V^T P^T (head_dim on M). In both
 //   results a lane owns one column, so the softmax statistics and the output
 //   rescale stay in the lane; only the row max needs one cross-lane step
-//   (lanes l and l^32), and the S^T accumulator already has the layout of the
-//   P^T operand (no shuffle between the two products).
-// * Q stays in registers for the whole key loop. K (row-major) and V
-//   (transposed to [d][key]) are staged per 64-key tile in LDS, double
-//   buffered, with XOR swizzles against bank conflicts; the next tile's global
-//   loads are issued before the current tile's MFMAs.
-// * Online softmax in the base-2 domain with fp32 statistics; the accumulator
-//   is rescaled only when some lane's running max moved. Masks are evaluated
-//   only on tiles that cross a causal or document edge of the wave's columns;
-//   tiles entirely outside them are skipped.
+//   (v_permlane32_swap between lanes l and l^32), and the S^T accumulator
+//   already has the layout of the P^T operand.
+// * Q stays in registers for the whole key loop. K and V tiles of 64 keys go
+//   from HBM straight into LDS (buffer_load_dwordx4 ... lds, no register
+//   staging), row-major with XOR swizzles, double buffered: the next tile's
+//   loads are in flight while the current one is consumed. The buffer
+//   descriptor moves with the tile and its size ends at the sequence end, so
+//   rows past the end read as zero. K operands are read with ds_read_b128; the
+//   V^T operand with the transposing ds_read_b64_tr_b16 from the row-major V
+//   tile.
+// * Each 64-key tile is consumed in two 32-key halves, software pipelined so
+//   that the softmax VALU work of one half is issued between the MFMAs of the
+//   next product: QK(0); QK(1) with softmax(0); PV(0) with softmax(1); PV(1).
+// * Online softmax in the base-2 domain with fp32 statistics; probabilities
+//   are rounded to bf16 once and the row sums accumulate those rounded values
+//   (v_dot2_f32_bf16), so numerator and denominator use the same weights. The
+//   reference the exponents are taken against moves only when a score exceeds
+//   it by more than 2^8 (exact: softmax does not depend on the reference, and
+//   the weights stay below 256), so the accumulator is almost never rescaled;
+//   a per-tile exact max would force a rescale in most tiles, since with 64
+//   columns per wave some column nearly always finds a new maximum. Masks are
+//   evaluated only on tiles that cross a causal or document edge of the
+//   wave's columns.
 // * Workgroups are issued longest-first (last token tiles first), and the KV
 //   head is the fastest-varying index so the workgroups of one KV head land on
 //   one XCD (blockIdx % 8) and share its L2.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace la {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kCols = 256;   // columns per workgroup
-constexpr int kKT = 64;      // keys per tile
+constexpr int kCols = 256;    // columns per workgroup
+constexpr int kKT = 64;       // keys per tile
+constexpr float kLazy = 8.f;  // log2 headroom of the lazily moved softmax reference
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+using lds_void = __attribute__((address_space(3))) void;
+using lds_i16x4 = __attribute__((address_space(3))) i16x4;
+
+// Physical 16-byte chunk of logical chunk c in row r of a K tile / V tile.
+template <int CH>
+__device__ __forceinline__ int k_chunk(int c, int r) { return c ^ (r & (CH - 1)); }
+// V: rows 1 apart are spread by 4 chunks (64 bytes), so one transposing read
+// of 32 lanes (4 consecutive rows x two 32-byte halves of a 32-column block)
+// touches every bank of the 256-byte row once. An XOR with a row-only term is
+// its own inverse, which the loader relies on.
+template <int CH>
+__device__ __forceinline__ int v_chunk(int c, int r) { return c ^ (CH == 16 ? 4 * (r & 3) : 2 * (r & 3)); }
+
+// One 16-byte-per-lane load from `base` into LDS: lane i's 16 bytes at byte
+// offset `voff` land at dst + 16 i; bytes at or past `bytes_valid` read as zero.
+__device__ __forceinline__ void load_lds16(const void* base, int bytes_valid, int voff, char* dst) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes_valid, kRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_kernel(PrefillArgs a) {
   constexpr int TQ = kCols / G;          // tokens per workgroup
   constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;             // 32-row blocks of O^T
-  constexpr int CH = D / 8;              // 16-byte chunks per K row
-  constexpr int KLOADS = kKT * CH / 256; // K chunks loaded per thread
-  constexpr int VTHREADS = (kKT / 4) * CH;
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int ROW = D * 2;             // bytes per LDS row
+  constexpr int TILE = kKT * ROW;        // bytes per K or V tile
+  constexpr int NL = kKT * CH / 64 / 4;  // 1 KB loads per wave per K or V tile
 
-  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][kKT * D];
-  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * kKT];
+  __shared__ __attribute__((aligned(1024))) char lds[4 * TILE];   // K0 V0 K1 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -86,13 +132,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     valid[cb] = tok[cb] < S;
     st[cb] = valid[cb] ? start_of(tok[cb]) : 0;
   }
-  const int w_tmin = t0 + (wave * 64) / G;
+  const int w_tmin = min(t0 + (wave * 64) / G, S - 1);
   const int w_tmax_raw = t0 + (wave * 64 + 63) / G;
-  const bool wave_active = w_tmin < S;
   const bool wave_all_valid = w_tmax_raw < S;
   const int w_tmax = min(w_tmax_raw, S - 1);
-  const int w_smin = wave_active ? start_of(w_tmin) : 0;
-  const int w_smax = wave_active ? start_of(w_tmax) : 0;
+  const int w_smax = start_of(w_tmax);
 
   // ---- Q operand (B of S^T = K Q^T): Q[col][16ks + 8hi + i] ----------------
   bf16x8 qreg[2][KS];
@@ -113,151 +157,176 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   float m[2] = {-INFINITY, -INFINITY};
   float l[2] = {0.f, 0.f};
 
-  // ---- K/V tile staging ----------------------------------------------------
-  bf16x8 kr[KLOADS];
-  bf16x8 vr[4];
-  auto load_tile = [&](int kt) {
+  // ---- tile staging: per-lane byte offsets of this wave's 1 KB loads --------
+  int koff[NL], voff[NL];
 #pragma unroll
-    for (int n = 0; n < KLOADS; ++n) {
-      const int id = tid + 256 * n;
-      const int key = id / CH, c = id % CH;
-      const int j = kt + key;
-      kr[n] = j < S ? load8(kbase + j * a.ks_s + 8 * c) : zero_bf16x8();
-    }
-    if (tid < VTHREADS) {
-      const int kg = tid / CH, c = tid % CH;
+  for (int n = 0; n < NL; ++n) {
+    const int p = (n * 4 + wave) * 64 + lane;   // LDS chunk written by this lane
+    const int row = p / CH, ph = p % CH;
+    koff[n] = (int)(row * a.ks_s * (int64_t)sizeof(T) + 8 * k_chunk<CH>(ph, row) * (int)sizeof(T));
+    voff[n] = (int)(row * a.vs_s * (int64_t)sizeof(T) + 8 * v_chunk<CH>(ph, row) * (int)sizeof(T));
+  }
+  auto stage = [&](int kt, char* dst) {
+    if constexpr (std::is_same<T, __bf16>::value) {
+      const int64_t rows = S - kt;   // rows past the sequence end read as zero
+      const int kb_ = (int)min(rows * a.ks_s * 2, (int64_t)0x7fffffff);
+      const int vb_ = (int)min(rows * a.vs_s * 2, (int64_t)0x7fffffff);
+      const void* kp = kbase + kt * a.ks_s;
+      const void* vp = vbase + kt * a.vs_s;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = kt + 4 * kg + i;
-        vr[i] = j < S ? load8(vbase + j * a.vs_s + 8 * c) : zero_bf16x8();
+      for (int n = 0; n < NL; ++n) {
+        load_lds16(kp, kb_, koff[n], dst + (n * 4 + wave) * 1024);
+        load_lds16(vp, vb_, voff[n], dst + TILE + (n * 4 + wave) * 1024);
+      }
+    } else {   // fp32 inputs: convert to bf16 on the way into LDS
+      for (int p = tid; p < kKT * CH; p += 256) {
+        const int row = p / CH, ph = p % CH;
+        const int j = kt + row;
+        bf16x8 kv = zero_bf16x8(), vv = zero_bf16x8();
+        if (j < S) {
+          kv = load8(kbase + j * a.ks_s + 8 * k_chunk<CH>(ph, row));
+          vv = load8(vbase + j * a.vs_s + 8 * v_chunk<CH>(ph, row));
+        }
+        *reinterpret_cast<bf16x8*>(dst + p * 16) = kv;
+        *reinterpret_cast<bf16x8*>(dst + TILE + p * 16) = vv;
       }
     }
   };
-  auto store_tile = [&](int stage) {
-    __bf16* lk = lds_k[stage];
+
+  // ---- per-lane LDS operand offsets ------------------------------------------
+  // K operand: row 32kb + lc, logical chunk 2ks + hi.
+  const int k_lane = lc * ROW;
+  const int k_x = hi ^ (lc & (CH - 1));              // physical chunk = (2ks) ^ k_x
+  // V^T operand (transposing read): the 16-lane group g = lane/16 covers
+  // d = 32db + 16(g&1) + (lane&15) and keys 16ks + 4hi (+8) + 0..3; its input
+  // lane L = lane&15 addresses row 16ks + 4hi + L/4 at d0 = 32db + 16(g&1) + 4(L%4).
+  const int L16 = lane & 15;
+  const int vrow = 4 * hi + (L16 >> 2);
+  int v_lane[DB];
 #pragma unroll
-    for (int n = 0; n < KLOADS; ++n) {
-      const int id = tid + 256 * n;
-      const int key = id / CH, c = id % CH;
-      *reinterpret_cast<bf16x8*>(lk + key * D + 8 * (c ^ (key & (CH - 1)))) = kr[n];
+  for (int db = 0; db < DB; ++db)
+    v_lane[db] = vrow * ROW + 16 * v_chunk<CH>(4 * db + 2 * ((lane >> 4) & 1) + ((L16 >> 1) & 1), vrow) + 8 * (L16 & 1);
+
+  auto qk = [&](const char* lk, int kb, f32x16* s) {
+    bf16x8 ka[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      ka[ks] = *reinterpret_cast<const bf16x8*>(lk + kb * 32 * ROW + k_lane + 16 * ((2 * ks) ^ k_x));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s[0] = mfma32(ka[ks], qreg[0][ks], s[0]);
+      s[1] = mfma32(ka[ks], qreg[1][ks], s[1]);
     }
-    if (tid < VTHREADS) {
-      __bf16* lv = lds_v[stage];
-      const int kg = tid / CH, c = tid % CH;
+  };
+  auto mask = [&](f32x16* s, int kb, int kt) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * c + e;
-        bf16x4 w;
-        w[0] = vr[0][e];
-        w[1] = vr[1][e];
-        w[2] = vr[2][e];
-        w[3] = vr[3][e];
-        *reinterpret_cast<bf16x4*>(lv + d * kKT + 4 * (kg ^ (d & 15))) = w;
+    for (int cb = 0; cb < 2; ++cb) {
+      const int lo = valid[cb] ? st[cb] - kt : kKT;
+      const int hi_ = valid[cb] ? tok[cb] - kt : -1;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kr = kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
+        s[cb][j] = (kr >= lo && kr <= hi_) ? s[cb][j] : -INFINITY;
+      }
+    }
+  };
+  // softmax of one half: returns whether some lane moved its reference
+  auto softmax = [&](const f32x16* s, bf16x8 (*p)[2], float* alpha) -> bool {
+    bool moved = false;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float mx = s[cb][0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[cb][j]);
+      mx = max_xor32(mx);
+      alpha[cb] = 1.f;
+      if (mx * a.scale_log2 > m[cb] * a.scale_log2 + kLazy) {   // also when m = -inf
+        alpha[cb] = fast_exp2((m[cb] - mx) * a.scale_log2);        // 0 when m = -inf
+        m[cb] = mx;
+        moved = true;
+      }
+      const float mc = m[cb] == -INFINITY ? 0.f : m[cb] * a.scale_log2;
+      float rs = 0.f;
+      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          bf16x2 pr;
+          pr[0] = to_bf16(fast_exp2(fmaf(s[cb][8 * h2 + i], a.scale_log2, -mc)));
+          pr[1] = to_bf16(fast_exp2(fmaf(s[cb][8 * h2 + i + 1], a.scale_log2, -mc)));
+          p[cb][h2][i] = pr[0];
+          p[cb][h2][i + 1] = pr[1];
+          rs = __builtin_amdgcn_fdot2_f32_bf16(pr, one, rs, false);
+        }
+      l[cb] = l[cb] * alpha[cb] + rs;
+    }
+    return moved;
+  };
+  // accumulator rescale in place (rare); written so the accumulator never
+  // leaves the AGPRs the MFMAs keep it in
+  auto rescale = [&](const float* alpha) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float x = acc[db][cb][j], t;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(x), "=&v"(t) : "v"(alpha[cb]));
+          acc[db][cb][j] = x;
+        }
+  };
+  auto pv = [&](const char* lv, int kb, const bf16x8 (*p)[2]) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int ks = 2 * kb + h2;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const char* vp = lv + 16 * ks * ROW + v_lane[db];
+        const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
+        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * ROW));
+        const bf16x8 va = __builtin_shufflevector(__builtin_bit_cast(bf16x4, r0),
+                                                  __builtin_bit_cast(bf16x4, r1), 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[db][0] = mfma32(va, p[0][h2], acc[db][0]);
+        acc[db][1] = mfma32(va, p[1][h2], acc[db][1]);
       }
     }
   };
 
   const int n_tiles = (kv_hi - kv_lo) / kKT + 1;
-  load_tile(kv_lo);
-  store_tile(0);
+  stage(kv_lo, lds);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int n = 0; n < n_tiles; ++n) {
     const int kt = kv_lo + n * kKT;
-    const int stage = n & 1;
-    if (n + 1 < n_tiles) load_tile(kt + kKT);
+    const char* lk = lds + (n & 1) * 2 * TILE;
+    const char* lv = lk + TILE;
+    if (n + 1 < n_tiles) stage(kt + kKT, lds + ((n + 1) & 1) * 2 * TILE);
 
-    const bool skip = !wave_active || kt > w_tmax || kt + kKT - 1 < w_smin;
-    if (!skip) {
-      const bool need_mask = !wave_all_valid || kt + kKT - 1 > w_tmin || kt < w_smax;
-      const __bf16* lk = lds_k[stage];
-      const __bf16* lv = lds_v[stage];
+    const bool need_mask = !wave_all_valid || kt + kKT - 1 > w_tmin || kt < w_smax;
+    f32x16 s0[2], s1[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s0[cb][j] = s1[cb][j] = 0.f;
+    bf16x8 p0[2][2], p1[2][2];
+    float alpha0[2], alpha1[2];
 
-      // The tile is consumed in two 32-key halves kb, each with its own
-      // online-softmax step, which keeps the score block at 32 registers.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // S^T[key][col] for keys kt + 32kb .. kt + 32kb + 31
-        f32x16 s[2];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) s[cb][j] = 0.f;
-        const int key = kb * 32 + lc;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int c = 2 * ks + hi;
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lk + key * D + 8 * (c ^ (key & (CH - 1))));
-          s[0] = mfma32(ka, qreg[0][ks], s[0]);
-          s[1] = mfma32(ka, qreg[1][ks], s[1]);
-        }
+    qk(lk, 0, s0);
+    if (need_mask) mask(s0, 0, kt);
+    qk(lk, 1, s1);                                   // MFMAs overlap the softmax below
+    const bool mv0 = softmax(s0, p0, alpha0);
+    if (__any(mv0)) rescale(alpha0);
+    if (need_mask) mask(s1, 1, kt);
+    pv(lv, 0, p0);                                   // MFMAs overlap the softmax below
+    const bool mv1 = softmax(s1, p1, alpha1);
+    if (__any(mv1)) rescale(alpha1);
+    pv(lv, 1, p1);
 
-        if (need_mask) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int kj = kt + kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-              const bool vis = valid[cb] && kj >= st[cb] && kj <= tok[cb];
-              if (!vis) s[cb][j] = -INFINITY;
-            }
-          }
-        }
-
-        // online softmax, base 2
-        float alpha[2];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[cb][j]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float mnew = fmaxf(m[cb], mx);
-          const float mc = mnew == -INFINITY ? 0.f : mnew * a.scale_log2;
-          alpha[cb] = fast_exp2(m[cb] * a.scale_log2 - mc);
-          m[cb] = mnew;
-          float rs = 0.f;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float p = fast_exp2(fmaf(s[cb][j], a.scale_log2, -mc));
-            s[cb][j] = p;
-            rs += p;
-          }
-          l[cb] = l[cb] * alpha[cb] + rs;
-        }
-        if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-              for (int j = 0; j < 16; ++j) acc[db][cb][j] *= alpha[cb];
-        }
-
-        // O^T += V^T P^T, 16 keys per step
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int ks = 2 * kb + h2;
-          bf16x8 p[2];
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) p[cb][i] = to_bf16(s[cb][8 * h2 + i]);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int d = db * 32 + lc;
-            const __bf16* row = lv + d * kKT;
-            const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(row + 4 * ((4 * ks + hi) ^ (d & 15)));
-            const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(row + 4 * ((4 * ks + 2 + hi) ^ (d & 15)));
-            const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[db][0] = mfma32(va, p[0], acc[db][0]);
-            acc[db][1] = mfma32(va, p[1], acc[db][1]);
-          }
-        }
-      }
-    }
-
-    if (n + 1 < n_tiles) store_tile(stage ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
