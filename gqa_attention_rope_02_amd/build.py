@@ -33,8 +33,10 @@ def _flags():
             "-Wno-unused-result"]
 
 
-# Per-source extra flags (none at present).
-EXTRA = {}
+# Per-source extra flags. The prefill kernel asks for MFMA "VGPR form"
+# (accumulators in architectural VGPRs): at two waves per SIMD this removes
+# the accumulator copies between register files that the AGPR form costs.
+EXTRA = {"gqa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -53,6 +53,8 @@ namespace la {
 namespace {
 
 constexpr int kCols = 256;    // columns per workgroup
+constexpr int kNW = 8;        // waves per workgroup
+constexpr int kCB = kCols / kNW / 32;   // 32-column blocks per wave
 constexpr int kKT = 64;       // keys per tile
 constexpr float kLazy = 8.f;  // log2 headroom of the lazily moved softmax reference
 constexpr int kRsrcWord3 = 0x00020000;
@@ -86,7 +88,7 @@ __device__ __forceinline__ float max_xor32(float x) {
 }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int TQ = kCols / G;          // tokens per workgroup
   constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
@@ -94,7 +96,7 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int CH = D / 8;              // 16-byte chunks per row
   constexpr int ROW = D * 2;             // bytes per LDS row
   constexpr int TILE = kKT * ROW;        // bytes per K or V tile
-  constexpr int NL = kKT * CH / 64 / 4;  // 1 KB loads per wave per K or V tile
+  constexpr int NL = kKT * CH / 64 / kNW;  // 1 KB loads per wave per K or V tile
 
   __shared__ __attribute__((aligned(1024))) char lds[4 * TILE];   // K0 V0 K1 V1
 
@@ -122,46 +124,50 @@ void prefill_kernel(PrefillArgs a) {
   const T* vbase = static_cast<const T*>(a.v) + b * a.vs_b + kvh * a.vs_h;
 
   // ---- this lane's two columns (one per 32-column block) -------------------
-  int tok[2], head[2], st[2];
-  bool valid[2];
+  int tok[kCB], head[kCB], st[kCB];
+  bool valid[kCB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int col = wave * 64 + cb * 32 + lc;
+  for (int cb = 0; cb < kCB; ++cb) {
+    const int col = wave * 32 * kCB + cb * 32 + lc;
     tok[cb] = t0 + col / G;
     head[cb] = kvh * G + col % G;
     valid[cb] = tok[cb] < S;
     st[cb] = valid[cb] ? start_of(tok[cb]) : 0;
   }
-  const int w_tmin = min(t0 + (wave * 64) / G, S - 1);
-  const int w_tmax_raw = t0 + (wave * 64 + 63) / G;
+  const int w_tmin = min(t0 + (wave * 32 * kCB) / G, S - 1);
+  const int w_tmax_raw = t0 + (wave * 32 * kCB + 32 * kCB - 1) / G;
   const bool wave_all_valid = w_tmax_raw < S;
   const int w_tmax = min(w_tmax_raw, S - 1);
   const int w_smax = start_of(w_tmax);
 
   // ---- Q operand (B of S^T = K Q^T): Q[col][16ks + 8hi + i] ----------------
-  bf16x8 qreg[2][KS];
+  bf16x8 qreg[kCB][KS];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < kCB; ++cb) {
     const T* qp = qbase + tok[cb] * a.qs_s + head[cb] * a.qs_h + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qreg[cb][ks] = valid[cb] ? load8(qp + 16 * ks) : zero_bf16x8();
   }
 
-  f32x16 acc[DB][2];
+  f32x16 acc[DB][kCB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[db][cb][j] = 0.f;
-  float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
+  float m[kCB], l[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    m[cb] = -INFINITY;
+    l[cb] = 0.f;
+  }
 
   // ---- tile staging: per-lane byte offsets of this wave's 1 KB loads --------
   int koff[NL], voff[NL];
 #pragma unroll
   for (int n = 0; n < NL; ++n) {
-    const int p = (n * 4 + wave) * 64 + lane;   // LDS chunk written by this lane
+    const int p = (n * kNW + wave) * 64 + lane;   // LDS chunk written by this lane
     const int row = p / CH, ph = p % CH;
     koff[n] = (int)(row * a.ks_s * (int64_t)sizeof(T) + 8 * k_chunk<CH>(ph, row) * (int)sizeof(T));
     voff[n] = (int)(row * a.vs_s * (int64_t)sizeof(T) + 8 * v_chunk<CH>(ph, row) * (int)sizeof(T));
@@ -175,11 +181,11 @@ void prefill_kernel(PrefillArgs a) {
       const void* vp = vbase + kt * a.vs_s;
 #pragma unroll
       for (int n = 0; n < NL; ++n) {
-        load_lds16(kp, kb_, koff[n], dst + (n * 4 + wave) * 1024);
-        load_lds16(vp, vb_, voff[n], dst + TILE + (n * 4 + wave) * 1024);
+        load_lds16(kp, kb_, koff[n], dst + (n * kNW + wave) * 1024);
+        load_lds16(vp, vb_, voff[n], dst + TILE + (n * kNW + wave) * 1024);
       }
     } else {   // fp32 inputs: convert to bf16 on the way into LDS
-      for (int p = tid; p < kKT * CH; p += 256) {
+      for (int p = tid; p < kKT * CH; p += 64 * kNW) {
         const int row = p / CH, ph = p % CH;
         const int j = kt + row;
         bf16x8 kv = zero_bf16x8(), vv = zero_bf16x8();
@@ -213,14 +219,13 @@ void prefill_kernel(PrefillArgs a) {
     for (int ks = 0; ks < KS; ++ks)
       ka[ks] = *reinterpret_cast<const bf16x8*>(lk + kb * 32 * ROW + k_lane + 16 * ((2 * ks) ^ k_x));
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s[0] = mfma32(ka[ks], qreg[0][ks], s[0]);
-      s[1] = mfma32(ka[ks], qreg[1][ks], s[1]);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) s[cb] = mfma32(ka[ks], qreg[cb][ks], s[cb]);
   };
   auto mask = [&](f32x16* s, int kb, int kt) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < kCB; ++cb) {
       const int lo = valid[cb] ? st[cb] - kt : kKT;
       const int hi_ = valid[cb] ? tok[cb] - kt : -1;
 #pragma unroll
@@ -234,7 +239,7 @@ void prefill_kernel(PrefillArgs a) {
   auto softmax = [&](const f32x16* s, bf16x8 (*p)[2], float* alpha) -> bool {
     bool moved = false;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < kCB; ++cb) {
       float mx = s[cb][0];
 #pragma unroll
       for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[cb][j]);
@@ -269,7 +274,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           float x = acc[db][cb][j], t;
@@ -289,8 +294,8 @@ void prefill_kernel(PrefillArgs a) {
         const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * ROW));
         const bf16x8 va = __builtin_shufflevector(__builtin_bit_cast(bf16x4, r0),
                                                   __builtin_bit_cast(bf16x4, r1), 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[db][0] = mfma32(va, p[0][h2], acc[db][0]);
-        acc[db][1] = mfma32(va, p[1][h2], acc[db][1]);
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb) acc[db][cb] = mfma32(va, p[cb][h2], acc[db][cb]);
       }
     }
   };
@@ -307,13 +312,13 @@ void prefill_kernel(PrefillArgs a) {
     if (n + 1 < n_tiles) stage(kt + kKT, lds + ((n + 1) & 1) * 2 * TILE);
 
     const bool need_mask = !wave_all_valid || kt + kKT - 1 > w_tmin || kt < w_smax;
-    f32x16 s0[2], s1[2];
+    f32x16 s0[kCB], s1[kCB];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s0[cb][j] = s1[cb][j] = 0.f;
-    bf16x8 p0[2][2], p1[2][2];
-    float alpha0[2], alpha1[2];
+    bf16x8 p0[kCB][2], p1[kCB][2];
+    float alpha0[kCB], alpha1[kCB];
 
     qk(lk, 0, s0);
     if (need_mask) mask(s0, 0, kt);
@@ -332,7 +337,7 @@ void prefill_kernel(PrefillArgs a) {
 
   // ---- epilogue --------------------------------------------------------------
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < kCB; ++cb) {
     const float lt = l[cb] + __shfl_xor(l[cb], 32);
     if (!valid[cb]) continue;
     // true division (once per output): a row whose weights are all exact gets
@@ -354,7 +359,7 @@ void prefill_kernel(PrefillArgs a) {
 template <typename T, int D, int G>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)a.B * a.Hkv * a.n_qtiles;
-  hipLaunchKernelGGL((prefill_kernel<T, D, G>), dim3(grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_kernel<T, D, G>), dim3(grid), dim3(64 * kNW), 0, st, a);
   return hipGetLastError();
 }
 
