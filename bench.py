@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "GQA prefill TFLOP/s (% MFMA peak) + decode KV-read GB/s (% HBM peak), 1 GPU"
-KV_CHUNK = 2048
+KV_CHUNK = 256
 
 
 def log(*a):

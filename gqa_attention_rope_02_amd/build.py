@@ -36,7 +36,8 @@ def _flags():
 # Per-source extra flags. The prefill kernel asks for MFMA "VGPR form"
 # (accumulators in architectural VGPRs): at two waves per SIMD this removes
 # the accumulator copies between register files that the AGPR form costs.
-EXTRA = {"gqa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {"gqa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "gqa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

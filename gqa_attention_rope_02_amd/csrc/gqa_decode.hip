@@ -1,223 +1,318 @@
-// Split-KV decode over a KV cache and the log-sum-exp merge of its splits.
+// Split-KV decode over a KV cache and the log-sum-exp merge of its partials.
 //
 // What is computed: one new token per sequence attends, with each of its Hq
 // query heads, to every cached token of the KV head its group shares ("How
 // Meta's Llama 3.1 405B Architecture Actually Works", GQA paragraph: grouping
 // query heads onto one key/value head shrinks the cache read while decoding).
-// The cache window is cut into splits of kv_chunk slots; each split's
-// softmax-normalised output and log-sum-exp are merged afterwards by
-// O = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max lse).
+// Partial results over runs of consecutive cache slots are merged afterwards
+// by O = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max lse).
 //
-// How (gfx950): the path is bound by the HBM read of the cache (16 FLOP per
-// byte at 16 query heads per KV head), so the kernel is built to keep cache
-// bytes in flight and to read each byte exactly once:
-// * one workgroup = one (sequence, KV head, split); the g query heads of the
-//   group are the 16 columns of a 16x16 MFMA tile, so every K/V byte loaded
-//   serves all g heads;
-// * 64-key tiles are fetched with coalesced 16-byte loads (each 256-byte row
-//   by 16 consecutive lanes), the next tile's loads issued before the current
-//   tile is consumed, and staged through LDS (V transposed to [d][key]) with
-//   XOR swizzles; each of the four waves takes 16 keys of the tile, runs
-//   S^T = K Q^T on the 16x16x32 MFMA and O^T += V^T P^T on the 16x16x16 MFMA,
-//   and keeps its own online-softmax state, merged across waves through LDS
-//   at the end of the split.
+// How (gfx950): the step is bound by the HBM read of the cache (16 FLOP per
+// byte at 16 query heads per KV head), so the kernel exists to keep enough
+// cache bytes in flight, to read each byte once and to keep every wave busy to
+// the end:
+// * the cache of all (sequence, KV head) pairs forms one stream of 16-key
+//   tiles, cut into splits of kv_chunk slots; every wave of a persistent grid
+//   (one workgroup of four waves per CU) takes the splits that start in its
+//   equal slice of the tile stream, so waves end within a split of each other;
+// * consecutive splits of one (sequence, KV head) taken by one wave form a run
+//   with one online-softmax state; the run's partial goes to the slot of its
+//   first split and the other slots of the run get lse = -inf;
+// * each wave streams its tiles HBM -> LDS directly (buffer_load_dwordx4 ...
+//   lds) through its own four-stage ring, three tiles of K and V in flight, so
+//   waves never wait on each other; a buffer descriptor ends at the split's
+//   last valid row, so rows past it read as zero, and the stream continues
+//   across splits and runs, so it never drains between them;
+// * the g query heads of the group are the 16 columns of the MFMA tiles:
+//   S^T = K Q^T on the 16x16x32 MFMA, O^T += V^T P^T on the 16x16x16 MFMA with
+//   V^T read by the transposing ds_read_b64_tr_b16; every K/V byte loaded
+//   serves all g heads. Online softmax with a lazily moved reference (moved
+//   only when a score exceeds it by 2^8), row sums from the bf16-rounded P.
+// * Every load of the stream is an LDS-direct buffer load and they complete in
+//   issue order, so "tile p has landed" is "at most the loads of the tiles
+//   issued after it are pending", whatever other memory operations (query
+//   loads, partial stores) are outstanding.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace la {
 namespace {
 
-constexpr int kKT = 64;
+constexpr int kKT = 16;       // keys per wave tile
+constexpr int kNS = 4;        // LDS ring stages per wave
+constexpr int kWaves = 4;     // waves per workgroup
+constexpr float kLazy = 8.f;  // log2 headroom of the lazily moved softmax reference
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kMaxB = kDecodeMaxBatch;   // sequences per call (tables in LDS)
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+using lds_void = __attribute__((address_space(3))) void;
+using lds_i16x4 = __attribute__((address_space(3))) i16x4;
+
+template <int CH>
+__device__ __forceinline__ int k_chunk(int c, int r) { return c ^ (r & (CH - 1)); }
+template <int CH>
+__device__ __forceinline__ int v_chunk(int c, int r) { return c ^ (CH == 16 ? 4 * (r & 3) : 2 * (r & 3)); }
+
+__device__ __forceinline__ void load_lds16(const void* base, int bytes_valid, int voff, char* dst) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes_valid, kRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// One work item: split s of KV head kvh of sequence b, keys [k0, k1).
+struct Item {
+  int b, kvh, s, ns, L, k0, k1, nt;   // ns: splits of sequence b; nt: tiles of the item
+};
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-  constexpr int CH = D / 8;
-  constexpr int KLOADS = kKT * CH / 256;
-  constexpr int VTHREADS = (kKT / 4) * CH;
-  constexpr int KS = D / 32;      // k-steps of S^T (16x16x32)
-  constexpr int DB = D / 16;      // 16-row blocks of O^T
+__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int ROW = D * 2;           // bytes per row
+  constexpr int TB = kKT * ROW;        // bytes of one K or V tile
+  constexpr int NLD = kKT * CH / 64;   // 1 KB loads per tile per tensor
+  constexpr int KS = D / 32;           // k-steps of S^T (16x16x32)
+  constexpr int DB = D / 16;           // 16-row blocks of O^T
 
-  __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][kKT * D];
-  __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * kKT];
+  __shared__ __attribute__((aligned(1024))) char ring[kWaves][kNS][2][TB];
+  __shared__ int s_len[kMaxB];         // clamped sequence lengths
+  __shared__ int s_items[kMaxB + 1];   // items before sequence b
+  __shared__ int s_tiles[kMaxB + 1];   // tiles before sequence b
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
   const int lc = lane & 15, lg = lane >> 4;
+  const int C = a.kv_chunk;
+  const int TPS = C / kKT;             // tiles of a full split
 
-  // blockIdx.x = (b * Hkv + kvh) * max_splits + split
-  const int split = blockIdx.x % a.max_splits;
-  const int bh = blockIdx.x / a.max_splits;
-  const int kvh = bh % a.Hkv, b = bh / a.Hkv;
-  const int L = min(a.seq_lens[b], a.Lmax);   // never read past the cache window
-  const int k_begin = split * a.kv_chunk;
-  const int k_end = min(k_begin + a.kv_chunk, L);
-
-  float* o_part = a.o_part;
-  float* lse_part = a.lse_part;
-  if (k_begin >= k_end) {  // empty split: o = 0, lse = -inf
-    for (int x = tid; x < G * D; x += 256) {
-      const int col = x / D, d = x % D;
-      const int64_t row = ((int64_t)b * a.Hq + kvh * G + col) * a.max_splits + split;
-      o_part[row * D + d] = 0.f;
-      if (d == 0) lse_part[row] = -INFINITY;
-    }
-    return;
-  }
-
-  const __bf16* kbase = static_cast<const __bf16*>(a.k) + b * a.cs_b + kvh * a.cs_h;
-  const __bf16* vbase = static_cast<const __bf16*>(a.v) + b * a.cs_b + kvh * a.cs_h;
-
-  // Q operand (B of S^T = K Q^T): Q[col][32ks + 8lg + i]; columns >= G are 0.
-  bf16x8 qreg[KS];
-  {
-    const bool ok = lc < G;
-    const __bf16* qp = static_cast<const __bf16*>(a.q) + b * a.qs_b + (kvh * G + (ok ? lc : 0)) * a.qs_h + 8 * lg;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[ks] = ok ? load8(qp + 32 * ks) : zero_bf16x8();
-  }
-
-  f32x4 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
-
-  bf16x8 kr[KLOADS];
-  bf16x8 vr[4];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int n = 0; n < KLOADS; ++n) {
-      const int id = tid + 256 * n;
-      const int key = id / CH, c = id % CH;
-      const int j = kt + key;
-      kr[n] = j < k_end ? load8(kbase + j * a.cs_l + 8 * c) : zero_bf16x8();
-    }
-    if (tid < VTHREADS) {
-      const int kg = tid / CH, c = tid % CH;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = kt + 4 * kg + i;
-        vr[i] = j < k_end ? load8(vbase + j * a.cs_l + 8 * c) : zero_bf16x8();
+  // ---- item and tile tables (the stream order is b, kvh, split) --------------
+  for (int b = threadIdx.x; b < a.B; b += blockDim.x) s_len[b] = max(1, min(a.seq_lens[b], a.Lmax));
+  __syncthreads();
+  if (wave == 0) {
+    int ci = 0, ct = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+      const int b = b0 + lane;
+      int ni = 0, nt = 0;
+      if (b < a.B) {
+        const int L = s_len[b];
+        ni = ((L + C - 1) / C) * a.Hkv;
+        nt = ((L + kKT - 1) / kKT) * a.Hkv;
       }
-    }
-  };
-  auto store_tile = [&](int stage) {
-    __bf16* lk = lds_k[stage];
 #pragma unroll
-    for (int n = 0; n < KLOADS; ++n) {
-      const int id = tid + 256 * n;
-      const int key = id / CH, c = id % CH;
-      *reinterpret_cast<bf16x8*>(lk + key * D + 8 * (c ^ (key & (CH - 1)))) = kr[n];
-    }
-    if (tid < VTHREADS) {
-      __bf16* lv = lds_v[stage];
-      const int kg = tid / CH, c = tid % CH;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * c + e;
-        bf16x4 w;
-        w[0] = vr[0][e];
-        w[1] = vr[1][e];
-        w[2] = vr[2][e];
-        w[3] = vr[3][e];
-        *reinterpret_cast<bf16x4*>(lv + d * kKT + 4 * (kg ^ (d & 15))) = w;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int x = __shfl_up(ni, o), y = __shfl_up(nt, o);
+        if (lane >= o) {
+          ni += x;
+          nt += y;
+        }
       }
+      if (b < a.B) {
+        s_items[b + 1] = ci + ni;
+        s_tiles[b + 1] = ct + nt;
+      }
+      ci += __shfl(ni, 63);
+      ct += __shfl(nt, 63);
     }
-  };
-
-  const int n_tiles = (k_end - k_begin + kKT - 1) / kKT;
-  load_tile(k_begin);
-  store_tile(0);
+    if (lane == 0) {
+      s_items[0] = 0;
+      s_tiles[0] = 0;
+    }
+  }
   __syncthreads();
 
-  for (int n = 0; n < n_tiles; ++n) {
-    const int kt = k_begin + n * kKT;
-    const int stage = n & 1;
-    if (n + 1 < n_tiles) load_tile(kt + kKT);
-
-    const int wk0 = kt + 16 * wave;   // first key of this wave's slice
-    if (wk0 < k_end) {
-      const __bf16* lk = lds_k[stage];
-      const __bf16* lv = lds_v[stage];
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      const int key = 16 * wave + lc;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int c = 4 * ks + lg;
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lk + key * D + 8 * (c ^ (key & (CH - 1))));
-        s = mfma16k32(ka, qreg[ks], s);
-      }
-      // lane holds S^T[key = wk0 + 4lg + j][col = lc]
-      if (wk0 + 16 > k_end) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (wk0 + 4 * lg + j >= k_end) s[j] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m, mx);
-      const float mc = mnew * a.scale_log2;   // finite: the slice holds >= 1 key
-      const float alpha = fast_exp2(m * a.scale_log2 - mc);
-      m = mnew;
-      bf16x4 p;
-      float rs = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float e = fast_exp2(fmaf(s[j], a.scale_log2, -mc));
-        rs += e;
-        p[j] = to_bf16(e);
-      }
-      l = l * alpha + rs;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = 16 * db + lc;
-        const bf16x4 va = *reinterpret_cast<const bf16x4*>(lv + d * kKT + 4 * ((4 * wave + lg) ^ (d & 15)));
-        acc[db] = mfma16k16(va, p, acc[db]);
+  const int NI = uni(s_items[a.B]);
+  const int T = uni(s_tiles[a.B]);
+  auto item_at = [&](int i) -> Item {
+    int lo = 0, hi = a.B;   // s_items[lo] <= i < s_items[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (uni(s_items[mid]) <= i) lo = mid; else hi = mid;
+    }
+    Item it;
+    it.b = lo;
+    it.L = uni(s_len[lo]);
+    it.ns = (it.L + C - 1) / C;
+    const int r = i - uni(s_items[lo]);
+    it.kvh = r / it.ns;
+    it.s = r - it.kvh * it.ns;
+    it.k0 = it.s * C;
+    it.k1 = min(it.k0 + C, it.L);
+    it.nt = (it.k1 - it.k0 + kKT - 1) / kKT;
+    return it;
+  };
+  auto next_item = [&](Item& it) {   // the item after it in stream order (b, kvh, split)
+    if (++it.s == it.ns) {
+      it.s = 0;
+      if (++it.kvh == a.Hkv) {
+        it.kvh = 0;
+        ++it.b;
+        it.L = uni(s_len[it.b]);
+        it.ns = (it.L + C - 1) / C;
       }
     }
+    it.k0 = it.s * C;
+    it.k1 = min(it.k0 + C, it.L);
+    it.nt = (it.k1 - it.k0 + kKT - 1) / kKT;
+  };
+  auto start_tile = [&](int i) -> int {
+    if (i >= NI) return T;
+    const Item it = item_at(i);
+    return uni(s_tiles[it.b]) + it.kvh * ((it.L + kKT - 1) / kKT) + it.s * TPS;
+  };
+  auto first_item_from = [&](int64_t t) -> int {   // smallest i with start_tile(i) >= t
+    int lo = 0, hi = NI;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (start_tile(mid) >= t) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+  };
+  // this wave's share: the items starting in its equal slice of the tile stream
+  const int W = gridDim.x * kWaves;
+  const int gw = blockIdx.x * kWaves + wave;
+  const int i0 = first_item_from((int64_t)gw * T / W);
+  const int i1 = first_item_from((int64_t)(gw + 1) * T / W);
+  if (i0 >= i1) return;
 
-    if (n + 1 < n_tiles) store_tile(stage ^ 1);
-    __syncthreads();
+  // ---- per-lane constant offsets ---------------------------------------------
+  int koffv[NLD], voffv[NLD];
+#pragma unroll
+  for (int n = 0; n < NLD; ++n) {
+    const int p = n * 64 + lane;   // LDS chunk written by this lane
+    const int row = p / CH, ph = p % CH;
+    koffv[n] = (int)(row * a.cs_l * 2 + 16 * k_chunk<CH>(ph, row));
+    voffv[n] = (int)(row * a.cs_l * 2 + 16 * v_chunk<CH>(ph, row));
   }
-
-  // ---- merge the four waves' partial softmax states --------------------------
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  float* red = reinterpret_cast<float*>(&lds_k[0][0]);   // [4][16][D] accumulators
-  float* red_m = reinterpret_cast<float*>(&lds_v[0][0]); // [4][16]
-  float* red_l = red_m + 64;                              // [4][16]
+  // K operand (A of S^T = K Q^T): row lc, logical chunk 4ks + lg
+  const int k_lane = lc * ROW;
+  // V^T operand (A of O^T += V^T P^T, 16x16x16): group lg covers keys 4lg + 0..3;
+  // input lane L = lc addresses row 4lg + L/4 at d0 = 16db + 4(L%4)
+  const int vrow = 4 * lg + (lc >> 2);
+  int v_lane[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) red[(wave * 16 + lc) * D + 16 * db + 4 * lg + j] = acc[db][j];
-  if (lg == 0) {
-    red_m[wave * 16 + lc] = m;
-    red_l[wave * 16 + lc] = l;
-  }
-  __syncthreads();
-  for (int x = tid; x < G * (D / 4); x += 256) {
-    const int col = x / (D / 4), d0 = 4 * (x % (D / 4));
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w * 16 + col]);
-    const float Mc = M * a.scale_log2;
-    float Ltot = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float e = fast_exp2(red_m[w * 16 + col] * a.scale_log2 - Mc);   // 0 for an idle wave
-      Ltot += e * red_l[w * 16 + col];
-      const f32x4 v = *reinterpret_cast<const f32x4*>(&red[(w * 16 + col) * D + d0]);
-      o += e * v;
+    v_lane[db] = vrow * ROW + 16 * v_chunk<CH>(2 * db + ((lc >> 1) & 1), vrow) + 8 * (lc & 1);
+
+  char* my = &ring[wave][0][0][0];
+
+  // ---- load cursor over the wave's tile stream --------------------------------
+  int li = i0, lt = 0;
+  Item lit = item_at(i0);
+  auto issue = [&](int st) {
+    const __bf16* kb = static_cast<const __bf16*>(a.k);
+    const __bf16* vb = static_cast<const __bf16*>(a.v);
+    int bytes = 0;   // past the stream end: loads that read nothing keep the count uniform
+    if (li < i1) {
+      const int key = lit.k0 + lt * kKT;
+      const int64_t base = lit.b * a.cs_b + lit.kvh * a.cs_h + (int64_t)key * a.cs_l;
+      kb += base;
+      vb += base;
+      const int rows = min(kKT, lit.k1 - key);
+      bytes = (int)(((int64_t)(rows - 1) * a.cs_l + D) * 2);
+      if (++lt == lit.nt) {
+        ++li;
+        lt = 0;
+        if (li < i1) next_item(lit);
+      }
     }
-    const int64_t row = ((int64_t)b * a.Hq + kvh * G + col) * a.max_splits + split;
-    *reinterpret_cast<f32x4*>(&o_part[row * D + d0]) = o / Ltot;
-    if (d0 == 0) lse_part[row] = M * a.scale + fast_log2(Ltot) * kLn2;
+    char* dst = my + st * 2 * TB;
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+      load_lds16(kb, bytes, koffv[n], dst + n * 1024);
+      load_lds16(vb, bytes, voffv[n], dst + TB + n * 1024);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < kNS - 1; ++s) issue(s);
+
+  // ---- compute cursor -------------------------------------------------------------
+  bf16x8 qreg[KS];
+  f32x4 acc[DB];
+  float m = -INFINITY, l = 0.f;
+  int ci = i0, ct = 0, run_s0 = 0;
+  Item cit = item_at(i0);
+  for (int p = 0; ci < i1; ++p) {
+    if (ct == 0 && (ci == i0 || cit.s == 0)) {   // a run of this (b, kvh) starts
+      const bool ok = lc < G;
+      const __bf16* qp = static_cast<const __bf16*>(a.q) + cit.b * a.qs_b +
+                         (cit.kvh * G + (ok ? lc : 0)) * a.qs_h + 8 * lg;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qreg[ks] = ok ? load8(qp + 32 * ks) : zero_bf16x8();
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m = -INFINITY;
+      l = 0.f;
+      run_s0 = cit.s;
+    }
+    // tile p has landed once no more than the loads of tiles p+1 .. p+kNS-2 are pending
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NLD * (kNS - 2)) : "memory");
+    issue((p + kNS - 1) % kNS);
+
+    const char* lk = my + (p % kNS) * 2 * TB;
+    const char* lv = lk + TB;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lk + k_lane + 16 * k_chunk<CH>(4 * ks + lg, lc));
+      s = mfma16k32(ka, qreg[ks], s);
+    }
+    // lane holds S^T[key = key0 + 4lg + j][col = lc]
+    const int kbase = cit.k0 + ct * kKT + 4 * lg;
+    if (cit.k0 + (ct + 1) * kKT > cit.k1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (kbase + j >= cit.k1) s[j] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool mv = mx * a.scale_log2 > m * a.scale_log2 + kLazy;
+    if (__any(mv)) {   // rare after a run's first tile
+      const float al = mv ? fast_exp2((m - mx) * a.scale_log2) : 1.f;   // 0 when m = -inf
+      m = mv ? mx : m;
+      l *= al;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= al;
+    }
+    const float mc = m * a.scale_log2;   // finite: the tile holds at least one key
+    bf16x2 p01, p23;
+    p01[0] = to_bf16(fast_exp2(fmaf(s[0], a.scale_log2, -mc)));
+    p01[1] = to_bf16(fast_exp2(fmaf(s[1], a.scale_log2, -mc)));
+    p23[0] = to_bf16(fast_exp2(fmaf(s[2], a.scale_log2, -mc)));
+    p23[1] = to_bf16(fast_exp2(fmaf(s[3], a.scale_log2, -mc)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    l = __builtin_amdgcn_fdot2_f32_bf16(p01, one, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16(p23, one, l, false);
+    const bf16x4 pv = {p01[0], p01[1], p23[0], p23[1]};
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lv + v_lane[db]));
+      acc[db] = mfma16k16(__builtin_bit_cast(bf16x4, r), pv, acc[db]);
+    }
+
+    if (++ct == cit.nt) {   // item done
+      if (ci + 1 == i1 || cit.s + 1 == cit.ns) {   // run done: its partial goes to slot run_s0
+        float lt2 = l + __shfl_xor(l, 16);
+        lt2 += __shfl_xor(lt2, 32);
+        if (lc < G) {
+          const int64_t row = ((int64_t)cit.b * a.Hq + cit.kvh * G + lc) * a.max_splits;
+          float* op = a.o_part + (row + run_s0) * D;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<f32x4*>(op + 16 * db + 4 * lg) = acc[db] / lt2;
+          if (lg == 0) a.lse_part[row + run_s0] = m * a.scale + fast_log2(lt2) * kLn2;
+          for (int s2 = run_s0 + 1 + lg; s2 <= cit.s; s2 += 4) a.lse_part[row + s2] = -INFINITY;
+        }
+      }
+      ++ci;
+      ct = 0;
+      if (ci < i1) next_item(cit);
+    }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // loads past the stream end
 }
 
 template <int D>
@@ -231,16 +326,24 @@ __global__ __launch_bounds__(256) void combine_kernel_f(CombineArgs a, int dt) {
   const float* lp = a.lse_part + (int64_t)pair * a.max_splits;
   const float* op = a.o_part + (int64_t)pair * a.max_splits * D;
   float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, lp[s]);
+  for (int s = lane; s < n; s += 64) M = fmaxf(M, lp[s]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float W = 0.f;
   float o[D / 64];
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) o[i] = 0.f;
-  for (int s = 0; s < n; ++s) {
-    const float w = expf(lp[s] - M);
-    W += w;
+  for (int s0 = 0; s0 < n; s0 += 64) {   // slots with lse = -inf carry nothing and are skipped
+    const float ls = s0 + lane < n ? lp[s0 + lane] : -INFINITY;
+    uint64_t live = __ballot(ls != -INFINITY);
+    while (live) {
+      const int j = __builtin_ctzll(live);
+      live &= live - 1;
+      const float w = expf(__shfl(ls, j) - M);
+      W += w;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) o[i] += w * op[(int64_t)s * D + lane + 64 * i];
+      for (int i = 0; i < D / 64; ++i) o[i] += w * op[(int64_t)(s0 + j) * D + lane + 64 * i];
+    }
   }
   if (dt == 0) {
     __bf16* out = static_cast<__bf16*>(a.o) + b * a.os_b + h * a.os_h;
@@ -254,10 +357,19 @@ __global__ __launch_bounds__(256) void combine_kernel_f(CombineArgs a, int dt) {
   if (a.lse && lane == 0) a.lse[pair] = M + logf(W);
 }
 
+int g_num_cu = 0;   // the grid size only shapes the work split, never the result
+
 template <int D, int G>
 hipError_t launch_dt(const DecodeArgs& a, hipStream_t st) {
-  const unsigned grid = (unsigned)a.B * a.Hkv * a.max_splits;
-  hipLaunchKernelGGL((decode_kernel<D, G>), dim3(grid), dim3(256), 0, st, a);
+  if (g_num_cu == 0) {
+    int dev = 0;
+    hipGetDevice(&dev);
+    hipDeviceGetAttribute(&g_num_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (g_num_cu <= 0) g_num_cu = 256;
+  }
+  // persistent grid: one workgroup per CU (the LDS ring takes most of a CU's LDS)
+  const unsigned grid = (unsigned)g_num_cu;
+  hipLaunchKernelGGL((decode_kernel<D, G>), dim3(grid), dim3(64 * kWaves), 0, st, a);
   return hipGetLastError();
 }
 

@@ -63,6 +63,9 @@ struct CombineArgs {
 // Launchers: return hipSuccess or the launch error. dt: 0 = bf16, 1 = fp32.
 hipError_t launch_rope_pair(const RopeArgs& q, const RopeArgs& k, int D, int dt, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int D, int G, int dt, hipStream_t st);
+// Sequences per gqa_decode call (the kernel keeps per-sequence tables in LDS).
+constexpr int kDecodeMaxBatch = 1024;
+
 hipError_t launch_decode(const DecodeArgs& a, int D, int G, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int D, int dt, hipStream_t st);
 

@@ -100,6 +100,9 @@ la_status gqa_prefill(const void* q, const void* k, const void* v, void* o, floa
   if (!strides_ok(q_strides, 3, es) || !strides_ok(k_strides, 3, es) ||
       !strides_ok(v_strides, 3, es) || !strides_ok(o_strides, 3, es))
     return LA_ERR_INVALID_ARG;
+  // key/value rows of consecutive tokens may not overlap (tiles are fetched
+  // with a byte range that ends at the last token's row)
+  if (k_strides[1] < D || v_strides[1] < D) return LA_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return LA_ERR_INVALID_ARG;
   const int G = Hq / Hkv;
   const int tq = la::prefill_tokens_per_block(G);
@@ -137,6 +140,13 @@ la_status gqa_decode(const void* q, const int64_t q_strides[2], const void* k_ca
   if (!strides_ok(q_strides, 2, 2) || !strides_ok(cache_strides, 3, 2)) return LA_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return LA_ERR_INVALID_ARG;
   if ((long long)B * Hkv * max_splits > 0x7fffffffLL) return LA_ERR_INVALID_ARG;
+  if ((long long)B * Hkv * ((Lmax + 15) / 16) > 0x7fffffffLL) return LA_ERR_INVALID_ARG;
+  if ((long long)B * Hq * max_splits * D > 0x7fffffffffffLL) return LA_ERR_INVALID_ARG;
+  if (B > la::kDecodeMaxBatch) return LA_ERR_UNSUPPORTED;
+  // cache rows may not overlap, and a 16-key tile must span less than 2 GiB
+  // (32-bit buffer range)
+  if (cache_strides[2] < D) return LA_ERR_INVALID_ARG;
+  if (cache_strides[2] > (1LL << 24)) return LA_ERR_UNSUPPORTED;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
 
   la::DecodeArgs a{};

@@ -88,7 +88,8 @@ la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
  * on queries and keys that are ALREADY ROTATED (see rope_qk) [P2, P4].
  *
  * q: [B, S, Hq, D], k and v: [B, S, Hkv, D], o: [B, S, Hq, D], all of type
- * `dt`, strides (b, s, h) in q_strides, k_strides, v_strides, o_strides.
+ * `dt`, strides (b, s, h) in q_strides, k_strides, v_strides, o_strides; the
+ * token strides of k and v are at least D (rows do not overlap).
  * cu_docs: int32 [B, n_docs + 1], row b non-decreasing from 0 to S: document
  *   d of sequence b is the token range [cu_docs[b][d], cu_docs[b][d+1])
  *   (empty documents are allowed and hold no token). NULL means one document
@@ -119,20 +120,27 @@ la_status gqa_prefill(const void* q, const void* k, const void* v, void* o, floa
  * q: bf16 [B, Hq, D], strides q_strides = (b, h), already rotated at position
  *   seq_lens[b] - 1.
  * k_cache, v_cache: bf16 [B, Hkv, Lmax, D] with strides cache_strides =
- *   (b, h, l) shared by both; slots 0..seq_lens[b]-1 hold the rotated keys and
+ *   (b, h, l) shared by both, D <= l-stride <= 2^24; slots 0..seq_lens[b]-1 hold the rotated keys and
  *   the values of every token of sequence b, the new token included.
  * seq_lens: int32 [B] on the device, 1 <= seq_lens[b] <= Lmax.
  * Split s of sequence b covers cache slots [s*kv_chunk, min((s+1)*kv_chunk,
- *   seq_lens[b])); every slot of the cache window is visible.
+ *   seq_lens[b])), s < n_b = ceil(seq_lens[b] / kv_chunk); every slot of the
+ *   cache window is visible.
  * o_part: fp32 [B, Hq, max_splits, D], lse_part: fp32 [B, Hq, max_splits]
- *   (contiguous, caller-owned workspace of B*Hq*max_splits*(D+1)*4 bytes):
- *   the split's softmax-normalised output and natural-log log-sum-exp; a
- *   split with no slots gets o = 0 and lse = -inf.
+ *   (contiguous, caller-owned workspace of B*Hq*max_splits*(D+1)*4 bytes).
+ *   For each (b, h) the splits s < n_b are covered by runs of consecutive
+ *   splits; a run starting at split s stores at slot s the softmax-normalised
+ *   output and natural-log log-sum-exp over all keys of the run, and its other
+ *   slots get lse = -inf (their o is left unwritten). Slots s >= n_b are not
+ *   written. Merging the slots s < n_b by their log-sum-exp weights (as
+ *   gqa_decode_combine does) gives the attention output; the grouping into
+ *   runs depends on the device and may change between calls.
  * Requirements: kv_chunk a positive multiple of 64; max_splits >=
- *   ceil(Lmax / kv_chunk); dt of q and caches is bf16 only.
+ *   ceil(Lmax / kv_chunk); B <= 1024; dt of q and caches is bf16 only.
  * Errors: INVALID_ARG for null pointers, sizes < 1, kv_chunk not a multiple
- * of 64, max_splits too small, bad strides or alignment; UNSUPPORTED for D
- * or group size outside the supported set.
+ * of 64, max_splits too small, sizes whose index arithmetic would overflow,
+ * bad strides or alignment; UNSUPPORTED for D or group size outside the
+ * supported set, or B > 1024.
  */
 la_status gqa_decode(const void* q, const int64_t q_strides[2],
                      const void* k_cache, const void* v_cache, const int64_t cache_strides[3],
@@ -143,8 +151,9 @@ la_status gqa_decode(const void* q, const int64_t q_strides[2],
 /*
  * gqa_decode_combine — merge the split partials of gqa_decode by their
  * log-sum-exp weights: with M = max_s lse_s and w_s = exp(lse_s - M),
- * o = sum_s w_s o_s / sum_s w_s and lse = M + ln(sum_s w_s), over the splits
- * s < ceil(seq_lens[b] / kv_chunk).
+ * o = sum_s w_s o_s / sum_s w_s and lse = M + ln(sum_s w_s), over the slots
+ * s < ceil(seq_lens[b] / kv_chunk) (min max_splits); slots with lse = -inf
+ * carry no weight and their o is not read.
  * o: [B, Hq, D] of type dt (bf16 or fp32) with strides o_strides = (b, h);
  * lse: optional fp32 [B, Hq] (contiguous), NULL to skip.
  * Errors: as gqa_decode for the shared arguments; UNSUPPORTED for D not in
