@@ -129,6 +129,51 @@ def rope_attention(q, k, v, cu_docs=None, base: float = 500000.0, positions=None
                      cu_docs, scale, rows)
 
 
+def rope_attention_rows(q, k, v, rows, cu_docs=None, base: float = 500000.0,
+                        scale: Optional[float] = None, block: int = 64
+                        ) -> Tuple[np.ndarray, np.ndarray]:
+    """``rope_attention`` of one sequence, restricted to the query rows asked
+    for, at sizes where rotating every token in fp64 is out of reach.
+
+    q [S,Hq,D], k and v [S,Hkv,D] (raw, unrotated; any array type), rows the
+    token indices to evaluate. Row i sees keys j in [start of its document, i];
+    only those keys and the asked-for query rows are rotated (at their token
+    index) and converted to fp64, one document at a time. Returns O [R,Hq,D]
+    and LSE [Hq,R] for the rows in the order given.
+    """
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    cu = np.asarray([0, S] if cu_docs is None else cu_docs, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    doc = document_of(cu, S)
+    O = np.zeros((rows.size, Hq, D))
+    LSE = np.zeros((Hq, rows.size))
+    for d in np.unique(doc[rows]):
+        sel = np.flatnonzero(doc[rows] == d)
+        lo, hi = int(cu[d]), int(rows[sel].max()) + 1
+        kr = rope(k[lo:hi], np.arange(lo, hi), base)            # [W, Hkv, D]
+        vw = _f64(v[lo:hi])
+        for b0 in range(0, sel.size, block):
+            idx = sel[b0:b0 + block]
+            ri = rows[idx]
+            qr = rope(q[ri], ri, base)                         # [n, Hq, D]
+            visible = np.arange(lo, hi)[None, :] <= ri[:, None]
+            n = ri.size
+            for kv in range(Hkv):
+                heads = slice(kv * g, (kv + 1) * g)
+                s = (qr[:, heads, :].reshape(n * g, D) @ kr[:, kv, :].T).reshape(n, g, hi - lo) * scale
+                s = np.where(visible[:, None, :], s, -np.inf)
+                m = s.max(axis=2, keepdims=True)
+                e = np.exp(s - m)
+                l = e.sum(axis=2, keepdims=True)
+                pv = (e.reshape(n * g, hi - lo) @ vw[:, kv, :]).reshape(n, g, D)
+                O[idx, heads, :] = pv / l
+                LSE[heads, idx] = (m + np.log(l))[:, :, 0].T
+    return O, LSE
+
+
 def _decode_scores(qb, kb, scale):
     # qb [g, D] (the g query heads of one KV head), kb [L, D] -> [g, L]
     return (qb @ kb.T) * scale

@@ -74,41 +74,11 @@ def test_decode_matches_oracle(B, Hq, Hkv, D, lens, Lmax, chunks):
         H.say("decode", B, Hq, Hkv, D, tuple(lens), "chunk", chunk)
         op, lp, o, lse = run_decode(qr, kc, vc, lens, chunk)
         max_splits = op.shape[2]
-        n_runs = check_partials(op, lp, q_rot, k_rot, vs, lens, chunk)
+        n_runs = H.check_partials(op, lp, q_rot, k_rot, vs, lens, chunk)
         H.say("  runs", n_runs, "of splits", Hq * int(sum(-(-int(L) // chunk) for L in lens)))
         H.assert_close(o, Ow)
         H.assert_close(lse, Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
 
-
-def check_partials(op, lp, q_rot, k_rot, vs, lens, chunk):
-    """The workspace holds runs of consecutive splits: a finite lse at slot s
-    starts a run that ends at the next finite slot (or at the last split); its
-    o and lse are those of all keys of the run, i.e. the oracle's per-split
-    partials merged over the run. Slot 0 always starts a run, and slots past
-    the last split are never written (they keep the NaN fill)."""
-    op, lp = op.numpy(), lp.numpy()
-    max_splits = op.shape[2]
-    opw, lpw = orc.decode_partials(q_rot, k_rot, vs, lens, chunk, max_splits)
-    got_o, got_l, want_o, want_l = [], [], [], []
-    n_runs = 0
-    for b, L in enumerate(lens):
-        n = -(-int(L) // chunk)
-        assert np.isnan(lp[b, :, n:]).all() and np.isnan(op[b, :, n:]).all()
-        for h in range(lp.shape[1]):
-            live = np.flatnonzero(np.isfinite(lp[b, h, :n]))
-            assert live.size and live[0] == 0
-            assert np.isneginf(np.delete(lp[b, h, :n], live)).all()
-            ends = list(live[1:]) + [n]
-            for s, t in zip(live, ends):
-                mo, ml = orc.combine(opw[b, h, s:t], lpw[b, h, s:t])
-                got_o.append(op[b, h, s])
-                got_l.append(lp[b, h, s])
-                want_o.append(mo)
-                want_l.append(ml)
-                n_runs += 1
-    H.assert_close(np.array(got_o), np.array(want_o), what="o_part runs")
-    H.assert_close(np.array(got_l), np.array(want_l), H.LSE_MAX_ABS, H.LSE_MAX_ABS, "lse_part runs")
-    return n_runs
 
 
 def test_decode_equals_last_row_of_gpu_prefill():

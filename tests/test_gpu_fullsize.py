@@ -1,0 +1,120 @@
+"""The full-size workloads on the GPU, in the launch configuration bench.py
+times: rope_qk then gqa_prefill over the whole packed sequence, and
+gqa_decode + gqa_decode_combine over the whole cache with bench.py's kv_chunk.
+
+Outputs the oracle cannot afford everywhere are checked on sampled query rows
+(every document's first and last row, rows either side of drawn 64-row tile
+edges, uniformly drawn rows) against the fp64 row oracle; closed-form probes
+(q = 0: uniform attention over the visible keys) check the mask and the head
+mapping exactly over every row and head.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_helpers as H
+from oracle import reference as orc
+from workloads import CONFIGS, draw_cu_docs, draw_prefill_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+# sampled rows per workload: (uniform draws, tile edges drawn)
+SAMPLES = {"llama8b": (2048, None), "llama405b": (384, 64), "long128k": (96, 32)}
+
+
+def _run_full_prefill(q, k, v, cu):
+    """rope_qk + gqa_prefill exactly as bench.py launches them; device outputs."""
+    import gqa_attention_rope_02_amd as la
+    dev = torch.device("cuda")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    qr, kr = torch.empty_like(qd), torch.empty_like(kd)
+    la.rope_qk(qd, qr, kd, kr)
+    del qd, kd
+    o = torch.full_like(qr, float("nan"))
+    lse = torch.full((q.shape[0], q.shape[2], q.shape[1]), float("nan"), device=dev)
+    cu_d = torch.as_tensor(cu, dtype=torch.int32).reshape(1, -1).to(dev)
+    la.gqa_prefill(qr, kr, vd, o, lse, cu_d)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("name", ["llama8b", "llama405b", "long128k"])
+def test_full_size_prefill_sampled_rows(name):
+    w = CONFIGS[name]
+    H.say("full-size prefill", name, w.S, w.Hq, w.Hkv)
+    q, k, v = draw_prefill_inputs(w.B, w.S, w.Hq, w.Hkv, w.D, w.dtype, w.seed)
+    cu = draw_cu_docs(w.S, w.seed, w.n_docs, w.n_docs_max)
+    o, lse = _run_full_prefill(q, k, v, cu)
+    n_random, n_edges = SAMPLES[name]
+    rows = sample_rows(w.S, cu, w.seed, n_random=n_random, n_edges=n_edges)
+    idx = torch.as_tensor(rows, device=o.device)
+    got_o = o[0].index_select(0, idx).cpu()
+    got_l = lse[0].index_select(1, idx).cpu()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    del o, lse
+    Ow, Lw = orc.rope_attention_rows(q[0], k[0], v[0], rows, cu, w.rope_base)
+    H.say("  rows", rows.size)
+    H.assert_close(got_o, Ow)
+    H.assert_close(got_l, Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+
+
+@pytest.mark.parametrize("name", ["llama8b", "llama405b", "long128k"])
+def test_full_size_prefill_exact_probes(name):
+    """q = 0 makes every visible key weigh 1: exp(LSE) is the exact count of
+    visible keys; a V channel holding the document index comes back exactly
+    (only same-document keys mix); one holding the KV head index comes back as
+    h // g for query head h."""
+    w = CONFIGS[name]
+    H.say("full-size probes", name)
+    dev = torch.device("cuda")
+    cu = draw_cu_docs(w.S, w.seed, w.n_docs, w.n_docs_max)
+    doc = orc.document_of(cu, w.S)
+    _, k, v = draw_prefill_inputs(w.B, w.S, 1, w.Hkv, w.D, w.dtype, w.seed)
+    v[0, :, :, 0] = torch.as_tensor(doc, dtype=torch.bfloat16)[:, None]
+    v[0, :, :, 1] = torch.arange(w.Hkv, dtype=torch.bfloat16)[None, :]
+    q = torch.zeros(w.B, w.S, w.Hq, w.D, dtype=torch.bfloat16, device=dev)
+    o, lse = _run_full_prefill(q, k, v, cu)
+    g = w.Hq // w.Hkv
+    count = np.arange(w.S) - cu[doc] + 1
+    got = np.rint(np.exp(lse[0].double().cpu().numpy()))
+    assert np.array_equal(got, np.broadcast_to(count, (w.Hq, w.S)))
+    ch = o[0, :, :, :2].float().cpu().numpy()
+    assert np.array_equal(ch[:, :, 0], np.broadcast_to(doc[:, None], (w.S, w.Hq)))
+    assert np.array_equal(ch[:, :, 1], np.broadcast_to((np.arange(w.Hq) // g)[None, :], (w.S, w.Hq)))
+
+
+def test_full_size_decode_sampled_heads():
+    """The 405B-shape decode of bench.py (16 sequences, cache lengths up to
+    128K, 128 query heads on 8 KV heads, its kv_chunk): for every sequence the
+    16 query heads of two KV heads against the oracle, and the partial-result
+    workspace of those heads (runs of merged splits) against the oracle's
+    per-split partials merged over each run."""
+    import bench
+    import gqa_attention_rope_02_amd as la
+    H.say("full-size decode405b")
+    st = bench.setup_decode()
+    w, lens, chunk = st["w"], st["lens"], bench.KV_CHUNK
+    op = torch.full_like(st["op"], float("nan"))
+    lp = torch.full_like(st["lp"], float("nan"))
+    o = torch.full_like(st["o"], float("nan"))
+    lse = torch.full((w.B, w.Hq), float("nan"), device=o.device)
+    la.gqa_decode(st["q"], st["kc"], st["vc"], st["sl"], chunk, op, lp)
+    la.gqa_decode_combine(op, lp, st["sl"], chunk, o, lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    g = w.Hq // w.Hkv
+    n_runs = 0
+    for b in range(w.B):
+        L = int(lens[b])
+        for kvh in (b % w.Hkv, (b + 3) % w.Hkv):
+            heads = slice(kvh * g, (kvh + 1) * g)
+            qb = st["q"][b:b + 1, heads].cpu()
+            kb = [st["kc"][b, kvh:kvh + 1, :L].cpu()]
+            vb = [st["vc"][b, kvh:kvh + 1, :L].cpu()]
+            Ow, Lw = orc.decode(qb, kb, vb, [L])
+            H.assert_close(o[b:b + 1, heads].cpu(), Ow, what=f"O b={b} kvh={kvh}")
+            H.assert_close(lse[b:b + 1, heads].cpu(), Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+            n_runs += H.check_partials(op[b:b + 1, heads].cpu(), lp[b:b + 1, heads].cpu(),
+                                       qb, kb, vb, [L], chunk)
+    H.say("  runs checked", n_runs)

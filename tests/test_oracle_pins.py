@@ -45,6 +45,32 @@ def test_brute_force_equals_oracle(seed, S, Hq, Hkv, D, ndocs, pos):
     np.testing.assert_allclose(L, np.array(Lb), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("seed,S,Hq,Hkv,D,ndocs", [(7, 15, 4, 2, 8, 3), (8, 12, 8, 1, 6, 1)])
+def test_brute_force_equals_row_oracle(seed, S, Hq, Hkv, D, ndocs):
+    """The row-restricted oracle (rotating only the rows and document windows it
+    needs) against brute force, rows in a scrambled order."""
+    q, k, v = _tiny(seed, 1, S, Hq, Hkv, D, "bf16")
+    cu = draw_cu_docs(S, seed, n_docs=ndocs)
+    rows = np.random.default_rng(seed).permutation(S)[: S - 2]
+    O, L = orc.rope_attention_rows(q[0], k[0], v[0], rows, cu, 500000.0)
+    qb, kb, vb = (x.double().numpy().tolist() for x in (q, k, v))
+    Ob, Lb = brute.brute_rope_attention(qb, kb, vb, cu.tolist(), 500000.0)
+    np.testing.assert_allclose(O, np.array(Ob)[0][rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, np.array(Lb)[0][:, rows], rtol=0, atol=1e-12)
+
+
+def test_row_oracle_matches_block_oracle_at_moderate_size():
+    """Many documents, GQA 4:1, rows spanning block and document edges."""
+    S, Hq, Hkv, D = 700, 16, 4, 64
+    q, k, v = draw_prefill_inputs(1, S, Hq, Hkv, D, "bf16", 9)
+    cu = draw_cu_docs(S, 9, n_docs_max=8)
+    rows = np.unique(np.concatenate([cu[:-1], cu[1:] - 1, np.arange(0, S, 37), [63, 64, 65]]))
+    O, L = orc.rope_attention_rows(q[0], k[0], v[0], rows, cu, 500000.0, block=16)
+    Ow, Lw = orc.rope_attention(q, k, v, cu, 500000.0, rows=rows)
+    np.testing.assert_allclose(O, Ow[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, Lw[0], rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------- library routine
 
 def _torch_rope_complex(x, positions, base):
