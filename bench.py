@@ -185,6 +185,31 @@ def decode_bytes(st) -> float:
     return float(np.sum(st["lens"].astype(np.int64))) * w.Hkv * w.D * 2 * 2
 
 
+# ------------------------------------------------------------ counter scale
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(reps: int = 3):
+    """A plain elementwise device copy of COPY_BYTES (read once, written once):
+    what FETCH_SIZE and WRITE_SIZE read for it is the scale that turns those
+    counters into HBM bytes for the attention kernels of the same run."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"kernel": "elementwise mul by 1.0 (plain copy)", "bytes_read": COPY_BYTES,
+            "bytes_written": COPY_BYTES, "ms": round(ms, 4),
+            "gbs": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}
+
+
 # ----------------------------------------------------------------- cpu oracle
 
 def cpu_baseline(host_inputs, w, cu, budget_s: float = 20.0):
@@ -224,8 +249,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "llama8b", "llama405b", "decode405b", "copy"],
+                    default=None, help="run one part: both prefills, the decode, one workload, "
+                                       "or only the copy used to scale HBM counters")
     ap.add_argument("--with-128k", action="store_true", help="also time the S=131072 prefill")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain device copy of known size (scale for FETCH/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -242,8 +271,17 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) Q/K/V, seeded document cuts)"}
     phash = kernel_hash("gqa_prefill.hip")
+    run_8b = args.only in (None, "prefill", "llama8b")
+    run_405 = args.only in (None, "prefill", "llama405b")
+    run_dec = args.only in (None, "decode", "decode405b")
 
-    if args.only in (None, "prefill"):
+    if args.calibrate_copy or args.only == "copy":
+        out["copy_calibration"] = copy_calibration()
+        if args.only == "copy":
+            out.update(value=out["copy_calibration"]["gbs"], unit="GB/s",
+                       config={"workload": "plain device copy of 1 GiB"})
+
+    if run_8b:
         st, host = setup_prefill("llama8b")
         w, cu = st["w"], st["cu"]
         t = time_prefill(st, args.steps, args.warmup)
@@ -268,6 +306,7 @@ def main():
             out["cpu_baseline"] = cpu_baseline(host, w, cu)
         del st
 
+    if run_405:
         st3, _ = setup_prefill("llama405b")
         t3 = time_prefill(st3, max(3, args.steps // 2), args.warmup)
         fl3 = prefill_flops(st3["w"], st3["cu"])
@@ -279,6 +318,10 @@ def main():
             "frac_kernel": round(fl3 / (t3["prefill_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "ms_per_step": round(t3["gpu_ms_per_step"], 4), "prefill_ms": round(t3["prefill_ms"], 4),
             "rope_ms": round(t3["rope_ms"], 4), "traffic": measured_traffic("gqa_prefill", "llama405b", phash)}
+        if not run_8b:
+            out.update(value=out["prefill_405b"]["tflops_path"], unit="TFLOP/s",
+                       ms_per_step=out["prefill_405b"]["ms_per_step"],
+                       config={"workload": out["prefill_405b"]["workload"]})
         del st3
         if args.with_128k:
             st5, _ = setup_prefill("long128k")
@@ -292,7 +335,7 @@ def main():
             del st5
         torch.cuda.empty_cache()
 
-    if args.only in (None, "decode"):
+    if run_dec:
         sd = setup_decode()
         td = time_decode(sd, args.steps, args.warmup)
         nbytes = decode_bytes(sd)
@@ -308,7 +351,7 @@ def main():
                          "traffic": measured_traffic("gqa_decode", "decode405b", dhash),
                          "launch_ms": round(td["decode_ms"], 4)},
             "combine_ms": round(td["combine_ms"], 4)}
-        if args.only == "decode":
+        if not (run_8b or run_405):
             out.update(value=round(gbs, 1), unit="GB/s", ms_per_step=round(td["ms_per_step"], 4),
                        config={"workload": out["decode_405b"]["workload"]},
                        roofline=out["decode_405b"]["roofline"])
