@@ -11,9 +11,8 @@
 // How (gfx950):
 // * One workgroup = one (sequence, KV head, tile of 256/g tokens): its 256
 //   "columns" are the (token, query head) pairs of the g heads sharing the KV
-//   head, so each K/V byte staged in LDS feeds 256 query rows. Four waves own
-//   64 columns each (one wave per SIMD; 64 columns per wave keep the LDS
-//   operand traffic at half of what the LDS delivers at full MFMA rate).
+//   head, so each K/V byte staged in LDS feeds 256 query rows. Eight waves own
+//   32 columns each, two waves per SIMD.
 // * The contractions run transposed on the 32x32x16 bf16 MFMA: S^T = K Q^T
 //   (keys on M, columns on N) and O^T = V^T P^T (head_dim on M). In both
 //   results a lane owns one column, so the softmax statistics and the output
@@ -22,25 +21,27 @@
 //   already has the layout of the P^T operand.
 // * Q stays in registers for the whole key loop. K and V tiles of 64 keys go
 //   from HBM straight into LDS (buffer_load_dwordx4 ... lds, no register
-//   staging), row-major with XOR swizzles, double buffered: the next tile's
-//   loads are in flight while the current one is consumed. The buffer
-//   descriptor moves with the tile and its size ends at the sequence end, so
-//   rows past the end read as zero. K operands are read with ds_read_b128; the
-//   V^T operand with the transposing ds_read_b64_tr_b16 from the row-major V
-//   tile.
-// * Each 64-key tile is consumed in two 32-key halves, software pipelined so
-//   that the softmax VALU work of one half is issued between the MFMAs of the
-//   next product: QK(0); QK(1) with softmax(0); PV(0) with softmax(1); PV(1).
+//   staging), row-major with XOR swizzles, through four stages: a tile is
+//   issued three tiles before it is read. The buffer descriptor moves with the
+//   tile and its size ends at the sequence end, so rows past the end read as
+//   zero. K operands are read with ds_read_b128; the V^T operand with the
+//   transposing ds_read_b64_tr_b16 from the row-major V tile.
+// * The two waves of a SIMD run one phase apart ("ping-pong"): each wave
+//   alternates an MFMA phase (PV of tile k and QK of tile k+1: 32 MFMAs and
+//   their 48 operand reads, kept eight reads ahead) with a softmax phase
+//   (mask, max, exp, bf16 rounding, row sums of tile k+1), every phase ends at
+//   a workgroup barrier, and the other wave of the SIMD is then in the other
+//   kind of phase. On gfx950 the VALU work of one wave and the MFMAs of the
+//   other do not run concurrently; what the offset buys is that each wave's
+//   waits (MFMA results, LDS reads, exp latency) are filled by the other.
 // * Online softmax in the base-2 domain with fp32 statistics; probabilities
 //   are rounded to bf16 once and the row sums accumulate those rounded values
 //   (v_dot2_f32_bf16), so numerator and denominator use the same weights. The
 //   reference the exponents are taken against moves only when a score exceeds
 //   it by more than 2^8 (exact: softmax does not depend on the reference, and
-//   the weights stay below 256), so the accumulator is almost never rescaled;
-//   a per-tile exact max would force a rescale in most tiles, since with 64
-//   columns per wave some column nearly always finds a new maximum. Masks are
-//   evaluated only on tiles that cross a causal or document edge of the
-//   wave's columns.
+//   the weights stay below 256), so the accumulator is almost never rescaled.
+//   Masks are evaluated only on tiles that cross a causal or document edge of
+//   the wave's columns.
 // * Workgroups are issued longest-first (last token tiles first), and the KV
 //   head is the fastest-varying index so the workgroups of one KV head land on
 //   one XCD (blockIdx % 8) and share its L2.
@@ -58,6 +59,10 @@ constexpr int kCB = kCols / kNW / 32;   // 32-column blocks per wave
 constexpr int kKT = 64;       // keys per tile
 constexpr float kLazy = 8.f;  // log2 headroom of the lazily moved softmax reference
 constexpr int kRsrcWord3 = 0x00020000;
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; a field at its maximum does not wait)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -98,7 +103,7 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int TILE = kKT * ROW;        // bytes per K or V tile
   constexpr int NL = kKT * CH / 64 / kNW;  // 1 KB loads per wave per K or V tile
 
-  __shared__ __attribute__((aligned(1024))) char lds[4 * TILE];   // K0 V0 K1 V1
+  __shared__ __attribute__((aligned(1024))) char lds[8 * TILE];   // four stages of (K, V)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -174,7 +179,7 @@ void prefill_kernel(PrefillArgs a) {
   }
   auto stage = [&](int kt, char* dst) {
     if constexpr (std::is_same<T, __bf16>::value) {
-      const int64_t rows = S - kt;   // rows past the sequence end read as zero
+      const int64_t rows = max(S - kt, 0);   // rows past the sequence end read as zero
       const int kb_ = (int)min(rows * a.ks_s * 2, (int64_t)0x7fffffff);
       const int vb_ = (int)min(rows * a.vs_s * 2, (int64_t)0x7fffffff);
       const void* kp = kbase + kt * a.ks_s;
@@ -213,127 +218,179 @@ void prefill_kernel(PrefillArgs a) {
   for (int db = 0; db < DB; ++db)
     v_lane[db] = vrow * ROW + 16 * v_chunk<CH>(4 * db + 2 * ((lane >> 4) & 1) + ((L16 >> 1) & 1), vrow) + 8 * (L16 & 1);
 
-  auto qk = [&](const char* lk, int kb, f32x16* s) {
-    bf16x8 ka[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      ka[ks] = *reinterpret_cast<const bf16x8*>(lk + kb * 32 * ROW + k_lane + 16 * ((2 * ks) ^ k_x));
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) s[cb] = mfma32(ka[ks], qreg[cb][ks], s[cb]);
+  // ---- ping-pong schedule ------------------------------------------------------
+  // Waves w and w + 4 share a SIMD; they form groups A (waves 0-3) and B (4-7).
+  // Work of a wave per tile k: QK(k) (MFMA), SM(k) (mask + softmax, VALU),
+  // PV(k) (MFMA). Every wave runs QK(0) | SM(0) | X(0) | SM(1) | X(1) | ... |
+  // X(n-1), X(k) = PV(k) + QK(k+1); group B runs it one phase behind group A
+  // and every phase ends with a workgroup barrier, so in every phase one wave
+  // of each SIMD feeds the matrix core while the other runs its softmax on the
+  // VALU. K/V: four LDS stages; tile k+3 is issued at the start of iteration k
+  // (phase 2k+2, when the stage of tile k-1 is free in both groups) and must
+  // have landed at the end of phase 2k+5, before its first read in phase 2k+6.
+  const int n_tiles = (kv_hi - kv_lo) / kKT + 1;
+  const int group = wave >> 2;
+  auto stage_ptr = [&](int k) -> char* { return lds + (k & 3) * 2 * TILE; };
+  // tiles past the last one are issued as loads that read nothing, so every
+  // wave has the same number of loads in flight at every wait
+  auto issue = [&](int k) { stage(k < n_tiles ? kv_lo + k * kKT : S, stage_ptr(k)); };
+  auto barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(kLgkm0);   // this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
   };
-  auto mask = [&](f32x16* s, int kb, int kt) {
+
+  f32x16 sc[2];           // S^T of one tile: [32-key block]
+  bf16x8 pc[2][2];        // P^T of one tile: [32-key block][16-key half]
+
+  auto qk_tile = [&](const char* lk) {
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      const int lo = valid[cb] ? st[cb] - kt : kKT;
-      const int hi_ = valid[cb] ? tok[cb] - kt : -1;
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int kr = kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-        s[cb][j] = (kr >= lo && kr <= hi_) ? s[cb][j] : -INFINITY;
+      for (int j = 0; j < 16; ++j) sc[kb][j] = 0.f;
+#pragma unroll
+      for (int k4 = 0; k4 < KS; k4 += 4) {
+        bf16x8 ka[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          ka[u] = *reinterpret_cast<const bf16x8*>(lk + kb * 32 * ROW + k_lane + 16 * ((2 * (k4 + u)) ^ k_x));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sc[kb] = mfma32(ka[u], qreg[0][k4 + u], sc[kb]);
       }
     }
   };
-  // softmax of one half: returns whether some lane moved its reference
-  auto softmax = [&](const f32x16* s, bf16x8 (*p)[2], float* alpha) -> bool {
-    bool moved = false;
+  auto pv_tile = [&](const char* lv) {
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      float mx = s[cb][0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[cb][j]);
-      mx = max_xor32(mx);
-      alpha[cb] = 1.f;
-      if (mx * a.scale_log2 > m[cb] * a.scale_log2 + kLazy) {   // also when m = -inf
-        alpha[cb] = fast_exp2((m[cb] - mx) * a.scale_log2);        // 0 when m = -inf
-        m[cb] = mx;
-        moved = true;
-      }
-      const float mc = m[cb] == -INFINITY ? 0.f : m[cb] * a.scale_log2;
-      float rs = 0.f;
-      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          bf16x2 pr;
-          pr[0] = to_bf16(fast_exp2(fmaf(s[cb][8 * h2 + i], a.scale_log2, -mc)));
-          pr[1] = to_bf16(fast_exp2(fmaf(s[cb][8 * h2 + i + 1], a.scale_log2, -mc)));
-          p[cb][h2][i] = pr[0];
-          p[cb][h2][i + 1] = pr[1];
-          rs = __builtin_amdgcn_fdot2_f32_bf16(pr, one, rs, false);
-        }
-      l[cb] = l[cb] * alpha[cb] + rs;
-    }
-    return moved;
-  };
-  // accumulator rescale in place (rare); written so the accumulator never
-  // leaves the AGPRs the MFMAs keep it in
-  auto rescale = [&](const float* alpha) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int cb = 0; cb < kCB; ++cb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float x = acc[db][cb][j], t;
-          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                       : "+a"(x), "=&v"(t) : "v"(alpha[cb]));
-          acc[db][cb][j] = x;
-        }
-  };
-  auto pv = [&](const char* lv, int kb, const bf16x8 (*p)[2]) {
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int ks = 2 * kb + h2;
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 va[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const char* vp = lv + 16 * ks * ROW + v_lane[db];
         const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
         const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * ROW));
-        const bf16x8 va = __builtin_shufflevector(__builtin_bit_cast(bf16x4, r0),
-                                                  __builtin_bit_cast(bf16x4, r1), 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) acc[db][cb] = mfma32(va, p[cb][h2], acc[db][cb]);
+        va[db] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, r0), __builtin_bit_cast(bf16x4, r1),
+                                         0, 1, 2, 3, 4, 5, 6, 7);
       }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db][0] = mfma32(va[db], pc[ks >> 1][ks & 1], acc[db][0]);
     }
   };
-
-  const int n_tiles = (kv_hi - kv_lo) / kKT + 1;
-  stage(kv_lo, lds);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int n = 0; n < n_tiles; ++n) {
-    const int kt = kv_lo + n * kKT;
-    const char* lk = lds + (n & 1) * 2 * TILE;
-    const char* lv = lk + TILE;
-    if (n + 1 < n_tiles) stage(kt + kKT, lds + ((n + 1) & 1) * 2 * TILE);
-
-    const bool need_mask = !wave_all_valid || kt + kKT - 1 > w_tmin || kt < w_smax;
-    f32x16 s0[kCB], s1[kCB];
+  auto sm_tile = [&](int k) {
+    const int kt = kv_lo + k * kKT;
+    if (!wave_all_valid || kt + kKT - 1 > w_tmin || kt < w_smax) {
+      const int lo = valid[0] ? st[0] - kt : kKT;
+      const int hi_ = valid[0] ? tok[0] - kt : -1;
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s0[cb][j] = s1[cb][j] = 0.f;
-    bf16x8 p0[kCB][2], p1[kCB][2];
-    float alpha0[kCB], alpha1[kCB];
+        for (int j = 0; j < 16; ++j) {
+          const int kr = kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
+          sc[kb][j] = (kr >= lo && kr <= hi_) ? sc[kb][j] : -INFINITY;
+        }
+    }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
+    mx = max_xor32(mx);
+    const bool mv = mx * a.scale_log2 > m[0] * a.scale_log2 + kLazy;   // also when m = -inf
+    if (__any(mv)) {   // rare after the first tiles: move the reference, rescale
+      const float al = mv ? fast_exp2((m[0] - mx) * a.scale_log2) : 1.f;   // 0 when m = -inf
+      m[0] = mv ? mx : m[0];
+      l[0] *= al;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db][0] *= al;
+    }
+    const float mc = m[0] == -INFINITY ? 0.f : m[0] * a.scale_log2;
+    float rs = 0.f;
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          bf16x2 pr;
+          pr[0] = to_bf16(fast_exp2(fmaf(sc[kb][8 * h2 + i], a.scale_log2, -mc)));
+          pr[1] = to_bf16(fast_exp2(fmaf(sc[kb][8 * h2 + i + 1], a.scale_log2, -mc)));
+          pc[kb][h2][i] = pr[0];
+          pc[kb][h2][i + 1] = pr[1];
+          rs = __builtin_amdgcn_fdot2_f32_bf16(pr, one, rs, false);
+        }
+    l[0] += rs;
+  };
+  // the MFMA phase runs at raised priority, so the SIMD's arbiter keeps the
+  // matrix core fed from it first
+  // The refill of tile k+3 and the operand reads of the MFMA phase go through
+  // one call whose stage pointers are restrict, so the compiler does not take
+  // the refill's LDS-direct loads as writers of what the phase reads (it would
+  // otherwise wait for every load in flight before the first read); the
+  // vmcnt waits before the barriers order each stage's loads before its reads.
+  auto x_phase = [&](char* __restrict__ dst, int kd, const char* __restrict__ lv,
+                     const char* __restrict__ lk, int k) {
+    if (dst) stage(kd < n_tiles ? kv_lo + kd * kKT : S, dst);
+    __builtin_amdgcn_s_setprio(1);
+    // one block of 32 MFMAs and their 48 operand reads (after the last tile
+    // the QK of the stage beyond it is computed and dropped): keep eight reads
+    // ahead of the MFMAs instead of the one or two the default schedule keeps
+    pv_tile(lv);
+    qk_tile(lk);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // tile k+2 landed: only the loads issued after it (tile k+3) may be pending
+  auto landed = [&]() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL)); };
 
-    qk(lk, 0, s0);
-    if (need_mask) mask(s0, 0, kt);
-    qk(lk, 1, s1);                                   // MFMAs overlap the softmax below
-    const bool mv0 = softmax(s0, p0, alpha0);
-    if (__any(mv0)) rescale(alpha0);
-    if (need_mask) mask(s1, 1, kt);
-    pv(lv, 0, p0);                                   // MFMAs overlap the softmax below
-    const bool mv1 = softmax(s1, p1, alpha1);
-    if (__any(mv1)) rescale(alpha1);
-    pv(lv, 1, p1);
-
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  issue(0);
+  issue(1);
+  issue(2);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * NL));   // tile 0 landed
+  __builtin_amdgcn_s_barrier();
+  if (group == 0) {
+    __builtin_amdgcn_s_setprio(1);
+    qk_tile(stage_ptr(0));
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL));   // tile 1 landed
+    barrier();                                       // end of phase 0
+    sm_tile(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));        // tile 2 landed
+    barrier();                                       // end of phase 1
+    for (int k = 0; k < n_tiles; ++k) {
+      x_phase(stage_ptr(k + 3), k + 3, stage_ptr(k) + TILE, stage_ptr(k + 1), k);
+      barrier();                                     // end of phase 2k+2
+      if (k + 1 < n_tiles) sm_tile(k + 1);
+      landed();
+      barrier();                                     // end of phase 2k+3
+    }
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL));
+    barrier();                                       // end of phase 0
+    __builtin_amdgcn_s_setprio(1);
+    qk_tile(stage_ptr(0));
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    barrier();                                       // end of phase 1
+    for (int k = 0; k < n_tiles; ++k) {
+      issue(k + 3);
+      sm_tile(k);
+      barrier();                                     // end of phase 2k+2
+      x_phase(nullptr, 0, stage_ptr(k) + TILE, stage_ptr(k + 1), k);
+      landed();
+      barrier();                                     // end of phase 2k+3
+    }
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));          // loads past the last tile
 
   // ---- epilogue --------------------------------------------------------------
 #pragma unroll
