@@ -89,7 +89,23 @@ def setup_prefill(name: str):
     return st, (q, k, v)
 
 
-def time_prefill(st, steps: int, warmup: int):
+def settle(step, seconds: float):
+    """Run whole steps, untimed, for `seconds` of wall time before the warmup
+    steps: the GPU's clocks ramp up over the first tens of milliseconds of
+    sustained load, and a step of a quarter millisecond would otherwise be
+    timed partly at the idle clock."""
+    import torch
+    t = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t < seconds:
+        step()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def time_prefill(st, steps: int, warmup: int, settle_s: float = 0.0):
     import torch
     import gqa_attention_rope_02_amd as la
 
@@ -103,6 +119,7 @@ def time_prefill(st, steps: int, warmup: int):
         if evs:
             evs[2].record()
 
+    settle(step, settle_s)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -152,7 +169,7 @@ def setup_decode():
     return st
 
 
-def time_decode(st, steps: int, warmup: int):
+def time_decode(st, steps: int, warmup: int, settle_s: float = 0.0):
     import torch
     import gqa_attention_rope_02_amd as la
 
@@ -166,6 +183,7 @@ def time_decode(st, steps: int, warmup: int):
         if evs:
             evs[2].record()
 
+    settle(step, settle_s)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -246,8 +264,10 @@ def cpu_baseline(host_inputs, w, cu, budget_s: float = 20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed whole steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "llama8b", "llama405b", "decode405b", "copy"],
                     default=None, help="run one part: both prefills, the decode, one workload, "
@@ -268,6 +288,7 @@ def main():
     import gqa_attention_rope_02_amd  # noqa: F401  (fails loudly without the HIP library)
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "settle_s": args.settle,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) Q/K/V, seeded document cuts)"}
     phash = kernel_hash("gqa_prefill.hip")
@@ -284,7 +305,7 @@ def main():
     if run_8b:
         st, host = setup_prefill("llama8b")
         w, cu = st["w"], st["cu"]
-        t = time_prefill(st, args.steps, args.warmup)
+        t = time_prefill(st, args.steps, args.warmup, args.settle)
         fl = prefill_flops(w, cu)
         value = fl / (t["gpu_ms_per_step"] * 1e-3) / 1e12
         achieved = fl / (t["prefill_ms"] * 1e-3) / 1e12
@@ -308,7 +329,7 @@ def main():
 
     if run_405:
         st3, _ = setup_prefill("llama405b")
-        t3 = time_prefill(st3, max(3, args.steps // 2), args.warmup)
+        t3 = time_prefill(st3, max(3, args.steps // 2), args.warmup, args.settle)
         fl3 = prefill_flops(st3["w"], st3["cu"])
         out["prefill_405b"] = {
             "workload": "llama-3.1-405b attention layer prefill S=32768, 128 q / 8 kv heads",
@@ -337,7 +358,7 @@ def main():
 
     if run_dec:
         sd = setup_decode()
-        td = time_decode(sd, args.steps, args.warmup)
+        td = time_decode(sd, args.steps, args.warmup, args.settle)
         nbytes = decode_bytes(sd)
         gbs = nbytes / (td["decode_ms"] * 1e-3) / 1e9
         dhash = kernel_hash("gqa_decode.hip")

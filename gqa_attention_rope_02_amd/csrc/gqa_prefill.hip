@@ -25,7 +25,11 @@
 //   issued three tiles before it is read. The buffer descriptor moves with the
 //   tile and its size ends at the sequence end, so rows past the end read as
 //   zero. K operands are read with ds_read_b128; the V^T operand with the
-//   transposing ds_read_b64_tr_b16 from the row-major V tile.
+//   transposing ds_read_b64_tr_b16 from the row-major V tile. The four K
+//   stages fill the first 64 KB of LDS and the four V stages the second; the
+//   tile loop is unrolled over the stages, so every operand read is one
+//   per-lane address register plus a constant offset (no address arithmetic
+//   in the loop).
 // * The two waves of a SIMD run one phase apart ("ping-pong"): each wave
 //   alternates an MFMA phase (PV of tile k and QK of tile k+1: 32 MFMAs and
 //   their 48 operand reads, kept eight reads ahead) with a softmax phase
@@ -37,11 +41,18 @@
 // * Online softmax in the base-2 domain with fp32 statistics; probabilities
 //   are rounded to bf16 once and the row sums accumulate those rounded values
 //   (v_dot2_f32_bf16), so numerator and denominator use the same weights. The
-//   reference the exponents are taken against moves only when a score exceeds
-//   it by more than 2^8 (exact: softmax does not depend on the reference, and
-//   the weights stay below 256), so the accumulator is almost never rescaled.
-//   Masks are evaluated only on tiles that cross a causal or document edge of
-//   the wave's columns.
+//   reference the exponents are taken against is moved lazily (exact: softmax
+//   does not depend on the reference): a tile's weights are first taken
+//   against the current reference, and only if some lane's sum of them
+//   exceeds 2^8 (so possibly one weight does) is the tile max formed, the
+//   reference moved up to it, the accumulator rescaled and the weights redone.
+//   Weights therefore stay at most 256, and most tiles need neither a max nor
+//   a rescale. Masks are evaluated only on tiles that cross a causal or
+//   document edge of the wave's columns.
+// * Start of a workgroup: with at most 63 documents the row of document
+//   offsets is read with one load per lane and searched with wave ballots, the
+//   Q loads are issued right after it, and the first K/V tiles as soon as the
+//   key range is known, so these latencies overlap.
 // * Workgroups are issued longest-first (last token tiles first), and the KV
 //   head is the fastest-varying index so the workgroups of one KV head land on
 //   one XCD (blockIdx % 8) and share its L2.
@@ -57,7 +68,7 @@ constexpr int kCols = 256;    // columns per workgroup
 constexpr int kNW = 8;        // waves per workgroup
 constexpr int kCB = kCols / kNW / 32;   // 32-column blocks per wave
 constexpr int kKT = 64;       // keys per tile
-constexpr float kLazy = 8.f;  // log2 headroom of the lazily moved softmax reference
+constexpr float kLazyW = 256.f;   // bound on a weight under the lazily moved softmax reference
 constexpr int kRsrcWord3 = 0x00020000;
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8; a field at its maximum does not wait)
@@ -103,10 +114,12 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int TILE = kKT * ROW;        // bytes per K or V tile
   constexpr int NL = kKT * CH / 64 / kNW;  // 1 KB loads per wave per K or V tile
 
-  __shared__ __attribute__((aligned(1024))) char lds[8 * TILE];   // four stages of (K, V)
+  // four stages: K of stage s at s TILE, V of stage s at (4 + s) TILE, so
+  // every operand address is one per-lane register plus an offset below 64 KB
+  __shared__ __attribute__((aligned(1024))) char lds[8 * TILE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lc = lane & 31, hi = lane >> 5;
 
   const int bid = blockIdx.x;
@@ -119,16 +132,12 @@ void prefill_kernel(PrefillArgs a) {
   const int t_end = min(t0 + TQ, S);
   const int32_t* cu = a.cu_docs ? a.cu_docs + (int64_t)b * (a.n_docs + 1) : nullptr;
   const int n_docs = a.n_docs;
-  auto start_of = [&](int t) -> int { return cu ? doc_start(cu, n_docs, t) : 0; };
-  // clamp: out-of-contract offsets must not move the key range out of [0, t0]
-  const int kv_lo = max(0, min(start_of(t0), t0));
-  const int kv_hi = t_end - 1;
 
   const T* qbase = static_cast<const T*>(a.q) + b * a.qs_b;
   const T* kbase = static_cast<const T*>(a.k) + b * a.ks_b + kvh * a.ks_h;
   const T* vbase = static_cast<const T*>(a.v) + b * a.vs_b + kvh * a.vs_h;
 
-  // ---- this lane's two columns (one per 32-column block) -------------------
+  // ---- this lane's columns (one per 32-column block) -------------------------
   int tok[kCB], head[kCB], st[kCB];
   bool valid[kCB];
 #pragma unroll
@@ -137,22 +146,65 @@ void prefill_kernel(PrefillArgs a) {
     tok[cb] = t0 + col / G;
     head[cb] = kvh * G + col % G;
     valid[cb] = tok[cb] < S;
-    st[cb] = valid[cb] ? start_of(tok[cb]) : 0;
   }
   const int w_tmin = min(t0 + (wave * 32 * kCB) / G, S - 1);
   const int w_tmax_raw = t0 + (wave * 32 * kCB + 32 * kCB - 1) / G;
   const bool wave_all_valid = w_tmax_raw < S;
   const int w_tmax = min(w_tmax_raw, S - 1);
-  const int w_smax = start_of(w_tmax);
+
+  // ---- document starts ---------------------------------------------------------
+  // With at most 63 documents the offsets row is read once, one entry per
+  // lane, and every search is a ballot over the lanes. Longer rows are
+  // binary-searched in memory, before any other load is issued, so that the
+  // waits of one path do not land on the loads of the other.
+  const bool docs_in_lanes = cu && n_docs < 64;
+  int kv_start = 0, w_smax = 0;
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) st[cb] = 0;
+  if (cu && !docs_in_lanes) {
+    kv_start = doc_start(cu, n_docs, t0);
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) st[cb] = valid[cb] ? doc_start(cu, n_docs, tok[cb]) : 0;
+    w_smax = doc_start(cu, n_docs, w_tmax);
+  }
+  int cu_l = 0;
+  if (docs_in_lanes) cu_l = cu[min(lane, n_docs)];
 
   // ---- Q operand (B of S^T = K Q^T): Q[col][16ks + 8hi + i] ----------------
+  // Columns past the sequence end load the last token's row (no branch, so
+  // the wait for the offsets row does not also wait for Q); every key is
+  // masked for them and their outputs are not stored.
   bf16x8 qreg[kCB][KS];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
-    const T* qp = qbase + tok[cb] * a.qs_s + head[cb] * a.qs_h + 8 * hi;
+    const T* qp = qbase + min(tok[cb], S - 1) * a.qs_s + head[cb] * a.qs_h + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[cb][ks] = valid[cb] ? load8(qp + 16 * ks) : zero_bf16x8();
+    for (int ks = 0; ks < KS; ++ks) qreg[cb][ks] = load8(qp + 16 * ks);
   }
+
+  if (docs_in_lanes) {
+    // index of the document holding token t (the same t in every lane): the
+    // last of the first n_docs offsets that is <= t, else 0
+    auto doc_of = [&](int t) __attribute__((always_inline)) -> int {
+      const unsigned long long mk = __ballot(lane < n_docs && cu_l <= t);
+      return mk ? 63 - __clzll(mk) : 0;
+    };
+    const int d0 = doc_of(t0);
+    kv_start = __builtin_amdgcn_readlane(cu_l, d0);
+    // the documents that start inside this workgroup's tokens follow d0
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) st[cb] = kv_start;
+    for (int d = d0 + 1; d < n_docs; ++d) {
+      const int c = __builtin_amdgcn_readlane(cu_l, d);
+      if (c >= t_end) break;
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) st[cb] = tok[cb] >= c ? c : st[cb];
+    }
+    w_smax = __builtin_amdgcn_readlane(cu_l, doc_of(w_tmax));
+  }
+  // clamp: out-of-contract offsets must not move the key range out of [0, t0]
+  const int kv_lo = max(0, min(kv_start, t0));
+  const int kv_hi = t_end - 1;
 
   f32x16 acc[DB][kCB];
 #pragma unroll
@@ -177,7 +229,7 @@ void prefill_kernel(PrefillArgs a) {
     koff[n] = (int)(row * a.ks_s * (int64_t)sizeof(T) + 8 * k_chunk<CH>(ph, row) * (int)sizeof(T));
     voff[n] = (int)(row * a.vs_s * (int64_t)sizeof(T) + 8 * v_chunk<CH>(ph, row) * (int)sizeof(T));
   }
-  auto stage = [&](int kt, char* dst) {
+  auto stage = [&](int kt, char* dst) __attribute__((always_inline)) {
     if constexpr (std::is_same<T, __bf16>::value) {
       const int64_t rows = max(S - kt, 0);   // rows past the sequence end read as zero
       const int kb_ = (int)min(rows * a.ks_s * 2, (int64_t)0x7fffffff);
@@ -187,7 +239,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int n = 0; n < NL; ++n) {
         load_lds16(kp, kb_, koff[n], dst + (n * kNW + wave) * 1024);
-        load_lds16(vp, vb_, voff[n], dst + TILE + (n * kNW + wave) * 1024);
+        load_lds16(vp, vb_, voff[n], dst + 4 * TILE + (n * kNW + wave) * 1024);
       }
     } else {   // fp32 inputs: convert to bf16 on the way into LDS
       for (int p = tid; p < kKT * CH; p += 64 * kNW) {
@@ -199,7 +251,7 @@ void prefill_kernel(PrefillArgs a) {
           vv = load8(vbase + j * a.vs_s + 8 * v_chunk<CH>(ph, row));
         }
         *reinterpret_cast<bf16x8*>(dst + p * 16) = kv;
-        *reinterpret_cast<bf16x8*>(dst + TILE + p * 16) = vv;
+        *reinterpret_cast<bf16x8*>(dst + 4 * TILE + p * 16) = vv;
       }
     }
   };
@@ -217,6 +269,13 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db)
     v_lane[db] = vrow * ROW + 16 * v_chunk<CH>(4 * db + 2 * ((lane >> 4) & 1) + ((L16 >> 1) & 1), vrow) + 8 * (L16 & 1);
+  // the V region's start (64 KB) goes into the per-lane offsets, kept opaque
+  // so that it is not folded back into the reads' immediate offsets, which
+  // hold 16 bits: V reads take lds + stage * TILE as their base
+  int v_region = 4 * TILE;
+  asm volatile("" : "+v"(v_region));
+#pragma unroll
+  for (int db = 0; db < DB; ++db) v_lane[db] += v_region;
 
   // ---- ping-pong schedule ------------------------------------------------------
   // Waves w and w + 4 share a SIMD; they form groups A (waves 0-3) and B (4-7).
@@ -230,11 +289,11 @@ void prefill_kernel(PrefillArgs a) {
   // have landed at the end of phase 2k+5, before its first read in phase 2k+6.
   const int n_tiles = (kv_hi - kv_lo) / kKT + 1;
   const int group = wave >> 2;
-  auto stage_ptr = [&](int k) -> char* { return lds + (k & 3) * 2 * TILE; };
+  auto stage_ptr = [&](int k) __attribute__((always_inline)) -> char* { return lds + (k & 3) * TILE; };
   // tiles past the last one are issued as loads that read nothing, so every
   // wave has the same number of loads in flight at every wait
-  auto issue = [&](int k) { stage(k < n_tiles ? kv_lo + k * kKT : S, stage_ptr(k)); };
-  auto barrier = [&]() {
+  auto issue = [&](int k) __attribute__((always_inline)) { stage(k < n_tiles ? kv_lo + k * kKT : S, stage_ptr(k)); };
+  auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(kLgkm0);   // this wave's LDS reads are done
     __builtin_amdgcn_s_barrier();
   };
@@ -242,7 +301,7 @@ void prefill_kernel(PrefillArgs a) {
   f32x16 sc[2];           // S^T of one tile: [32-key block]
   bf16x8 pc[2][2];        // P^T of one tile: [32-key block][16-key half]
 
-  auto qk_tile = [&](const char* lk) {
+  auto qk_tile = [&](const char* lk) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -258,7 +317,7 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
   };
-  auto pv_tile = [&](const char* lv) {
+  auto pv_tile = [&](const char* lv) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8 va[DB];
@@ -274,7 +333,7 @@ void prefill_kernel(PrefillArgs a) {
       for (int db = 0; db < DB; ++db) acc[db][0] = mfma32(va[db], pc[ks >> 1][ks & 1], acc[db][0]);
     }
   };
-  auto sm_tile = [&](int k) {
+  auto sm_tile = [&](int k) __attribute__((always_inline)) {
     const int kt = kv_lo + k * kKT;
     if (!wave_all_valid || kt + kKT - 1 > w_tmin || kt < w_smax) {
       const int lo = valid[0] ? st[0] - kt : kKT;
@@ -287,36 +346,52 @@ void prefill_kernel(PrefillArgs a) {
           sc[kb][j] = (kr >= lo && kr <= hi_) ? sc[kb][j] : -INFINITY;
         }
     }
-    float mx = sc[0][0];
+    // P^T of the tile against the reference mc (log2 units); returns this
+    // lane's sum of the rounded weights
+    auto weights = [&](float mc) __attribute__((always_inline)) -> float {
+      float rs = 0.f;
+      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
-    mx = max_xor32(mx);
-    const bool mv = mx * a.scale_log2 > m[0] * a.scale_log2 + kLazy;   // also when m = -inf
-    if (__any(mv)) {   // rare after the first tiles: move the reference, rescale
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            bf16x2 pr;
+            pr[0] = to_bf16(fast_exp2(fmaf(sc[kb][8 * h2 + i], a.scale_log2, -mc)));
+            pr[1] = to_bf16(fast_exp2(fmaf(sc[kb][8 * h2 + i + 1], a.scale_log2, -mc)));
+            pc[kb][h2][i] = pr[0];
+            pc[kb][h2][i + 1] = pr[1];
+            rs = __builtin_amdgcn_fdot2_f32_bf16(pr, one, rs, false);
+          }
+      return rs;
+    };
+    // The reference must move only when a weight would exceed kLazyW. The
+    // weights are non-negative, so a lane whose sum is at most kLazyW holds
+    // none larger, and the tile max is needed only when some lane's sum is
+    // larger (or a column has no reference yet); the reference then moves to
+    // the tile max whenever that is higher.
+    bool slow = __any(m[0] == -INFINITY);
+    float rs = 0.f;
+    if (!slow) {
+      rs = weights(m[0] * a.scale_log2);
+      slow = __any(!(rs <= kLazyW));
+    }
+    if (slow) {
+      float mx = sc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
+      mx = max_xor32(mx);
+      const bool mv = mx > m[0];
       const float al = mv ? fast_exp2((m[0] - mx) * a.scale_log2) : 1.f;   // 0 when m = -inf
       m[0] = mv ? mx : m[0];
       l[0] *= al;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db][0] *= al;
+      rs = weights(m[0] == -INFINITY ? 0.f : m[0] * a.scale_log2);
     }
-    const float mc = m[0] == -INFINITY ? 0.f : m[0] * a.scale_log2;
-    float rs = 0.f;
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          bf16x2 pr;
-          pr[0] = to_bf16(fast_exp2(fmaf(sc[kb][8 * h2 + i], a.scale_log2, -mc)));
-          pr[1] = to_bf16(fast_exp2(fmaf(sc[kb][8 * h2 + i + 1], a.scale_log2, -mc)));
-          pc[kb][h2][i] = pr[0];
-          pc[kb][h2][i + 1] = pr[1];
-          rs = __builtin_amdgcn_fdot2_f32_bf16(pr, one, rs, false);
-        }
     l[0] += rs;
   };
   // the MFMA phase runs at raised priority, so the SIMD's arbiter keeps the
@@ -327,7 +402,7 @@ void prefill_kernel(PrefillArgs a) {
   // otherwise wait for every load in flight before the first read); the
   // vmcnt waits before the barriers order each stage's loads before its reads.
   auto x_phase = [&](char* __restrict__ dst, int kd, const char* __restrict__ lv,
-                     const char* __restrict__ lk, int k) {
+                     const char* __restrict__ lk, int k) __attribute__((always_inline)) {
     if (dst) stage(kd < n_tiles ? kv_lo + kd * kKT : S, dst);
     __builtin_amdgcn_s_setprio(1);
     // one block of 32 MFMAs and their 48 operand reads (after the last tile
@@ -350,7 +425,7 @@ void prefill_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_setprio(0);
   };
   // tile k+2 landed: only the loads issued after it (tile k+3) may be pending
-  auto landed = [&]() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL)); };
+  auto landed = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL)); };
 
   issue(0);
   issue(1);
@@ -366,12 +441,23 @@ void prefill_kernel(PrefillArgs a) {
     sm_tile(0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));        // tile 2 landed
     barrier();                                       // end of phase 1
-    for (int k = 0; k < n_tiles; ++k) {
-      x_phase(stage_ptr(k + 3), k + 3, stage_ptr(k) + TILE, stage_ptr(k + 1), k);
+    // unrolled over the four stages so every stage offset is a constant
+    auto step = [&](auto U, int k) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      x_phase(lds + ((u + 3) & 3) * TILE, k + 3, lds + u * TILE, lds + ((u + 1) & 3) * TILE, k);
       barrier();                                     // end of phase 2k+2
       if (k + 1 < n_tiles) sm_tile(k + 1);
       landed();
       barrier();                                     // end of phase 2k+3
+    };
+    for (int k = 0; k < n_tiles; k += 4) {
+      step(std::integral_constant<int, 0>{}, k);
+      if (k + 1 >= n_tiles) break;
+      step(std::integral_constant<int, 1>{}, k + 1);
+      if (k + 2 >= n_tiles) break;
+      step(std::integral_constant<int, 2>{}, k + 2);
+      if (k + 3 >= n_tiles) break;
+      step(std::integral_constant<int, 3>{}, k + 3);
     }
   } else {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL));
@@ -381,13 +467,23 @@ void prefill_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     barrier();                                       // end of phase 1
-    for (int k = 0; k < n_tiles; ++k) {
-      issue(k + 3);
+    auto step = [&](auto U, int k) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      stage(k + 3 < n_tiles ? kv_lo + (k + 3) * kKT : S, lds + ((u + 3) & 3) * TILE);
       sm_tile(k);
       barrier();                                     // end of phase 2k+2
-      x_phase(nullptr, 0, stage_ptr(k) + TILE, stage_ptr(k + 1), k);
+      x_phase(nullptr, 0, lds + u * TILE, lds + ((u + 1) & 3) * TILE, k);
       landed();
       barrier();                                     // end of phase 2k+3
+    };
+    for (int k = 0; k < n_tiles; k += 4) {
+      step(std::integral_constant<int, 0>{}, k);
+      if (k + 1 >= n_tiles) break;
+      step(std::integral_constant<int, 1>{}, k + 1);
+      if (k + 2 >= n_tiles) break;
+      step(std::integral_constant<int, 2>{}, k + 2);
+      if (k + 3 >= n_tiles) break;
+      step(std::integral_constant<int, 3>{}, k + 3);
     }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));          // loads past the last tile
@@ -397,16 +493,23 @@ void prefill_kernel(PrefillArgs a) {
   for (int cb = 0; cb < kCB; ++cb) {
     const float lt = l[cb] + __shfl_xor(l[cb], 32);
     if (!valid[cb]) continue;
-    // true division (once per output): a row whose weights are all exact gets
-    // an exactly rounded mean
+    // o = acc / lt as the reciprocal's product plus one residual step
+    // (q + (acc - q lt) / lt, residual by FMA): a quotient that fp32 can hold
+    // comes out exactly, so a row whose weights are all exact gets an exactly
+    // rounded mean
+    const float rl = __builtin_amdgcn_rcpf(lt);
+    auto quot = [&](float x) __attribute__((always_inline)) {
+      const float q = x * rl;
+      return fmaf(fmaf(-q, lt, x), rl, q);
+    };
     T* op = static_cast<T*>(a.o) + b * a.os_b + tok[cb] * a.os_s + head[cb] * a.os_h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
         const int d = db * 32 + 8 * jq + 4 * hi;
-        store4(op + d, acc[db][cb][4 * jq] / lt, acc[db][cb][4 * jq + 1] / lt,
-               acc[db][cb][4 * jq + 2] / lt, acc[db][cb][4 * jq + 3] / lt);
+        store4(op + d, quot(acc[db][cb][4 * jq]), quot(acc[db][cb][4 * jq + 1]),
+               quot(acc[db][cb][4 * jq + 2]), quot(acc[db][cb][4 * jq + 3]));
       }
     if (a.lse && hi == 0)
       a.lse[((int64_t)b * a.Hq + head[cb]) * S + tok[cb]] = m[cb] * a.scale + fast_log2(lt) * kLn2;
