@@ -63,6 +63,26 @@ __device__ __forceinline__ void load_lds16(const void* base, int bytes_valid, in
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Lane exchanges on the VALU (v_permlane16/32_swap), not through the LDS
+// crossbar that __shfl_xor (ds_bpermute) uses: the tile loop runs them while
+// its LDS-direct loads are in flight.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // One work item: split s of KV head kvh of sequence b, keys [k0, k1).
 struct Item {
   int b, kvh, s, ns, L, k0, k1, nt;   // ns: splits of sequence b; nt: tiles of the item
@@ -259,16 +279,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lk + k_lane + 16 * k_chunk<CH>(4 * ks + lg, lc));
       s = mfma16k32(ka, qreg[ks], s);
     }
-    // lane holds S^T[key = key0 + 4lg + j][col = lc]
+    // lane holds S^T[key = key0 + 4lg + j][col = lc]. Keys past the item's
+    // end (only in its last tile) are masked without a branch: the scores are
+    // read here right after their MFMA, and the compiler pads that read with
+    // the wait the matrix core needs only on a single path.
     const int kbase = cit.k0 + ct * kKT + 4 * lg;
-    if (cit.k0 + (ct + 1) * kKT > cit.k1) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (kbase + j >= cit.k1) s[j] = -INFINITY;
-    }
+    for (int j = 0; j < 4; ++j) s[j] = kbase + j < cit.k1 ? s[j] : -INFINITY;
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const bool mv = mx * a.scale_log2 > m * a.scale_log2 + kLazy;
     if (__any(mv)) {   // rare after a run's first tile
       const float al = mv ? fast_exp2((m - mx) * a.scale_log2) : 1.f;   // 0 when m = -inf
@@ -295,8 +314,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 
     if (++ct == cit.nt) {   // item done
       if (ci + 1 == i1 || cit.s + 1 == cit.ns) {   // run done: its partial goes to slot run_s0
-        float lt2 = l + __shfl_xor(l, 16);
-        lt2 += __shfl_xor(lt2, 32);
+        const float lt2 = add_xor32(add_xor16(l));
         if (lc < G) {
           const int64_t row = ((int64_t)cit.b * a.Hq + cit.kvh * G + lc) * a.max_splits;
           float* op = a.o_part + (row + run_s0) * D;

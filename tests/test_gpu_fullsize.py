@@ -118,3 +118,51 @@ def test_full_size_decode_sampled_heads():
             n_runs += H.check_partials(op[b:b + 1, heads].cpu(), lp[b:b + 1, heads].cpu(),
                                        qb, kb, vb, [L], chunk)
     H.say("  runs checked", n_runs)
+
+
+def test_full_size_decode_is_deterministic():
+    """The 405B-shape decode three times on the same inputs, workspaces
+    NaN-filled before each call: partial results, their LSE and the combined
+    output agree bit for bit (a result that depends on timing, such as a read
+    of a matrix-core result before it is ready, shows up here)."""
+    import bench
+    import gqa_attention_rope_02_amd as la
+    H.say("full-size decode determinism")
+    st = bench.setup_decode()
+    chunk = bench.KV_CHUNK
+    first = None
+    for _ in range(3):
+        op = torch.full_like(st["op"], float("nan"))
+        lp = torch.full_like(st["lp"], float("nan"))
+        o = torch.full_like(st["o"], float("nan"))
+        la.gqa_decode(st["q"], st["kc"], st["vc"], st["sl"], chunk, op, lp)
+        la.gqa_decode_combine(op, lp, st["sl"], chunk, o)
+        torch.cuda.synchronize()
+        live = torch.isfinite(lp)
+        got = (lp.nan_to_num(0.0), op * live[..., None], o)
+        if first is None:
+            first = got
+        else:
+            for a, b in zip(first, got):
+                assert torch.equal(a.nan_to_num(0.0), b.nan_to_num(0.0))
+
+
+@pytest.mark.parametrize("name", ["llama8b", "llama405b"])
+def test_full_size_prefill_is_deterministic(name):
+    """The bench prefill three times on the same rotated inputs: O and LSE
+    agree bit for bit."""
+    import bench
+    import gqa_attention_rope_02_amd as la
+    H.say("full-size prefill determinism", name)
+    st, _ = bench.setup_prefill(name)
+    la.rope_qk(st["q"], st["qr"], st["k"], st["kr"])
+    first = None
+    for _ in range(3):
+        o = torch.full_like(st["o"], float("nan"))
+        lse = torch.full_like(st["lse"], float("nan"))
+        la.gqa_prefill(st["qr"], st["kr"], st["v"], o, lse, st["cu_d"])
+        torch.cuda.synchronize()
+        if first is None:
+            first = (o, lse)
+        else:
+            assert torch.equal(first[0], o) and torch.equal(first[1], lse)
