@@ -112,10 +112,10 @@ def time_prefill(st, steps: int, warmup: int, settle_s: float = 0.0):
     def step(evs=None):
         if evs:
             evs[0].record()
-        la.rope_qk(st["q"], st["qr"], st["k"], st["kr"])
+        la.rope_qk(None, None, st["k"], st["kr"])          # keys; the queries rotate in the kernel
         if evs:
             evs[1].record()
-        la.gqa_prefill(st["qr"], st["kr"], st["v"], st["o"], st["lse"], st["cu_d"])
+        la.gqa_prefill_rope(st["q"], st["kr"], st["v"], st["o"], st["lse"], st["cu_d"])
         if evs:
             evs[2].record()
 
@@ -310,13 +310,14 @@ def main():
         value = fl / (t["gpu_ms_per_step"] * 1e-3) / 1e12
         achieved = fl / (t["prefill_ms"] * 1e-3) / 1e12
         out.update(value=round(value, 2), unit="TFLOP/s", ms_per_step=round(t["gpu_ms_per_step"], 4))
-        out["config"] = {"workload": "llama-3.1-8b attention layer prefill: rope_qk + gqa_prefill, "
+        out["config"] = {"workload": "llama-3.1-8b attention layer prefill: rope_qk (keys) + "
+                                     "gqa_prefill_rope (queries rotated in the kernel), "
                                      "causal + cross-document mask",
                          "batch": w.B, "seq_len": w.S, "q_heads": w.Hq, "kv_heads": w.Hkv,
                          "head_dim": w.D, "rope_base": w.rope_base, "documents": int(cu.size - 1),
                          "allowed_pairs": allowed_pairs(cu), "flops_per_step": fl,
                          "parallelism": "none (1 GPU)"}
-        out["roofline"] = {"kernel": "gqa_prefill", "bound": "mfma", "achieved": round(achieved, 2),
+        out["roofline"] = {"kernel": "gqa_prefill_rope", "bound": "mfma", "achieved": round(achieved, 2),
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                            "traffic": measured_traffic("gqa_prefill", "llama8b", phash),

@@ -1,6 +1,6 @@
 """Python binding of the gfx950 GQA + RoPE attention library.
 
-The four calls mirror the C ABI in ``include/llama_attn.h`` one to one and only
+The calls mirror the C ABI in ``include/llama_attn.h`` one to one and only
 marshal arguments: tensor pointers, element strides, sizes and the current HIP
 stream. Every step of the computation runs in the library's HIP kernels;
 PyTorch provides device memory and streams. Tensors must live on the GPU.
@@ -12,6 +12,9 @@ contiguous):
   q [B,S,Hq,D], k [B,S,Hkv,D] (either pair may be None); positions int32 [B,S].
 * ``gqa_prefill(q, k, v, o, lse=None, cu_docs=None, softmax_scale=0.0)``:
   q/o [B,S,Hq,D], k/v [B,S,Hkv,D], cu_docs int32 [B, n_docs+1], lse fp32 [B,Hq,S].
+* ``gqa_prefill_rope(q, k, v, o, lse=None, cu_docs=None, softmax_scale=0.0,
+  positions=None, rope_base=500000.0)``: as gqa_prefill with unrotated q (the
+  kernel rotates it; k must be rotated, e.g. by rope_qk with q_in None).
 * ``gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk, o_part, lse_part,
   softmax_scale=0.0)``: q [B,Hq,D], caches [B,Hkv,Lmax,D], seq_lens int32 [B],
   o_part fp32 [B,Hq,max_splits,D], lse_part fp32 [B,Hq,max_splits].
@@ -25,8 +28,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["LlamaAttnError", "rope_qk", "gqa_prefill", "gqa_decode", "gqa_decode_combine",
-           "version", "LA_BF16", "LA_FP32"]
+__all__ = ["LlamaAttnError", "rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_decode",
+           "gqa_decode_combine", "version", "LA_BF16", "LA_FP32"]
 
 LA_BF16, LA_FP32 = 0, 1
 _DT = {torch.bfloat16: LA_BF16, torch.float32: LA_FP32}
@@ -129,6 +132,27 @@ def gqa_prefill(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float = 0.0):
         _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
         _i32(cu_docs), n_docs, float(softmax_scale), _stream())
     _check(st, "gqa_prefill")
+
+
+def gqa_prefill_rope(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float = 0.0,
+                     positions=None, rope_base: float = 500000.0):
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    n_docs = cu_docs.shape[-1] - 1 if cu_docs is not None else 1
+    _same_shape("gqa_prefill_rope", (q, o), (k, v))
+    if tuple(k.shape) != (B, S, Hkv, D):
+        raise ValueError("gqa_prefill_rope: k/v must be [B, S, Hkv, D]")
+    if lse is not None and tuple(lse.shape) != (B, Hq, S):
+        raise ValueError("gqa_prefill_rope: lse must be [B, Hq, S]")
+    if cu_docs is not None and (cu_docs.dim() != 2 or cu_docs.shape[0] != B):
+        raise ValueError("gqa_prefill_rope: cu_docs must be [B, n_docs + 1]")
+    if positions is not None and tuple(positions.shape) != (B, S):
+        raise ValueError("gqa_prefill_rope: positions must be [B, S]")
+    st = _lib.load().gqa_prefill_rope(
+        _dev(q), _dev(k), _dev(v), _dev(o), _f32c(lse), _dtype(q), B, S, Hq, Hkv, D,
+        _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
+        _i32(cu_docs), n_docs, float(softmax_scale), _i32(positions), float(rope_base), _stream())
+    _check(st, "gqa_prefill_rope")
 
 
 def gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk: int, o_part, lse_part,

@@ -34,6 +34,21 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 __device__ __forceinline__ bf16x8 load8(const __bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
+// the same 8 elements as fp32
+__device__ __forceinline__ void load8_f32(const __bf16* p, float* x) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+}
+__device__ __forceinline__ void load8_f32(const float* p, float* x) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[i + 4] = b[i];
+  }
+}
 __device__ __forceinline__ bf16x8 load8(const float* p) {
   const f32x4 a = *reinterpret_cast<const f32x4*>(p);
   const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);

@@ -175,11 +175,18 @@ void prefill_kernel(PrefillArgs a) {
   // the wait for the offsets row does not also wait for Q); every key is
   // masked for them and their outputs are not stored.
   bf16x8 qreg[kCB][KS];
+  float qraw[kCB][KS][8];   // unrotated queries (RoPE in the kernel), else unused
+  const bool rope_q = a.rope_q != 0;
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
     const T* qp = qbase + min(tok[cb], S - 1) * a.qs_s + head[cb] * a.qs_h + 8 * hi;
+    if (rope_q) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[cb][ks] = load8(qp + 16 * ks);
+      for (int ks = 0; ks < KS; ++ks) load8_f32(qp + 16 * ks, qraw[cb][ks]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qreg[cb][ks] = load8(qp + 16 * ks);
+    }
   }
 
   if (docs_in_lanes) {
@@ -430,6 +437,34 @@ void prefill_kernel(PrefillArgs a) {
   issue(0);
   issue(1);
   issue(2);
+  if (rope_q) {
+    // RoPE of this lane's query channels 16ks + 8hi + 0..7, i.e. the pairs
+    // k = 8ks + 4hi + p: the angle position * theta_k is formed and reduced
+    // in fp64 in revolutions (theta_k / 2pi from the host), its sine and
+    // cosine taken in fp32 (v_sin/v_cos take revolutions), the pair rotated
+    // in fp32 and rounded to bf16. Runs while the first K/V tiles load.
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const int t = min(tok[cb], S - 1);
+      const double pos = a.positions ? (double)a.positions[(int64_t)b * S + t] : (double)t;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 r;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int k0 = 8 * ks + p;
+          const double th = hi ? a.theta_rev[k0 + 4] : a.theta_rev[k0];
+          const double rev = pos * th;
+          const float fr = (float)(rev - rint(rev));   // in [-1/2, 1/2]
+          const float cs = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
+          const float x0 = qraw[cb][ks][2 * p], x1 = qraw[cb][ks][2 * p + 1];
+          r[2 * p] = to_bf16(fmaf(x0, cs, -x1 * sn));
+          r[2 * p + 1] = to_bf16(fmaf(x0, sn, x1 * cs));
+        }
+        qreg[cb][ks] = r;
+      }
+    }
+  }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * NL));   // tile 0 landed
   __builtin_amdgcn_s_barrier();
   if (group == 0) {

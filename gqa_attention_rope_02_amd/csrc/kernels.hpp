@@ -34,6 +34,11 @@ struct PrefillArgs {
   int n_qtiles;               // ceil(S / tokens per workgroup)
   float scale_log2;           // softmax scale * log2(e)
   float scale;                // softmax scale
+  // RoPE of the queries inside the kernel (gqa_prefill_rope); rope_q = 0: the
+  // queries arrive rotated
+  int rope_q;
+  const int32_t* positions;   // [B, S] or null (position = s)
+  double theta_rev[64];       // theta_k / (2 pi), k < D/2: angles in revolutions
 };
 
 struct DecodeArgs {

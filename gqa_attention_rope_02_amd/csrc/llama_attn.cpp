@@ -83,12 +83,16 @@ la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
   return launched(la::launch_rope_pair(qa, ka, D, dt == LA_BF16 ? 0 : 1, stream));
 }
 
-la_status gqa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
-                      la_dtype dt, int B, int S, int Hq, int Hkv, int D,
-                      const int64_t q_strides[3], const int64_t k_strides[3],
-                      const int64_t v_strides[3], const int64_t o_strides[3],
-                      const int32_t* cu_docs, int n_docs, float softmax_scale,
-                      hipStream_t stream) {
+namespace {
+
+// gqa_prefill and gqa_prefill_rope: rope_base > 0 asks the kernel to rotate
+// the queries itself (positions as in rope_qk)
+la_status prefill_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                       la_dtype dt, int B, int S, int Hq, int Hkv, int D,
+                       const int64_t q_strides[3], const int64_t k_strides[3],
+                       const int64_t v_strides[3], const int64_t o_strides[3],
+                       const int32_t* cu_docs, int n_docs, float softmax_scale,
+                       const int32_t* positions, double rope_base, hipStream_t stream) {
   if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o) return LA_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return LA_ERR_INVALID_ARG;
@@ -121,7 +125,38 @@ la_status gqa_prefill(const void* q, const void* k, const void* v, void* o, floa
   a.n_qtiles = (int)n_qtiles;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  if (rope_base > 0.0) {
+    // theta_k = base^(-2k/D) as rope_qk forms it, here divided by 2 pi: the
+    // kernel works in revolutions
+    a.rope_q = 1;
+    a.positions = positions;
+    for (int kk = 0; kk < D / 2; ++kk)
+      a.theta_rev[kk] = std::exp2(-(2.0 * kk / D) * std::log2(rope_base)) / 6.283185307179586476925286766559;
+  }
   return launched(la::launch_prefill(a, D, G, dt == LA_BF16 ? 0 : 1, stream));
+}
+
+}  // namespace
+
+la_status gqa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                      la_dtype dt, int B, int S, int Hq, int Hkv, int D,
+                      const int64_t q_strides[3], const int64_t k_strides[3],
+                      const int64_t v_strides[3], const int64_t o_strides[3],
+                      const int32_t* cu_docs, int n_docs, float softmax_scale,
+                      hipStream_t stream) {
+  return prefill_impl(q, k, v, o, lse, dt, B, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
+                      o_strides, cu_docs, n_docs, softmax_scale, nullptr, 0.0, stream);
+}
+
+la_status gqa_prefill_rope(const void* q, const void* k, const void* v, void* o, float* lse,
+                           la_dtype dt, int B, int S, int Hq, int Hkv, int D,
+                           const int64_t q_strides[3], const int64_t k_strides[3],
+                           const int64_t v_strides[3], const int64_t o_strides[3],
+                           const int32_t* cu_docs, int n_docs, float softmax_scale,
+                           const int32_t* positions, double rope_base, hipStream_t stream) {
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
+  return prefill_impl(q, k, v, o, lse, dt, B, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
+                      o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base, stream);
 }
 
 la_status gqa_decode(const void* q, const int64_t q_strides[2], const void* k_cache,

@@ -114,6 +114,27 @@ la_status gqa_prefill(const void* q, const void* k, const void* v, void* o, floa
                       hipStream_t stream);
 
 /*
+ * gqa_prefill_rope — gqa_prefill on queries that are NOT rotated: the kernel
+ * applies the rotary embedding of rope_qk to each query tile in registers
+ * before its products [P1, P2, P4]; keys must arrive rotated (rope_qk with
+ * q_in = q_out = NULL). Saves writing and re-reading the rotated queries.
+ *
+ * Arguments as gqa_prefill, plus positions (int32 [B, S] or NULL for
+ * position = s) and rope_base, as rope_qk takes them. Rotation: the angle
+ * position * theta_k is formed and reduced modulo one turn in fp64, its sine
+ * and cosine are taken in fp32, the pair is rotated in fp32 and rounded to
+ * bf16; a rotated query element may differ by one bf16 ulp from rope_qk's
+ * (which rotates in fp64) in rare cases.
+ * Errors: those of gqa_prefill; INVALID_ARG for rope_base <= 0 or not finite.
+ */
+la_status gqa_prefill_rope(const void* q, const void* k, const void* v, void* o, float* lse,
+                           la_dtype dt, int B, int S, int Hq, int Hkv, int D,
+                           const int64_t q_strides[3], const int64_t k_strides[3],
+                           const int64_t v_strides[3], const int64_t o_strides[3],
+                           const int32_t* cu_docs, int n_docs, float softmax_scale,
+                           const int32_t* positions, double rope_base, hipStream_t stream);
+
+/*
  * gqa_decode — split-KV attention of one new token per sequence over its KV
  * cache; writes per-split partial results for gqa_decode_combine [P2].
  *

@@ -29,10 +29,10 @@ def lib():
     return _lib.load()
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_every_call():
     names = declared_functions()
-    for n in ("rope_qk", "gqa_prefill", "gqa_decode", "gqa_decode_combine", "la_status_str",
-              "la_version"):
+    for n in ("rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_decode", "gqa_decode_combine",
+              "la_status_str", "la_version"):
         assert n in names
 
 
@@ -75,6 +75,25 @@ def prefill(lib, **kw):
 ])
 def test_prefill_rejects(lib, kw, status):
     assert prefill(lib, **kw) == status
+
+
+def prefill_rope(lib, base=5e5, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dt=0, B=1, S=16, Hq=16, Hkv=1, D=128,
+                qs=S3, ks=S3, vs=S3, os_=S3, cu=None, nd=1, scale=0.0)
+    args.update(kw)
+    return lib.gqa_prefill_rope(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dt"],
+                                args["B"], args["S"], args["Hq"], args["Hkv"], args["D"], args["qs"],
+                                args["ks"], args["vs"], args["os_"], args["cu"], args["nd"],
+                                args["scale"], None, base, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(base=0.0), INVALID), (dict(base=-1.0), INVALID), (dict(base=float("inf")), INVALID),
+    (dict(base=float("nan")), INVALID), (dict(q=None), INVALID), (dict(D=96), UNSUPPORTED),
+    (dict(Hq=12, Hkv=8), INVALID), (dict(qs=S3_BAD), INVALID), (dict(cu=FAKE, nd=0), INVALID),
+])
+def test_prefill_rope_rejects(lib, kw, status):
+    assert prefill_rope(lib, **kw) == status
 
 
 def rope(lib, **kw):

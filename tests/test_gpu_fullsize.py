@@ -1,5 +1,6 @@
 """The full-size workloads on the GPU, in the launch configuration bench.py
-times: rope_qk then gqa_prefill over the whole packed sequence, and
+times: rope_qk on the keys then gqa_prefill_rope (queries rotated in the
+kernel) over the whole packed sequence, and
 gqa_decode + gqa_decode_combine over the whole cache with bench.py's kv_chunk.
 
 Outputs the oracle cannot afford everywhere are checked on sampled query rows
@@ -24,17 +25,18 @@ SAMPLES = {"llama8b": (2048, None), "llama405b": (384, 64), "long128k": (96, 32)
 
 
 def _run_full_prefill(q, k, v, cu):
-    """rope_qk + gqa_prefill exactly as bench.py launches them; device outputs."""
+    """The prefill path exactly as bench.py launches it: rope_qk on the keys,
+    then gqa_prefill_rope (queries rotated in the kernel); device outputs."""
     import gqa_attention_rope_02_amd as la
     dev = torch.device("cuda")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    qr, kr = torch.empty_like(qd), torch.empty_like(kd)
-    la.rope_qk(qd, qr, kd, kr)
-    del qd, kd
-    o = torch.full_like(qr, float("nan"))
+    kr = torch.empty_like(kd)
+    la.rope_qk(None, None, kd, kr)
+    del kd
+    o = torch.full_like(qd, float("nan"))
     lse = torch.full((q.shape[0], q.shape[2], q.shape[1]), float("nan"), device=dev)
     cu_d = torch.as_tensor(cu, dtype=torch.int32).reshape(1, -1).to(dev)
-    la.gqa_prefill(qr, kr, vd, o, lse, cu_d)
+    la.gqa_prefill_rope(qd, kr, vd, o, lse, cu_d)
     torch.cuda.synchronize()
     return o, lse
 
@@ -155,12 +157,12 @@ def test_full_size_prefill_is_deterministic(name):
     import gqa_attention_rope_02_amd as la
     H.say("full-size prefill determinism", name)
     st, _ = bench.setup_prefill(name)
-    la.rope_qk(st["q"], st["qr"], st["k"], st["kr"])
+    la.rope_qk(None, None, st["k"], st["kr"])
     first = None
     for _ in range(3):
         o = torch.full_like(st["o"], float("nan"))
         lse = torch.full_like(st["lse"], float("nan"))
-        la.gqa_prefill(st["qr"], st["kr"], st["v"], o, lse, st["cu_d"])
+        la.gqa_prefill_rope(st["q"], st["kr"], st["v"], o, lse, st["cu_d"])
         torch.cuda.synchronize()
         if first is None:
             first = (o, lse)
