@@ -15,7 +15,12 @@ struct RopeArgs {
   int H;                      // heads of this tensor
   const int32_t* positions;   // [B, S] or null
   int B, S;
-  double base;
+};
+
+// theta_k / (2 pi) = base^(-2k/D) / (2 pi) for k < D/2, formed on the host in
+// fp64: RoPE angles in revolutions
+struct RopeAngles {
+  double theta_rev[64];
 };
 
 struct PrefillArgs {
@@ -66,7 +71,8 @@ struct CombineArgs {
 };
 
 // Launchers: return hipSuccess or the launch error. dt: 0 = bf16, 1 = fp32.
-hipError_t launch_rope_pair(const RopeArgs& q, const RopeArgs& k, int D, int dt, hipStream_t st);
+hipError_t launch_rope_pair(const RopeArgs& q, const RopeArgs& k, const RopeAngles& ang, int D, int dt,
+                            hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int D, int G, int dt, hipStream_t st);
 // Sequences per gqa_decode call (the kernel keeps per-sequence tables in LDS).
 constexpr int kDecodeMaxBatch = 1024;

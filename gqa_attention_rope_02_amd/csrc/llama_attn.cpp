@@ -30,6 +30,13 @@ bool strides_ok(const int64_t* s, int n, int esize) {
 
 la_status launched(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH; }
 
+// theta_k = base^(-2k/D) (the RoPE frequencies), divided by 2 pi: the kernels
+// form the angles in revolutions
+void theta_revolutions(double base, int D, double* out) {
+  for (int kk = 0; kk < D / 2; ++kk)
+    out[kk] = std::exp2(-(2.0 * kk / D) * std::log2(base)) / 6.283185307179586476925286766559;
+}
+
 }  // namespace
 
 extern "C" {
@@ -72,15 +79,15 @@ la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
   la::RopeArgs qa{}, ka{};
   if (has_q) {
     qa = la::RopeArgs{q_in, q_out, q_in_strides[0], q_in_strides[1], q_in_strides[2],
-                      q_out_strides[0], q_out_strides[1], q_out_strides[2], Hq, positions, B, S,
-                      rope_base};
+                      q_out_strides[0], q_out_strides[1], q_out_strides[2], Hq, positions, B, S};
   }
   if (has_k) {
     ka = la::RopeArgs{k_in, k_out, k_in_strides[0], k_in_strides[1], k_in_strides[2],
-                      k_out_strides[0], k_out_strides[1], k_out_strides[2], Hkv, positions, B, S,
-                      rope_base};
+                      k_out_strides[0], k_out_strides[1], k_out_strides[2], Hkv, positions, B, S};
   }
-  return launched(la::launch_rope_pair(qa, ka, D, dt == LA_BF16 ? 0 : 1, stream));
+  la::RopeAngles ang{};
+  theta_revolutions(rope_base, D, ang.theta_rev);
+  return launched(la::launch_rope_pair(qa, ka, ang, D, dt == LA_BF16 ? 0 : 1, stream));
 }
 
 namespace {
@@ -126,12 +133,9 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   if (rope_base > 0.0) {
-    // theta_k = base^(-2k/D) as rope_qk forms it, here divided by 2 pi: the
-    // kernel works in revolutions
     a.rope_q = 1;
     a.positions = positions;
-    for (int kk = 0; kk < D / 2; ++kk)
-      a.theta_rev[kk] = std::exp2(-(2.0 * kk / D) * std::log2(rope_base)) / 6.283185307179586476925286766559;
+    theta_revolutions(rope_base, D, a.theta_rev);
   }
   return launched(la::launch_prefill(a, D, G, dt == LA_BF16 ? 0 : 1, stream));
 }
