@@ -53,6 +53,10 @@
 //   offsets is read with one load per lane and searched with wave ballots, the
 //   Q loads are issued right after it, and the first K/V tiles as soon as the
 //   key range is known, so these latencies overlap.
+// * The output goes through LDS (free once the last tile is read): each lane
+//   leaves its 4-value pieces of its column's row there and reads back 16
+//   contiguous bytes, so a wave stores whole rows with 16-byte writes
+//   instead of 8-byte pieces 256 bytes apart.
 // * Workgroups are issued longest-first (last token tiles first), and the KV
 //   head is the fastest-varying index so the workgroups of one KV head land on
 //   one XCD (blockIdx % 8) and share its L2.
@@ -524,31 +528,71 @@ void prefill_kernel(PrefillArgs a) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));          // loads past the last tile
 
   // ---- epilogue --------------------------------------------------------------
+  // o = acc / lt as the reciprocal's product plus one residual step
+  // (q + (acc - q lt) / lt, residual by FMA): a quotient that fp32 can hold
+  // comes out exactly, so a row whose weights are all exact gets an exactly
+  // rounded mean
+  float lt[kCB], rl[kCB];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
-    const float lt = l[cb] + __shfl_xor(l[cb], 32);
-    if (!valid[cb]) continue;
-    // o = acc / lt as the reciprocal's product plus one residual step
-    // (q + (acc - q lt) / lt, residual by FMA): a quotient that fp32 can hold
-    // comes out exactly, so a row whose weights are all exact gets an exactly
-    // rounded mean
-    const float rl = __builtin_amdgcn_rcpf(lt);
-    auto quot = [&](float x) __attribute__((always_inline)) {
-      const float q = x * rl;
-      return fmaf(fmaf(-q, lt, x), rl, q);
-    };
-    T* op = static_cast<T*>(a.o) + b * a.os_b + tok[cb] * a.os_s + head[cb] * a.os_h;
+    lt[cb] = l[cb] + __shfl_xor(l[cb], 32);
+    rl[cb] = __builtin_amdgcn_rcpf(lt[cb]);
+  }
+  auto quot = [&](float x, int cb) __attribute__((always_inline)) {
+    const float q = x * rl[cb];
+    return fmaf(fmaf(-q, lt[cb], x), rl[cb], q);
+  };
+  if constexpr (std::is_same<T, __bf16>::value) {
+    // Through LDS, so that the stores are whole rows: a lane holds 4-value
+    // pieces of its column's row; each wave writes its 32 rows into its own
+    // 32 x ROW bytes of LDS (16-byte chunk c of row r at c ^ (r & (CH - 1)),
+    // so the 32 rows of one write do not all land in one bank) and reads them
+    // back 16 contiguous bytes per lane, D/8 lanes per row. The barrier
+    // orders every wave's last operand reads and LDS-direct loads before the
+    // stage memory is reused; each wave then only touches its own rows.
+    static_assert(kCB == 1, "one 32-column block per wave");
+    __syncthreads();
+    char* ow = lds + wave * 32 * ROW;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
-        const int d = db * 32 + 8 * jq + 4 * hi;
-        store4(op + d, quot(acc[db][cb][4 * jq]), quot(acc[db][cb][4 * jq + 1]),
-               quot(acc[db][cb][4 * jq + 2]), quot(acc[db][cb][4 * jq + 3]));
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = to_bf16(quot(acc[db][0][4 * jq + e], 0));
+        *reinterpret_cast<bf16x4*>(ow + lc * ROW + 16 * ((4 * db + jq) ^ (lc & (CH - 1))) + 8 * hi) = v;
       }
-    if (a.lse && hi == 0)
-      a.lse[((int64_t)b * a.Hq + head[cb]) * S + tok[cb]] = m[cb] * a.scale + fast_log2(lt) * kLn2;
+    constexpr int RPI = 64 / CH;   // rows per wave-wide 16-byte access
+    const int ch = lane % CH;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = i * RPI + lane / CH;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(ow + row * ROW + 16 * (ch ^ (row & (CH - 1))));
+      const int col = wave * 32 + row;
+      const int t = t0 + col / G;
+      if (t < S)
+        *reinterpret_cast<bf16x8*>(static_cast<T*>(a.o) + b * a.os_b + t * a.os_s + (kvh * G + col % G) * a.os_h +
+                                   8 * ch) = v;
+    }
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      if (!valid[cb]) continue;
+      T* op = static_cast<T*>(a.o) + b * a.os_b + tok[cb] * a.os_s + head[cb] * a.os_h;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const int d = db * 32 + 8 * jq + 4 * hi;
+          store4(op + d, quot(acc[db][cb][4 * jq], cb), quot(acc[db][cb][4 * jq + 1], cb),
+                 quot(acc[db][cb][4 * jq + 2], cb), quot(acc[db][cb][4 * jq + 3], cb));
+        }
+    }
   }
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb)
+    if (a.lse && hi == 0 && valid[cb])
+      a.lse[((int64_t)b * a.Hq + head[cb]) * S + tok[cb]] = m[cb] * a.scale + fast_log2(lt[cb]) * kLn2;
 }
 
 template <typename T, int D, int G>
