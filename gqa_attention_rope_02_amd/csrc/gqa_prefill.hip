@@ -447,25 +447,66 @@ void prefill_kernel(PrefillArgs a) {
     // in fp64 in revolutions (theta_k / 2pi from the host), its sine and
     // cosine taken in fp32 (v_sin/v_cos take revolutions), the pair rotated
     // in fp32 and rounded to bf16. Runs while the first K/V tiles load.
+    auto rotate = [&](const float* x, const f32x4& cv, const f32x4& sv) __attribute__((always_inline)) {
+      bf16x8 r;
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      const int t = min(tok[cb], S - 1);
-      const double pos = a.positions ? (double)a.positions[(int64_t)b * S + t] : (double)t;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 r;
+      for (int p = 0; p < 4; ++p) {
+        r[2 * p] = to_bf16(fmaf(x[2 * p], cv[p], -x[2 * p + 1] * sv[p]));
+        r[2 * p + 1] = to_bf16(fmaf(x[2 * p], sv[p], x[2 * p + 1] * cv[p]));
+      }
+      return r;
+    };
+    if constexpr (TQ * (D / 2) * 4 <= TILE) {
+      // The g lanes of a token share its angles: the workgroup forms the
+      // cosine and sine of each (token, pair) once, into the fourth K and V
+      // stages (free until tile 3 is issued), token rows of D/2 values with
+      // 16-byte chunk c at c ^ (row & (CH - 1)).
+      for (int e = tid; e < TQ * CH; e += 64 * kNW) {
+        const int tt = e % TQ, c = e / TQ;
+        const int t = min(t0 + tt, S - 1);
+        const double pos = a.positions ? (double)a.positions[(int64_t)b * S + t] : (double)t;
+        f32x4 cv, sv;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const int k0 = 8 * ks + p;
-          const double th = hi ? a.theta_rev[k0 + 4] : a.theta_rev[k0];
-          const double rev = pos * th;
+          const double rev = pos * a.theta_rev[4 * c + p];
           const float fr = (float)(rev - rint(rev));   // in [-1/2, 1/2]
-          const float cs = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
-          const float x0 = qraw[cb][ks][2 * p], x1 = qraw[cb][ks][2 * p + 1];
-          r[2 * p] = to_bf16(fmaf(x0, cs, -x1 * sn));
-          r[2 * p + 1] = to_bf16(fmaf(x0, sn, x1 * cs));
+          cv[p] = __builtin_amdgcn_cosf(fr);
+          sv[p] = __builtin_amdgcn_sinf(fr);
         }
-        qreg[cb][ks] = r;
+        const int off = tt * ROW + 16 * (c ^ (tt & (CH - 1)));
+        *reinterpret_cast<f32x4*>(lds + 3 * TILE + off) = cv;
+        *reinterpret_cast<f32x4*>(lds + 7 * TILE + off) = sv;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) {
+        const int tt = (wave * 32 * kCB + cb * 32 + lc) / G;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int off = tt * ROW + 16 * ((2 * ks + hi) ^ (tt & (CH - 1)));
+          qreg[cb][ks] = rotate(qraw[cb][ks], *reinterpret_cast<const f32x4*>(lds + 3 * TILE + off),
+                                *reinterpret_cast<const f32x4*>(lds + 7 * TILE + off));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) {
+        const int t = min(tok[cb], S - 1);
+        const double pos = a.positions ? (double)a.positions[(int64_t)b * S + t] : (double)t;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          f32x4 cv, sv;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int k0 = 8 * ks + p;
+            const double th = hi ? a.theta_rev[k0 + 4] : a.theta_rev[k0];
+            const double rev = pos * th;
+            const float fr = (float)(rev - rint(rev));   // in [-1/2, 1/2]
+            cv[p] = __builtin_amdgcn_cosf(fr);
+            sv[p] = __builtin_amdgcn_sinf(fr);
+          }
+          qreg[cb][ks] = rotate(qraw[cb][ks], cv, sv);
+        }
       }
     }
   }
