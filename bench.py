@@ -1,15 +1,17 @@
 """Throughput of the GQA + RoPE attention path on one MI355X.
 
-One step = one pass of the prefill path (rope_qk on Q and K, then gqa_prefill
-with the causal + cross-document mask, writing O and the log-sum-exp) over
-one batch of seeded synthetic input of the Llama-3.1-8B layer shape
-(S=8192, 32 query heads on 8 KV heads, head_dim 128, bf16, 1-8 documents).
-Inputs are resident in HBM before the timed region starts.
+One step = one pass of the prefill path (rope_qk on the keys, then
+gqa_prefill_rope, which rotates the queries in the kernel and applies the
+causal + cross-document mask, writing O and the log-sum-exp) over one batch of
+seeded synthetic input of the Llama-3.1-8B layer shape (S=8192, 32 query heads
+on 8 KV heads, head_dim 128, bf16, 1-8 documents). Inputs are resident in HBM
+before the timed region starts.
 
-The JSON line also carries the 405B-shape prefill (S=32768, 128/8 heads) and
-the 405B-shape split-KV decode (16 sequences, cache lengths U[4096, 131072],
-measured as cache-read GB/s), each against its own roofline, plus the fp64
-oracle timed on a bounded row sample of the headline workload.
+The JSON line also carries the 8B-shape chunked prefill (the last 2048 tokens
+over a cached prefix of 6144), the 405B-shape prefill (S=32768, 128/8 heads)
+and the 405B-shape split-KV decode (16 sequences, cache lengths
+U[4096, 131072], measured as cache-read GB/s), each against its own roofline,
+plus the fp64 oracle timed on a bounded row sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--only prefill|decode] [--with-128k]
@@ -139,6 +141,53 @@ def time_prefill(st, steps: int, warmup: int, settle_s: float = 0.0):
 
 def prefill_flops(w, cu) -> float:
     return 4.0 * w.D * w.Hq * w.B * allowed_pairs(cu)
+
+
+def chunk_pairs(cu_docs: np.ndarray, S: int, Sq: int) -> int:
+    """Visible (query, key) pairs of the last Sq query rows of a sequence."""
+    cu = np.asarray(cu_docs, dtype=np.int64)
+    rows = np.arange(S - Sq, S)
+    start = cu[np.searchsorted(cu, rows, side="right") - 1]
+    return int(np.sum(rows - start + 1))
+
+
+def time_chunk(st, Sq: int, steps: int, warmup: int, settle_s: float = 0.0):
+    """Chunked prefill of the last Sq tokens over the cached prefix: rope_qk on
+    the block's keys (at their positions), then gqa_prefill_chunk with the
+    block's queries rotated in the kernel."""
+    import torch
+    import gqa_attention_rope_02_amd as la
+    w = st["w"]
+    S = w.S
+    dev = st["q"].device
+    qb = st["q"][:, S - Sq:]
+    kb_in, kb_out = st["k"][:, S - Sq:], st["kr"][:, S - Sq:]
+    pos = torch.arange(S - Sq, S, dtype=torch.int32, device=dev).reshape(1, Sq).expand(w.B, Sq).contiguous()
+    ob = torch.empty_like(qb)
+    lse = torch.empty(w.B, w.Hq, Sq, dtype=torch.float32, device=dev)
+    la.rope_qk(None, None, st["k"], st["kr"])               # the cached prefix (and block), once
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        la.rope_qk(None, None, kb_in, kb_out, positions=pos)
+        if evs:
+            evs[1].record()
+        la.gqa_prefill_chunk(qb, st["kr"], st["v"], ob, lse, st["cu_d"], rope_base=w.rope_base)
+        if evs:
+            evs[2].record()
+
+    settle(step, settle_s)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    return dict(rope_ms=float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+                chunk_ms=float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+                gpu_ms_per_step=float(np.mean([e[0].elapsed_time(e[2]) for e in evs])))
 
 
 # ---------------------------------------------------------------------- decode
@@ -323,6 +372,17 @@ def main():
                            "traffic": measured_traffic("gqa_prefill", "llama8b", phash),
                            "launch_ms": round(t["prefill_ms"], 4)}
         out["timing"] = {k: round(x, 4) for k, x in t.items()}
+        Sq = 2048
+        tc = time_chunk(st, Sq, args.steps, args.warmup, args.settle)
+        flc = 4.0 * w.D * w.Hq * w.B * chunk_pairs(cu, w.S, Sq)
+        out["prefill_chunk_8b"] = {
+            "workload": f"llama-3.1-8b chunked prefill: the last {Sq} of {w.S} tokens over the "
+                        f"cached prefix (rope_qk on the block's keys + gqa_prefill_chunk)",
+            "flops": flc,
+            "tflops_path": round(flc / (tc["gpu_ms_per_step"] * 1e-3) / 1e12, 2),
+            "tflops_kernel": round(flc / (tc["chunk_ms"] * 1e-3) / 1e12, 2),
+            "frac_kernel": round(flc / (tc["chunk_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "chunk_ms": round(tc["chunk_ms"], 4), "rope_ms": round(tc["rope_ms"], 4)}
         if not args.no_cpu_baseline:
             log("timing the fp64 oracle on a row sample ...")
             out["cpu_baseline"] = cpu_baseline(host, w, cu)

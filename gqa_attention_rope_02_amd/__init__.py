@@ -15,6 +15,11 @@ contiguous):
 * ``gqa_prefill_rope(q, k, v, o, lse=None, cu_docs=None, softmax_scale=0.0,
   positions=None, rope_base=500000.0)``: as gqa_prefill with unrotated q (the
   kernel rotates it; k must be rotated, e.g. by rope_qk with q_in None).
+* ``gqa_prefill_chunk(q, k, v, o, lse=None, cu_docs=None, softmax_scale=0.0,
+  positions=None, rope_base=0.0)``: q/o [B,Sq,Hq,D] are the last Sq tokens of
+  sequences whose k/v [B,S,Hkv,D] hold all S tokens (a cached prefix plus the
+  block); lse fp32 [B,Hq,Sq]; rope_base 0 = q already rotated, > 0 = rotate q
+  in the kernel at positions [B,Sq] (default S-Sq+i).
 * ``gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk, o_part, lse_part,
   softmax_scale=0.0)``: q [B,Hq,D], caches [B,Hkv,Lmax,D], seq_lens int32 [B],
   o_part fp32 [B,Hq,max_splits,D], lse_part fp32 [B,Hq,max_splits].
@@ -28,7 +33,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["LlamaAttnError", "rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_decode",
+__all__ = ["LlamaAttnError", "rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk", "gqa_decode",
            "gqa_decode_combine", "version", "LA_BF16", "LA_FP32"]
 
 LA_BF16, LA_FP32 = 0, 1
@@ -153,6 +158,27 @@ def gqa_prefill_rope(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float = 
         _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
         _i32(cu_docs), n_docs, float(softmax_scale), _i32(positions), float(rope_base), _stream())
     _check(st, "gqa_prefill_rope")
+
+
+def gqa_prefill_chunk(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float = 0.0,
+                      positions=None, rope_base: float = 0.0):
+    B, Sq, Hq, D = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    n_docs = cu_docs.shape[-1] - 1 if cu_docs is not None else 1
+    _same_shape("gqa_prefill_chunk", (q, o), (k, v))
+    if tuple(k.shape) != (B, S, Hkv, D):
+        raise ValueError("gqa_prefill_chunk: k/v must be [B, S, Hkv, D]")
+    if lse is not None and tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("gqa_prefill_chunk: lse must be [B, Hq, Sq]")
+    if cu_docs is not None and (cu_docs.dim() != 2 or cu_docs.shape[0] != B):
+        raise ValueError("gqa_prefill_chunk: cu_docs must be [B, n_docs + 1]")
+    if positions is not None and tuple(positions.shape) != (B, Sq):
+        raise ValueError("gqa_prefill_chunk: positions must be [B, Sq]")
+    st = _lib.load().gqa_prefill_chunk(
+        _dev(q), _dev(k), _dev(v), _dev(o), _f32c(lse), _dtype(q), B, Sq, S, Hq, Hkv, D,
+        _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
+        _i32(cu_docs), n_docs, float(softmax_scale), _i32(positions), float(rope_base), _stream())
+    _check(st, "gqa_prefill_chunk")
 
 
 def gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk: int, o_part, lse_part,

@@ -131,9 +131,13 @@ void prefill_kernel(PrefillArgs a) {
   const int r = bid / a.Hkv;
   const int b = r % a.B;
   const int qtile = a.n_qtiles - 1 - r / a.B;
-  const int S = a.S;
+  // Query rows 0 .. Sq-1 sit at key positions qo .. qo+Sq-1 of the S keys
+  // (qo = S - Sq: a block of new tokens after a cached prefix; 0 otherwise).
+  // Token indices below are query rows; positions (masks, documents, the key
+  // range) add qo.
+  const int S = a.S, Sq = a.Sq, qo = a.q_off;
   const int t0 = qtile * TQ;
-  const int t_end = min(t0 + TQ, S);
+  const int t_end = min(t0 + TQ, Sq);
   const int32_t* cu = a.cu_docs ? a.cu_docs + (int64_t)b * (a.n_docs + 1) : nullptr;
   const int n_docs = a.n_docs;
 
@@ -149,12 +153,12 @@ void prefill_kernel(PrefillArgs a) {
     const int col = wave * 32 * kCB + cb * 32 + lc;
     tok[cb] = t0 + col / G;
     head[cb] = kvh * G + col % G;
-    valid[cb] = tok[cb] < S;
+    valid[cb] = tok[cb] < Sq;
   }
-  const int w_tmin = min(t0 + (wave * 32 * kCB) / G, S - 1);
+  const int w_tmin = min(t0 + (wave * 32 * kCB) / G, Sq - 1);
   const int w_tmax_raw = t0 + (wave * 32 * kCB + 32 * kCB - 1) / G;
-  const bool wave_all_valid = w_tmax_raw < S;
-  const int w_tmax = min(w_tmax_raw, S - 1);
+  const bool wave_all_valid = w_tmax_raw < Sq;
+  const int w_tmax = min(w_tmax_raw, Sq - 1);
 
   // ---- document starts ---------------------------------------------------------
   // With at most 63 documents the offsets row is read once, one entry per
@@ -166,10 +170,10 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) st[cb] = 0;
   if (cu && !docs_in_lanes) {
-    kv_start = doc_start(cu, n_docs, t0);
+    kv_start = doc_start(cu, n_docs, t0 + qo);
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) st[cb] = valid[cb] ? doc_start(cu, n_docs, tok[cb]) : 0;
-    w_smax = doc_start(cu, n_docs, w_tmax);
+    for (int cb = 0; cb < kCB; ++cb) st[cb] = valid[cb] ? doc_start(cu, n_docs, tok[cb] + qo) : 0;
+    w_smax = doc_start(cu, n_docs, w_tmax + qo);
   }
   int cu_l = 0;
   if (docs_in_lanes) cu_l = cu[min(lane, n_docs)];
@@ -183,7 +187,7 @@ void prefill_kernel(PrefillArgs a) {
   const bool rope_q = a.rope_q != 0;
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
-    const T* qp = qbase + min(tok[cb], S - 1) * a.qs_s + head[cb] * a.qs_h + 8 * hi;
+    const T* qp = qbase + min(tok[cb], Sq - 1) * a.qs_s + head[cb] * a.qs_h + 8 * hi;
     if (rope_q) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) load8_f32(qp + 16 * ks, qraw[cb][ks]);
@@ -194,28 +198,29 @@ void prefill_kernel(PrefillArgs a) {
   }
 
   if (docs_in_lanes) {
-    // index of the document holding token t (the same t in every lane): the
-    // last of the first n_docs offsets that is <= t, else 0
+    // index of the document holding position t (the same t in every lane):
+    // the last of the first n_docs offsets that is <= t, else 0
     auto doc_of = [&](int t) __attribute__((always_inline)) -> int {
       const unsigned long long mk = __ballot(lane < n_docs && cu_l <= t);
       return mk ? 63 - __clzll(mk) : 0;
     };
-    const int d0 = doc_of(t0);
+    const int d0 = doc_of(t0 + qo);
     kv_start = __builtin_amdgcn_readlane(cu_l, d0);
     // the documents that start inside this workgroup's tokens follow d0
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) st[cb] = kv_start;
     for (int d = d0 + 1; d < n_docs; ++d) {
       const int c = __builtin_amdgcn_readlane(cu_l, d);
-      if (c >= t_end) break;
+      if (c >= t_end + qo) break;
 #pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) st[cb] = tok[cb] >= c ? c : st[cb];
+      for (int cb = 0; cb < kCB; ++cb) st[cb] = tok[cb] + qo >= c ? c : st[cb];
     }
-    w_smax = __builtin_amdgcn_readlane(cu_l, doc_of(w_tmax));
+    w_smax = __builtin_amdgcn_readlane(cu_l, doc_of(w_tmax + qo));
   }
-  // clamp: out-of-contract offsets must not move the key range out of [0, t0]
-  const int kv_lo = max(0, min(kv_start, t0));
-  const int kv_hi = t_end - 1;
+  // clamp: out-of-contract offsets must not move the key range out of
+  // [0, t0 + qo]
+  const int kv_lo = max(0, min(kv_start, t0 + qo));
+  const int kv_hi = t_end - 1 + qo;
 
   f32x16 acc[DB][kCB];
 #pragma unroll
@@ -346,9 +351,9 @@ void prefill_kernel(PrefillArgs a) {
   };
   auto sm_tile = [&](int k) __attribute__((always_inline)) {
     const int kt = kv_lo + k * kKT;
-    if (!wave_all_valid || kt + kKT - 1 > w_tmin || kt < w_smax) {
+    if (!wave_all_valid || kt + kKT - 1 > w_tmin + qo || kt < w_smax) {
       const int lo = valid[0] ? st[0] - kt : kKT;
-      const int hi_ = valid[0] ? tok[0] - kt : -1;
+      const int hi_ = valid[0] ? tok[0] + qo - kt : -1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -463,8 +468,8 @@ void prefill_kernel(PrefillArgs a) {
       // 16-byte chunk c at c ^ (row & (CH - 1)).
       for (int e = tid; e < TQ * CH; e += 64 * kNW) {
         const int tt = e % TQ, c = e / TQ;
-        const int t = min(t0 + tt, S - 1);
-        const double pos = a.positions ? (double)a.positions[(int64_t)b * S + t] : (double)t;
+        const int t = min(t0 + tt, Sq - 1);
+        const double pos = a.positions ? (double)a.positions[(int64_t)b * Sq + t] : (double)(t + qo);
         f32x4 cv, sv;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -491,8 +496,8 @@ void prefill_kernel(PrefillArgs a) {
     } else {
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
-        const int t = min(tok[cb], S - 1);
-        const double pos = a.positions ? (double)a.positions[(int64_t)b * S + t] : (double)t;
+        const int t = min(tok[cb], Sq - 1);
+        const double pos = a.positions ? (double)a.positions[(int64_t)b * Sq + t] : (double)(t + qo);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           f32x4 cv, sv;
@@ -611,7 +616,7 @@ void prefill_kernel(PrefillArgs a) {
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(ow + row * ROW + 16 * (ch ^ (row & (CH - 1))));
       const int col = wave * 32 + row;
       const int t = t0 + col / G;
-      if (t < S)
+      if (t < Sq)
         *reinterpret_cast<bf16x8*>(static_cast<T*>(a.o) + b * a.os_b + t * a.os_s + (kvh * G + col % G) * a.os_h +
                                    8 * ch) = v;
     }
@@ -633,7 +638,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb)
     if (a.lse && hi == 0 && valid[cb])
-      a.lse[((int64_t)b * a.Hq + head[cb]) * S + tok[cb]] = m[cb] * a.scale + fast_log2(lt[cb]) * kLn2;
+      a.lse[((int64_t)b * a.Hq + head[cb]) * Sq + tok[cb]] = m[cb] * a.scale + fast_log2(lt[cb]) * kLn2;
 }
 
 template <typename T, int D, int G>

@@ -35,8 +35,9 @@ struct PrefillArgs {
   int64_t os_b, os_s, os_h;
   const int32_t* cu_docs;     // [B, n_docs + 1] or null
   int n_docs;
-  int B, S, Hq, Hkv;
-  int n_qtiles;               // ceil(S / tokens per workgroup)
+  int B, S, Hq, Hkv;           // S: keys (and key positions) per sequence
+  int Sq, q_off;              // query rows per sequence, at positions q_off .. q_off + Sq - 1
+  int n_qtiles;               // ceil(Sq / tokens per workgroup)
   float scale_log2;           // softmax scale * log2(e)
   float scale;                // softmax scale
   // RoPE of the queries inside the kernel (gqa_prefill_rope); rope_q = 0: the

@@ -92,10 +92,11 @@ la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
 
 namespace {
 
-// gqa_prefill and gqa_prefill_rope: rope_base > 0 asks the kernel to rotate
-// the queries itself (positions as in rope_qk)
+// gqa_prefill, gqa_prefill_rope and gqa_prefill_chunk: the Sq queries of each
+// sequence are its last Sq tokens of S; rope_base > 0 asks the kernel to
+// rotate the queries itself (positions as in rope_qk)
 la_status prefill_impl(const void* q, const void* k, const void* v, void* o, float* lse,
-                       la_dtype dt, int B, int S, int Hq, int Hkv, int D,
+                       la_dtype dt, int B, int Sq, int S, int Hq, int Hkv, int D,
                        const int64_t q_strides[3], const int64_t k_strides[3],
                        const int64_t v_strides[3], const int64_t o_strides[3],
                        const int32_t* cu_docs, int n_docs, float softmax_scale,
@@ -103,6 +104,7 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
   if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o) return LA_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return LA_ERR_INVALID_ARG;
+  if (Sq < 1 || Sq > S) return LA_ERR_INVALID_ARG;
   if (cu_docs && n_docs < 1) return LA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return LA_ERR_INVALID_ARG;
   if (!supported_d(D) || !supported_g(Hq / Hkv)) return LA_ERR_UNSUPPORTED;
@@ -117,7 +119,7 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
   if (!std::isfinite(softmax_scale)) return LA_ERR_INVALID_ARG;
   const int G = Hq / Hkv;
   const int tq = la::prefill_tokens_per_block(G);
-  const long long n_qtiles = (S + tq - 1) / tq;
+  const long long n_qtiles = (Sq + tq - 1) / tq;
   if ((long long)B * Hkv * n_qtiles > 0x7fffffffLL) return LA_ERR_INVALID_ARG;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
 
@@ -129,6 +131,7 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
   a.os_b = o_strides[0]; a.os_s = o_strides[1]; a.os_h = o_strides[2];
   a.cu_docs = cu_docs; a.n_docs = cu_docs ? n_docs : 1;
   a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv;
+  a.Sq = Sq; a.q_off = S - Sq;
   a.n_qtiles = (int)n_qtiles;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -148,7 +151,7 @@ la_status gqa_prefill(const void* q, const void* k, const void* v, void* o, floa
                       const int64_t v_strides[3], const int64_t o_strides[3],
                       const int32_t* cu_docs, int n_docs, float softmax_scale,
                       hipStream_t stream) {
-  return prefill_impl(q, k, v, o, lse, dt, B, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
+  return prefill_impl(q, k, v, o, lse, dt, B, S, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
                       o_strides, cu_docs, n_docs, softmax_scale, nullptr, 0.0, stream);
 }
 
@@ -159,7 +162,18 @@ la_status gqa_prefill_rope(const void* q, const void* k, const void* v, void* o,
                            const int32_t* cu_docs, int n_docs, float softmax_scale,
                            const int32_t* positions, double rope_base, hipStream_t stream) {
   if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
-  return prefill_impl(q, k, v, o, lse, dt, B, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
+  return prefill_impl(q, k, v, o, lse, dt, B, S, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
+                      o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base, stream);
+}
+
+la_status gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, float* lse,
+                            la_dtype dt, int B, int Sq, int S, int Hq, int Hkv, int D,
+                            const int64_t q_strides[3], const int64_t k_strides[3],
+                            const int64_t v_strides[3], const int64_t o_strides[3],
+                            const int32_t* cu_docs, int n_docs, float softmax_scale,
+                            const int32_t* positions, double rope_base, hipStream_t stream) {
+  if (!(rope_base >= 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
+  return prefill_impl(q, k, v, o, lse, dt, B, Sq, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
                       o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base, stream);
 }
 

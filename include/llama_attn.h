@@ -135,6 +135,34 @@ la_status gqa_prefill_rope(const void* q, const void* k, const void* v, void* o,
                            const int32_t* positions, double rope_base, hipStream_t stream);
 
 /*
+ * gqa_prefill_chunk — prefill of a block of new tokens after a cached prefix
+ * (chunked prefill): the Sq queries of each sequence are its LAST Sq tokens,
+ * at positions S - Sq .. S - 1, and attend to the keys of all S tokens (the
+ * cached prefix and the block itself) under the same causal and document
+ * rules as gqa_prefill [P2, P4]. The result equals rows S - Sq .. S - 1 of
+ * gqa_prefill over the whole sequence.
+ *
+ * q: [B, Sq, Hq, D]; k and v: [B, S, Hkv, D] (keys rotated, e.g. by rope_qk,
+ *   each at its own position); o: [B, Sq, Hq, D]; strides as in gqa_prefill.
+ * cu_docs: as in gqa_prefill, over the S tokens (row b non-decreasing from 0
+ *   to S); NULL means one document per sequence.
+ * lse: optional fp32 [B, Hq, Sq] (contiguous), NULL to skip.
+ * rope_base: 0 means the queries arrive rotated; > 0 means they are rotated
+ *   in the kernel as in gqa_prefill_rope, at positions (int32 [B, Sq], or NULL
+ *   for position S - Sq + i of query row i).
+ * Requirements: 1 <= Sq <= S. Arithmetic as gqa_prefill (and
+ *   gqa_prefill_rope for the rotation).
+ * Errors: those of gqa_prefill; INVALID_ARG for Sq < 1 or Sq > S, and for
+ * rope_base < 0 or not finite.
+ */
+la_status gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, float* lse,
+                            la_dtype dt, int B, int Sq, int S, int Hq, int Hkv, int D,
+                            const int64_t q_strides[3], const int64_t k_strides[3],
+                            const int64_t v_strides[3], const int64_t o_strides[3],
+                            const int32_t* cu_docs, int n_docs, float softmax_scale,
+                            const int32_t* positions, double rope_base, hipStream_t stream);
+
+/*
  * gqa_decode — split-KV attention of one new token per sequence over its KV
  * cache; writes per-split partial results for gqa_decode_combine [P2].
  *

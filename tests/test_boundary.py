@@ -31,8 +31,8 @@ def lib():
 
 def test_header_declares_every_call():
     names = declared_functions()
-    for n in ("rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_decode", "gqa_decode_combine",
-              "la_status_str", "la_version"):
+    for n in ("rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk", "gqa_decode",
+              "gqa_decode_combine", "la_status_str", "la_version"):
         assert n in names
 
 
@@ -94,6 +94,26 @@ def prefill_rope(lib, base=5e5, **kw):
 ])
 def test_prefill_rope_rejects(lib, kw, status):
     assert prefill_rope(lib, **kw) == status
+
+
+def prefill_chunk(lib, base=0.0, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dt=0, B=1, Sq=4, S=16, Hq=16, Hkv=1,
+                D=128, qs=S3, ks=S3, vs=S3, os_=S3, cu=None, nd=1, scale=0.0)
+    args.update(kw)
+    return lib.gqa_prefill_chunk(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dt"],
+                                 args["B"], args["Sq"], args["S"], args["Hq"], args["Hkv"], args["D"],
+                                 args["qs"], args["ks"], args["vs"], args["os_"], args["cu"],
+                                 args["nd"], args["scale"], None, base, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Sq=0), INVALID), (dict(Sq=17), INVALID), (dict(S=0), INVALID),
+    (dict(base=-1.0), INVALID), (dict(base=float("inf")), INVALID), (dict(base=float("nan")), INVALID),
+    (dict(q=None), INVALID), (dict(D=96), UNSUPPORTED), (dict(Hq=12, Hkv=8), INVALID),
+    (dict(qs=S3_BAD), INVALID), (dict(cu=FAKE, nd=0), INVALID),
+])
+def test_prefill_chunk_rejects(lib, kw, status):
+    assert prefill_chunk(lib, **kw) == status
 
 
 def rope(lib, **kw):
