@@ -151,10 +151,14 @@ def chunk_pairs(cu_docs: np.ndarray, S: int, Sq: int) -> int:
     return int(np.sum(rows - start + 1))
 
 
-def time_chunk(st, Sq: int, steps: int, warmup: int, settle_s: float = 0.0):
+CHUNK_SPLIT_TILES = 24   # key tiles per piece for the chunked prefill (gqa_prefill_split)
+
+
+def time_chunk(st, Sq: int, steps: int, warmup: int, settle_s: float = 0.0, split_tiles: int = 0):
     """Chunked prefill of the last Sq tokens over the cached prefix: rope_qk on
     the block's keys (at their positions), then gqa_prefill_chunk with the
-    block's queries rotated in the kernel."""
+    block's queries rotated in the kernel (or gqa_prefill_split with key ranges
+    cut into pieces of split_tiles tiles, its workspace allocated beforehand)."""
     import torch
     import gqa_attention_rope_02_amd as la
     w = st["w"]
@@ -166,6 +170,8 @@ def time_chunk(st, Sq: int, steps: int, warmup: int, settle_s: float = 0.0):
     ob = torch.empty_like(qb)
     lse = torch.empty(w.B, w.Hq, Sq, dtype=torch.float32, device=dev)
     la.rope_qk(None, None, st["k"], st["kr"])               # the cached prefix (and block), once
+    if split_tiles:
+        op, lp = la.prefill_split_workspace(w.B, Sq, S, w.Hq, w.D, split_tiles, dev)
 
     def step(evs=None):
         if evs:
@@ -173,7 +179,11 @@ def time_chunk(st, Sq: int, steps: int, warmup: int, settle_s: float = 0.0):
         la.rope_qk(None, None, kb_in, kb_out, positions=pos)
         if evs:
             evs[1].record()
-        la.gqa_prefill_chunk(qb, st["kr"], st["v"], ob, lse, st["cu_d"], rope_base=w.rope_base)
+        if split_tiles:
+            la.gqa_prefill_split(qb, st["kr"], st["v"], ob, split_tiles, op, lp, lse, st["cu_d"],
+                                 rope_base=w.rope_base)
+        else:
+            la.gqa_prefill_chunk(qb, st["kr"], st["v"], ob, lse, st["cu_d"], rope_base=w.rope_base)
         if evs:
             evs[2].record()
 
@@ -373,16 +383,20 @@ def main():
                            "launch_ms": round(t["prefill_ms"], 4)}
         out["timing"] = {k: round(x, 4) for k, x in t.items()}
         Sq = 2048
-        tc = time_chunk(st, Sq, args.steps, args.warmup, args.settle)
+        tc = time_chunk(st, Sq, args.steps, args.warmup, args.settle, CHUNK_SPLIT_TILES)
+        tu = time_chunk(st, Sq, args.steps, args.warmup, 0.0)
         flc = 4.0 * w.D * w.Hq * w.B * chunk_pairs(cu, w.S, Sq)
         out["prefill_chunk_8b"] = {
             "workload": f"llama-3.1-8b chunked prefill: the last {Sq} of {w.S} tokens over the "
-                        f"cached prefix (rope_qk on the block's keys + gqa_prefill_chunk)",
+                        f"cached prefix (rope_qk on the block's keys + gqa_prefill_split, key ranges "
+                        f"in pieces of {CHUNK_SPLIT_TILES} x 64 keys, partials merged)",
             "flops": flc,
             "tflops_path": round(flc / (tc["gpu_ms_per_step"] * 1e-3) / 1e12, 2),
             "tflops_kernel": round(flc / (tc["chunk_ms"] * 1e-3) / 1e12, 2),
             "frac_kernel": round(flc / (tc["chunk_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "chunk_ms": round(tc["chunk_ms"], 4), "rope_ms": round(tc["rope_ms"], 4)}
+            "chunk_ms": round(tc["chunk_ms"], 4), "rope_ms": round(tc["rope_ms"], 4),
+            "unsplit_chunk_ms": round(tu["chunk_ms"], 4),
+            "unsplit_tflops_kernel": round(flc / (tu["chunk_ms"] * 1e-3) / 1e12, 2)}
         if not args.no_cpu_baseline:
             log("timing the fp64 oracle on a row sample ...")
             out["cpu_baseline"] = cpu_baseline(host, w, cu)

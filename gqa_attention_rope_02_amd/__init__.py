@@ -20,6 +20,11 @@ contiguous):
   sequences whose k/v [B,S,Hkv,D] hold all S tokens (a cached prefix plus the
   block); lse fp32 [B,Hq,Sq]; rope_base 0 = q already rotated, > 0 = rotate q
   in the kernel at positions [B,Sq] (default S-Sq+i).
+* ``gqa_prefill_split(q, k, v, o, split_tiles, o_part, lse_part, lse=None, cu_docs=None,
+  softmax_scale=0.0, positions=None, rope_base=0.0)``: gqa_prefill_chunk with each query
+  tile's key range cut into pieces of split_tiles x 64 keys (workspace o_part fp32
+  [max_splits,B,Sq,Hq,D], lse_part fp32 [max_splits,B,Hq,Sq]; ``prefill_split_workspace``
+  allocates it).
 * ``gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk, o_part, lse_part,
   softmax_scale=0.0)``: q [B,Hq,D], caches [B,Hkv,Lmax,D], seq_lens int32 [B],
   o_part fp32 [B,Hq,max_splits,D], lse_part fp32 [B,Hq,max_splits].
@@ -33,7 +38,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["LlamaAttnError", "rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk", "gqa_decode",
+__all__ = ["LlamaAttnError", "rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk",
+           "gqa_prefill_split", "prefill_split_workspace", "gqa_decode",
            "gqa_decode_combine", "version", "LA_BF16", "LA_FP32"]
 
 LA_BF16, LA_FP32 = 0, 1
@@ -179,6 +185,42 @@ def gqa_prefill_chunk(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float =
         _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
         _i32(cu_docs), n_docs, float(softmax_scale), _i32(positions), float(rope_base), _stream())
     _check(st, "gqa_prefill_chunk")
+
+
+def prefill_split_workspace(B: int, Sq: int, S: int, Hq: int, D: int, split_tiles: int, device=None):
+    """(o_part, lse_part) of the smallest max_splits gqa_prefill_split accepts."""
+    max_splits = (-(-S // 64) + split_tiles - 1) // split_tiles
+    o_part = torch.empty(max_splits, B, Sq, Hq, D, dtype=torch.float32, device=device)
+    lse_part = torch.empty(max_splits, B, Hq, Sq, dtype=torch.float32, device=device)
+    return o_part, lse_part
+
+
+def gqa_prefill_split(q, k, v, o, split_tiles: int, o_part, lse_part, lse=None, cu_docs=None,
+                      softmax_scale: float = 0.0, positions=None, rope_base: float = 0.0):
+    B, Sq, Hq, D = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    n_docs = cu_docs.shape[-1] - 1 if cu_docs is not None else 1
+    _same_shape("gqa_prefill_split", (q, o), (k, v))
+    max_splits = o_part.shape[0]
+    if tuple(k.shape) != (B, S, Hkv, D):
+        raise ValueError("gqa_prefill_split: k/v must be [B, S, Hkv, D]")
+    if lse is not None and tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("gqa_prefill_split: lse must be [B, Hq, Sq]")
+    if cu_docs is not None and (cu_docs.dim() != 2 or cu_docs.shape[0] != B):
+        raise ValueError("gqa_prefill_split: cu_docs must be [B, n_docs + 1]")
+    if positions is not None and tuple(positions.shape) != (B, Sq):
+        raise ValueError("gqa_prefill_split: positions must be [B, Sq]")
+    if tuple(o_part.shape) != (max_splits, B, Sq, Hq, D) or tuple(lse_part.shape) != (max_splits, B, Hq, Sq) \
+            or o_part.dtype != torch.float32 or lse_part.dtype != torch.float32 \
+            or not o_part.is_contiguous() or not lse_part.is_contiguous():
+        raise ValueError("gqa_prefill_split: workspace must be contiguous fp32 [max_splits, B, Sq, Hq, D] "
+                         "and [max_splits, B, Hq, Sq]")
+    st = _lib.load().gqa_prefill_split(
+        _dev(q), _dev(k), _dev(v), _dev(o), _f32c(lse), _dtype(q), B, Sq, S, Hq, Hkv, D,
+        _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
+        _i32(cu_docs), n_docs, float(softmax_scale), _i32(positions), float(rope_base),
+        int(split_tiles), int(max_splits), _dev(o_part), _dev(lse_part), _stream())
+    _check(st, "gqa_prefill_split")
 
 
 def gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk: int, o_part, lse_part,

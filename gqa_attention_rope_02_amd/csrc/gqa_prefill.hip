@@ -219,8 +219,32 @@ void prefill_kernel(PrefillArgs a) {
   }
   // clamp: out-of-contract offsets must not move the key range out of
   // [0, t0 + qo]
-  const int kv_lo = max(0, min(kv_start, t0 + qo));
+  int kv_lo = max(0, min(kv_start, t0 + qo));
   const int kv_hi = t_end - 1 + qo;
+  int n_tiles = (kv_hi - kv_lo) / kKT + 1;
+
+  // Split key ranges (split_tiles > 0): workgroup (tile, split sp) takes the
+  // key tiles [sp * split_tiles, (sp + 1) * split_tiles) of its query tile's
+  // range. A query tile that needs one split writes its final output (and
+  // marks its rows with lse_part = +inf in slot 0); one that needs more
+  // writes partial results to slot sp for the merge, and the workgroups of
+  // its unused slots mark them lse_part = -inf. Nothing has touched LDS yet.
+  const int sp = blockIdx.y;
+  int n_split = 1;
+  if (a.split_tiles > 0) {
+    n_split = (n_tiles + a.split_tiles - 1) / a.split_tiles;
+    if (sp >= n_split) {
+      if (n_split > 1 && hi == 0)
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb)
+          if (valid[cb])
+            a.lse_part[(((int64_t)sp * a.B + b) * a.Hq + head[cb]) * Sq + tok[cb]] = -INFINITY;
+      __builtin_amdgcn_s_waitcnt(0);   // the Q loads already issued
+      return;
+    }
+    kv_lo += sp * a.split_tiles * kKT;
+    n_tiles = min(a.split_tiles, n_tiles - sp * a.split_tiles);
+  }
 
   f32x16 acc[DB][kCB];
 #pragma unroll
@@ -303,7 +327,6 @@ void prefill_kernel(PrefillArgs a) {
   // VALU. K/V: four LDS stages; tile k+3 is issued at the start of iteration k
   // (phase 2k+2, when the stage of tile k-1 is free in both groups) and must
   // have landed at the end of phase 2k+5, before its first read in phase 2k+6.
-  const int n_tiles = (kv_hi - kv_lo) / kKT + 1;
   const int group = wave >> 2;
   auto stage_ptr = [&](int k) __attribute__((always_inline)) -> char* { return lds + (k & 3) * TILE; };
   // tiles past the last one are issued as loads that read nothing, so every
@@ -578,16 +601,40 @@ void prefill_kernel(PrefillArgs a) {
   // (q + (acc - q lt) / lt, residual by FMA): a quotient that fp32 can hold
   // comes out exactly, so a row whose weights are all exact gets an exactly
   // rounded mean
+  // (a row with no visible key in its range, possible with split key
+  // ranges, gets o = 0 and lse = -inf)
   float lt[kCB], rl[kCB];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
     lt[cb] = l[cb] + __shfl_xor(l[cb], 32);
-    rl[cb] = __builtin_amdgcn_rcpf(lt[cb]);
+    rl[cb] = lt[cb] > 0.f ? __builtin_amdgcn_rcpf(lt[cb]) : 0.f;
   }
   auto quot = [&](float x, int cb) __attribute__((always_inline)) {
     const float q = x * rl[cb];
     return fmaf(fmaf(-q, lt[cb], x), rl[cb], q);
   };
+  auto row_lse = [&](int cb) __attribute__((always_inline)) {
+    return lt[cb] > 0.f ? m[cb] * a.scale + fast_log2(lt[cb]) * kLn2 : -INFINITY;
+  };
+  if (n_split > 1) {
+    // partial result of this split: fp32 o (normalised by its own row sum)
+    // and lse, slot sp
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      if (!valid[cb]) continue;
+      float* op = a.o_part + ((((int64_t)sp * a.B + b) * Sq + tok[cb]) * a.Hq + head[cb]) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const f32x4 v = {quot(acc[db][cb][4 * jq], cb), quot(acc[db][cb][4 * jq + 1], cb),
+                           quot(acc[db][cb][4 * jq + 2], cb), quot(acc[db][cb][4 * jq + 3], cb)};
+          *reinterpret_cast<f32x4*>(op + db * 32 + 8 * jq + 4 * hi) = v;
+        }
+      if (hi == 0) a.lse_part[(((int64_t)sp * a.B + b) * a.Hq + head[cb]) * Sq + tok[cb]] = row_lse(cb);
+    }
+    return;
+  }
   if constexpr (std::is_same<T, __bf16>::value) {
     // Through LDS, so that the stores are whole rows: a lane holds 4-value
     // pieces of its column's row; each wave writes its 32 rows into its own
@@ -636,15 +683,66 @@ void prefill_kernel(PrefillArgs a) {
     }
   }
 #pragma unroll
-  for (int cb = 0; cb < kCB; ++cb)
-    if (a.lse && hi == 0 && valid[cb])
-      a.lse[((int64_t)b * a.Hq + head[cb]) * Sq + tok[cb]] = m[cb] * a.scale + fast_log2(lt[cb]) * kLn2;
+  for (int cb = 0; cb < kCB; ++cb) {
+    if (hi != 0 || !valid[cb]) continue;
+    if (a.lse) a.lse[((int64_t)b * a.Hq + head[cb]) * Sq + tok[cb]] = row_lse(cb);
+    if (a.split_tiles > 0) a.lse_part[((int64_t)b * a.Hq + head[cb]) * Sq + tok[cb]] = INFINITY;
+  }
 }
 
 template <typename T, int D, int G>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)a.B * a.Hkv * a.n_qtiles;
-  hipLaunchKernelGGL((prefill_kernel<T, D, G>), dim3(grid), dim3(64 * kNW), 0, st, a);
+  const unsigned splits = a.split_tiles > 0 ? (unsigned)a.max_splits : 1u;
+  hipLaunchKernelGGL((prefill_kernel<T, D, G>), dim3(grid, splits), dim3(64 * kNW), 0, st, a);
+  return hipGetLastError();
+}
+
+// Merge of split partials: one group of D/4 lanes per (sequence, query row,
+// head), 4 values per lane. Rows marked +inf in slot 0 were written whole by
+// the prefill kernel; the others take M = max_s lse_s, w_s = exp(lse_s - M),
+// o = sum_s w_s o_s / sum_s w_s, lse = M + ln(sum_s w_s) over the slots with
+// lse_s > -inf.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(PrefillArgs a) {
+  constexpr int LPR = D / 4;             // lanes per row
+  constexpr int RPB = 256 / LPR;         // rows per block
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;   // (b, tok, head), head fastest
+  const int lane = threadIdx.x % LPR;
+  const int64_t rows = (int64_t)a.B * a.Sq * a.Hq;
+  if (r >= rows) return;
+  const int h = (int)(r % a.Hq);
+  const int64_t bt = r / a.Hq;
+  const int tok = (int)(bt % a.Sq), b = (int)(bt / a.Sq);
+  const int64_t slot_stride = (int64_t)a.B * a.Hq * a.Sq;
+  const float* lp = a.lse_part + ((int64_t)b * a.Hq + h) * a.Sq + tok;
+  if (lp[0] == INFINITY) return;
+  float M = -INFINITY;
+  for (int s = 0; s < a.max_splits; ++s) M = fmaxf(M, lp[s * slot_stride]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float W = 0.f;
+  if (M > -INFINITY) {
+    for (int s = 0; s < a.max_splits; ++s) {
+      const float ls = lp[s * slot_stride];
+      if (!(ls > -INFINITY)) continue;
+      const float w = __expf(ls - M);
+      const f32x4 o = *reinterpret_cast<const f32x4*>(
+          a.o_part + ((((int64_t)s * a.B + b) * a.Sq + tok) * a.Hq + h) * D + 4 * lane);
+      acc += w * o;
+      W += w;
+    }
+  }
+  const float rw = W > 0.f ? 1.f / W : 0.f;
+  T* op = static_cast<T*>(a.o) + b * a.os_b + tok * a.os_s + h * a.os_h + 4 * lane;
+  store4(op, acc[0] * rw, acc[1] * rw, acc[2] * rw, acc[3] * rw);
+  if (a.lse && lane == 0) a.lse[((int64_t)b * a.Hq + h) * a.Sq + tok] = W > 0.f ? M + __logf(W) : -INFINITY;
+}
+
+template <typename T, int D>
+hipError_t launch_merge_t(const PrefillArgs& a, hipStream_t st) {
+  constexpr int RPB = 256 / (D / 4);
+  const int64_t rows = (int64_t)a.B * a.Sq * a.Hq;
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -665,6 +763,11 @@ hipError_t launch_g(const PrefillArgs& a, int G, hipStream_t st) {
 hipError_t launch_prefill(const PrefillArgs& a, int D, int G, int dt, hipStream_t st) {
   if (dt == 0) return D == 64 ? launch_g<__bf16, 64>(a, G, st) : launch_g<__bf16, 128>(a, G, st);
   return D == 64 ? launch_g<float, 64>(a, G, st) : launch_g<float, 128>(a, G, st);
+}
+
+hipError_t launch_prefill_merge(const PrefillArgs& a, int D, int dt, hipStream_t st) {
+  if (dt == 0) return D == 64 ? launch_merge_t<__bf16, 64>(a, st) : launch_merge_t<__bf16, 128>(a, st);
+  return D == 64 ? launch_merge_t<float, 64>(a, st) : launch_merge_t<float, 128>(a, st);
 }
 
 }  // namespace la

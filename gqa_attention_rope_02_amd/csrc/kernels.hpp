@@ -45,6 +45,11 @@ struct PrefillArgs {
   int rope_q;
   const int32_t* positions;   // [B, S] or null (position = s)
   double theta_rev[64];       // theta_k / (2 pi), k < D/2: angles in revolutions
+  // split key ranges (split_tiles > 0): partials in o_part fp32
+  // [max_splits, B, Sq, Hq, D] and lse_part fp32 [max_splits, B, Hq, Sq]
+  int split_tiles, max_splits;
+  float* o_part;
+  float* lse_part;
 };
 
 struct DecodeArgs {
@@ -75,6 +80,7 @@ struct CombineArgs {
 hipError_t launch_rope_pair(const RopeArgs& q, const RopeArgs& k, const RopeAngles& ang, int D, int dt,
                             hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int D, int G, int dt, hipStream_t st);
+hipError_t launch_prefill_merge(const PrefillArgs& a, int D, int dt, hipStream_t st);
 // Sequences per gqa_decode call (the kernel keeps per-sequence tables in LDS).
 constexpr int kDecodeMaxBatch = 1024;
 

@@ -100,7 +100,9 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
                        const int64_t q_strides[3], const int64_t k_strides[3],
                        const int64_t v_strides[3], const int64_t o_strides[3],
                        const int32_t* cu_docs, int n_docs, float softmax_scale,
-                       const int32_t* positions, double rope_base, hipStream_t stream) {
+                       const int32_t* positions, double rope_base, hipStream_t stream,
+                       int split_tiles = 0, int max_splits = 0, float* o_part = nullptr,
+                       float* lse_part = nullptr) {
   if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o) return LA_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return LA_ERR_INVALID_ARG;
@@ -122,6 +124,13 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
   const long long n_qtiles = (Sq + tq - 1) / tq;
   if ((long long)B * Hkv * n_qtiles > 0x7fffffffLL) return LA_ERR_INVALID_ARG;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+  if (split_tiles != 0) {
+    if (split_tiles < 1 || !o_part || !lse_part || !aligned16(o_part)) return LA_ERR_INVALID_ARG;
+    // a query tile's key range holds at most ceil(S / 64) tiles of 64 keys
+    const long long need = ((S + 63) / 64 + split_tiles - 1) / split_tiles;
+    if (max_splits < need || max_splits > 65535) return LA_ERR_INVALID_ARG;
+    if ((long long)max_splits * B * Sq * Hq * D > (1LL << 46)) return LA_ERR_INVALID_ARG;
+  }
 
   la::PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -140,7 +149,14 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
     a.positions = positions;
     theta_revolutions(rope_base, D, a.theta_rev);
   }
-  return launched(la::launch_prefill(a, D, G, dt == LA_BF16 ? 0 : 1, stream));
+  a.split_tiles = split_tiles;
+  a.max_splits = split_tiles ? max_splits : 1;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  const int dti = dt == LA_BF16 ? 0 : 1;
+  const la_status st = launched(la::launch_prefill(a, D, G, dti, stream));
+  if (st != LA_OK || split_tiles == 0) return st;
+  return launched(la::launch_prefill_merge(a, D, dti, stream));
 }
 
 }  // namespace
@@ -175,6 +191,20 @@ la_status gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o
   if (!(rope_base >= 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
   return prefill_impl(q, k, v, o, lse, dt, B, Sq, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
                       o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base, stream);
+}
+
+la_status gqa_prefill_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                            la_dtype dt, int B, int Sq, int S, int Hq, int Hkv, int D,
+                            const int64_t q_strides[3], const int64_t k_strides[3],
+                            const int64_t v_strides[3], const int64_t o_strides[3],
+                            const int32_t* cu_docs, int n_docs, float softmax_scale,
+                            const int32_t* positions, double rope_base, int split_tiles,
+                            int max_splits, float* o_part, float* lse_part, hipStream_t stream) {
+  if (!(rope_base >= 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
+  if (split_tiles < 1) return LA_ERR_INVALID_ARG;
+  return prefill_impl(q, k, v, o, lse, dt, B, Sq, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
+                      o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base, stream,
+                      split_tiles, max_splits, o_part, lse_part);
 }
 
 la_status gqa_decode(const void* q, const int64_t q_strides[2], const void* k_cache,

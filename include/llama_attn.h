@@ -163,6 +163,33 @@ la_status gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o
                             const int32_t* positions, double rope_base, hipStream_t stream);
 
 /*
+ * gqa_prefill_split — gqa_prefill_chunk with long key ranges split across
+ * workgroups, for load balance when a few query tiles see far more keys than
+ * the others (a block deep in a long document) [P2, P4]. Same result as
+ * gqa_prefill_chunk up to rounding (the softmax is merged from pieces).
+ *
+ * Arguments as gqa_prefill_chunk (Sq = S gives a whole-sequence prefill),
+ * plus: the key range of each query tile (256/g tokens) is cut into pieces of
+ * split_tiles tiles of 64 keys, one workgroup per piece; a tile with one
+ * piece writes o and lse directly, the others write per-piece partials to the
+ * caller's workspace, which a second kernel (same stream) merges by their
+ * log-sum-exp weights into o and lse.
+ * o_part: fp32 [max_splits, B, Sq, Hq, D], lse_part: fp32 [max_splits, B, Hq,
+ *   Sq] (contiguous, caller-owned, 16-byte aligned; contents are scratch).
+ * Requirements: split_tiles >= 1; max_splits >= ceil(ceil(S / 64) /
+ *   split_tiles) and <= 65535.
+ * Errors: those of gqa_prefill_chunk; INVALID_ARG for split_tiles < 1, a null
+ * or misaligned workspace, max_splits out of range.
+ */
+la_status gqa_prefill_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                            la_dtype dt, int B, int Sq, int S, int Hq, int Hkv, int D,
+                            const int64_t q_strides[3], const int64_t k_strides[3],
+                            const int64_t v_strides[3], const int64_t o_strides[3],
+                            const int32_t* cu_docs, int n_docs, float softmax_scale,
+                            const int32_t* positions, double rope_base, int split_tiles,
+                            int max_splits, float* o_part, float* lse_part, hipStream_t stream);
+
+/*
  * gqa_decode — split-KV attention of one new token per sequence over its KV
  * cache; writes per-split partial results for gqa_decode_combine [P2].
  *

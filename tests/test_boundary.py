@@ -31,8 +31,8 @@ def lib():
 
 def test_header_declares_every_call():
     names = declared_functions()
-    for n in ("rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk", "gqa_decode",
-              "gqa_decode_combine", "la_status_str", "la_version"):
+    for n in ("rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk", "gqa_prefill_split",
+              "gqa_decode", "gqa_decode_combine", "la_status_str", "la_version"):
         assert n in names
 
 
@@ -114,6 +114,28 @@ def prefill_chunk(lib, base=0.0, **kw):
 ])
 def test_prefill_chunk_rejects(lib, kw, status):
     assert prefill_chunk(lib, **kw) == status
+
+
+def prefill_split(lib, base=0.0, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dt=0, B=1, Sq=4, S=1000, Hq=16, Hkv=1,
+                D=128, qs=S3, ks=S3, vs=S3, os_=S3, cu=None, nd=1, scale=0.0, st=4, ms=4, op=FAKE,
+                lp=FAKE)
+    args.update(kw)
+    return lib.gqa_prefill_split(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dt"],
+                                 args["B"], args["Sq"], args["S"], args["Hq"], args["Hkv"], args["D"],
+                                 args["qs"], args["ks"], args["vs"], args["os_"], args["cu"],
+                                 args["nd"], args["scale"], None, base, args["st"], args["ms"],
+                                 args["op"], args["lp"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(st=0), INVALID), (dict(st=-2), INVALID), (dict(ms=3), INVALID),   # 16 tiles / 4 -> 4 needed
+    (dict(ms=70000), INVALID), (dict(op=None), INVALID), (dict(lp=None), INVALID),
+    (dict(op=FAKE + 4), INVALID), (dict(Sq=1001), INVALID), (dict(base=-1.0), INVALID),
+    (dict(D=96), UNSUPPORTED), (dict(q=None), INVALID),
+])
+def test_prefill_split_rejects(lib, kw, status):
+    assert prefill_split(lib, **kw) == status
 
 
 def rope(lib, **kw):
