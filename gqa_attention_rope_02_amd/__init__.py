@@ -25,6 +25,11 @@ contiguous):
   tile's key range cut into pieces of split_tiles x 64 keys (workspace o_part fp32
   [max_splits,B,Sq,Hq,D], lse_part fp32 [max_splits,B,Hq,Sq]; ``prefill_split_workspace``
   allocates it).
+* ``gqa_prefill_ring_step(q, k, v, q_off, k_off, o_acc, lse_acc, first, cu_docs=None,
+  softmax_scale=0.0, positions=None, rope_base=0.0)``: queries [B,Sq,Hq,D] at positions
+  q_off.. against a key shard k/v [B,Skv,Hkv,D] at positions k_off..; writes (first) or
+  merges the shard's result into o_acc fp32 [B,Sq,Hq,D], lse_acc fp32 [B,Hq,Sq].
+* ``gqa_prefill_ring_finalize(o_acc, lse_acc, o, lse=None)``: o [B,Sq,Hq,D] from them.
 * ``gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk, o_part, lse_part,
   softmax_scale=0.0)``: q [B,Hq,D], caches [B,Hkv,Lmax,D], seq_lens int32 [B],
   o_part fp32 [B,Hq,max_splits,D], lse_part fp32 [B,Hq,max_splits].
@@ -39,7 +44,8 @@ import torch
 from . import _lib
 
 __all__ = ["LlamaAttnError", "rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk",
-           "gqa_prefill_split", "prefill_split_workspace", "gqa_decode",
+           "gqa_prefill_split", "prefill_split_workspace", "gqa_prefill_ring_step",
+           "gqa_prefill_ring_finalize", "gqa_decode",
            "gqa_decode_combine", "version", "LA_BF16", "LA_FP32"]
 
 LA_BF16, LA_FP32 = 0, 1
@@ -221,6 +227,43 @@ def gqa_prefill_split(q, k, v, o, split_tiles: int, o_part, lse_part, lse=None, 
         _i32(cu_docs), n_docs, float(softmax_scale), _i32(positions), float(rope_base),
         int(split_tiles), int(max_splits), _dev(o_part), _dev(lse_part), _stream())
     _check(st, "gqa_prefill_split")
+
+
+def gqa_prefill_ring_step(q, k, v, q_off: int, k_off: int, o_acc, lse_acc, first: bool,
+                          cu_docs=None, softmax_scale: float = 0.0, positions=None,
+                          rope_base: float = 0.0):
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    n_docs = cu_docs.shape[-1] - 1 if cu_docs is not None else 1
+    _same_shape("gqa_prefill_ring_step", (k, v))
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("gqa_prefill_ring_step: k/v must be [B, Skv, Hkv, D]")
+    if tuple(o_acc.shape) != (B, Sq, Hq, D) or tuple(lse_acc.shape) != (B, Hq, Sq) \
+            or o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32 \
+            or not o_acc.is_contiguous() or not lse_acc.is_contiguous():
+        raise ValueError("gqa_prefill_ring_step: accumulators must be contiguous fp32 "
+                         "[B, Sq, Hq, D] and [B, Hq, Sq]")
+    if cu_docs is not None and (cu_docs.dim() != 2 or cu_docs.shape[0] != B):
+        raise ValueError("gqa_prefill_ring_step: cu_docs must be [B, n_docs + 1]")
+    if positions is not None and tuple(positions.shape) != (B, Sq):
+        raise ValueError("gqa_prefill_ring_step: positions must be [B, Sq]")
+    st = _lib.load().gqa_prefill_ring_step(
+        _dev(q), _dev(k), _dev(v), _dev(o_acc), _dev(lse_acc), _dtype(q), B, Sq, int(q_off), Skv,
+        int(k_off), Hq, Hkv, D, _strides(q, 3), _strides(k, 3), _strides(v, 3), _i32(cu_docs),
+        n_docs, float(softmax_scale), _i32(positions), float(rope_base), int(bool(first)), _stream())
+    _check(st, "gqa_prefill_ring_step")
+
+
+def gqa_prefill_ring_finalize(o_acc, lse_acc, o, lse=None):
+    B, Sq, Hq, D = o.shape
+    if tuple(o_acc.shape) != (B, Sq, Hq, D) or tuple(lse_acc.shape) != (B, Hq, Sq):
+        raise ValueError("gqa_prefill_ring_finalize: inconsistent shapes")
+    if lse is not None and tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("gqa_prefill_ring_finalize: lse must be [B, Hq, Sq]")
+    st = _lib.load().gqa_prefill_ring_finalize(
+        _dev(o_acc), _dev(lse_acc), _dev(o), _strides(o, 3), _f32c(lse), _dtype(o), B, Sq, Hq, D,
+        _stream())
+    _check(st, "gqa_prefill_ring_finalize")
 
 
 def gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk: int, o_part, lse_part,

@@ -136,6 +136,9 @@ void prefill_kernel(PrefillArgs a) {
   // Token indices below are query rows; positions (masks, documents, the key
   // range) add qo.
   const int S = a.S, Sq = a.Sq, qo = a.q_off;
+  // keys: positions k_off .. kend-1 in rows 0 .. S-1 of k and v (k_off = 0
+  // except for a key shard of a context-parallel ring step)
+  const int k_off = a.k_off, kend = a.k_off + a.S;
   const int t0 = qtile * TQ;
   const int t_end = min(t0 + TQ, Sq);
   const int32_t* cu = a.cu_docs ? a.cu_docs + (int64_t)b * (a.n_docs + 1) : nullptr;
@@ -219,8 +222,28 @@ void prefill_kernel(PrefillArgs a) {
   }
   // clamp: out-of-contract offsets must not move the key range out of
   // [0, t0 + qo]
-  int kv_lo = max(0, min(kv_start, t0 + qo));
-  const int kv_hi = t_end - 1 + qo;
+  int kv_lo = max(k_off, max(0, min(kv_start, t0 + qo)));
+  const int kv_hi = min(kend - 1, t_end - 1 + qo);
+  if (kv_lo > kv_hi) {
+    // no key of this shard is visible to any of the tile's rows (ring step):
+    // the first step of an accumulation still starts the rows at o = 0,
+    // lse = -inf
+    if (a.acc_mode == 1) {
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) {
+        if (!valid[cb]) continue;
+        float* op = a.o_acc + (((int64_t)b * Sq + tok[cb]) * a.Hq + head[cb]) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq)
+            *reinterpret_cast<f32x4*>(op + db * 32 + 8 * jq + 4 * hi) = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (hi == 0) a.lse_acc[((int64_t)b * a.Hq + head[cb]) * Sq + tok[cb]] = -INFINITY;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the Q loads already issued
+    return;
+  }
   int n_tiles = (kv_hi - kv_lo) / kKT + 1;
 
   // Split key ranges (split_tiles > 0): workgroup (tile, split sp) takes the
@@ -271,11 +294,11 @@ void prefill_kernel(PrefillArgs a) {
   }
   auto stage = [&](int kt, char* dst) __attribute__((always_inline)) {
     if constexpr (std::is_same<T, __bf16>::value) {
-      const int64_t rows = max(S - kt, 0);   // rows past the sequence end read as zero
+      const int64_t rows = max(kend - kt, 0);   // rows past the last key read as zero
       const int kb_ = (int)min(rows * a.ks_s * 2, (int64_t)0x7fffffff);
       const int vb_ = (int)min(rows * a.vs_s * 2, (int64_t)0x7fffffff);
-      const void* kp = kbase + kt * a.ks_s;
-      const void* vp = vbase + kt * a.vs_s;
+      const void* kp = kbase + (int64_t)(kt - k_off) * a.ks_s;
+      const void* vp = vbase + (int64_t)(kt - k_off) * a.vs_s;
 #pragma unroll
       for (int n = 0; n < NL; ++n) {
         load_lds16(kp, kb_, koff[n], dst + (n * kNW + wave) * 1024);
@@ -286,9 +309,9 @@ void prefill_kernel(PrefillArgs a) {
         const int row = p / CH, ph = p % CH;
         const int j = kt + row;
         bf16x8 kv = zero_bf16x8(), vv = zero_bf16x8();
-        if (j < S) {
-          kv = load8(kbase + j * a.ks_s + 8 * k_chunk<CH>(ph, row));
-          vv = load8(vbase + j * a.vs_s + 8 * v_chunk<CH>(ph, row));
+        if (j < kend) {
+          kv = load8(kbase + (int64_t)(j - k_off) * a.ks_s + 8 * k_chunk<CH>(ph, row));
+          vv = load8(vbase + (int64_t)(j - k_off) * a.vs_s + 8 * v_chunk<CH>(ph, row));
         }
         *reinterpret_cast<bf16x8*>(dst + p * 16) = kv;
         *reinterpret_cast<bf16x8*>(dst + 4 * TILE + p * 16) = vv;
@@ -331,7 +354,7 @@ void prefill_kernel(PrefillArgs a) {
   auto stage_ptr = [&](int k) __attribute__((always_inline)) -> char* { return lds + (k & 3) * TILE; };
   // tiles past the last one are issued as loads that read nothing, so every
   // wave has the same number of loads in flight at every wait
-  auto issue = [&](int k) __attribute__((always_inline)) { stage(k < n_tiles ? kv_lo + k * kKT : S, stage_ptr(k)); };
+  auto issue = [&](int k) __attribute__((always_inline)) { stage(k < n_tiles ? kv_lo + k * kKT : kend, stage_ptr(k)); };
   auto barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(kLgkm0);   // this wave's LDS reads are done
     __builtin_amdgcn_s_barrier();
@@ -374,9 +397,11 @@ void prefill_kernel(PrefillArgs a) {
   };
   auto sm_tile = [&](int k) __attribute__((always_inline)) {
     const int kt = kv_lo + k * kKT;
-    if (!wave_all_valid || kt + kKT - 1 > w_tmin + qo || kt < w_smax) {
+    // (keys at or past kend, the end of the keys held, are masked too: a
+    // ring step's key shard can end before the rows' positions)
+    if (!wave_all_valid || kt + kKT - 1 > w_tmin + qo || kt < w_smax || kt + kKT > kend) {
       const int lo = valid[0] ? st[0] - kt : kKT;
-      const int hi_ = valid[0] ? tok[0] + qo - kt : -1;
+      const int hi_ = valid[0] ? min(tok[0] + qo, kend - 1) - kt : -1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -442,7 +467,7 @@ void prefill_kernel(PrefillArgs a) {
   // vmcnt waits before the barriers order each stage's loads before its reads.
   auto x_phase = [&](char* __restrict__ dst, int kd, const char* __restrict__ lv,
                      const char* __restrict__ lk, int k) __attribute__((always_inline)) {
-    if (dst) stage(kd < n_tiles ? kv_lo + kd * kKT : S, dst);
+    if (dst) stage(kd < n_tiles ? kv_lo + kd * kKT : kend, dst);
     __builtin_amdgcn_s_setprio(1);
     // one block of 32 MFMAs and their 48 operand reads (after the last tile
     // the QK of the stage beyond it is computed and dropped): keep eight reads
@@ -577,7 +602,7 @@ void prefill_kernel(PrefillArgs a) {
     barrier();                                       // end of phase 1
     auto step = [&](auto U, int k) __attribute__((always_inline)) {
       constexpr int u = decltype(U)::value;
-      stage(k + 3 < n_tiles ? kv_lo + (k + 3) * kKT : S, lds + ((u + 3) & 3) * TILE);
+      stage(k + 3 < n_tiles ? kv_lo + (k + 3) * kKT : kend, lds + ((u + 3) & 3) * TILE);
       sm_tile(k);
       barrier();                                     // end of phase 2k+2
       x_phase(nullptr, 0, lds + u * TILE, lds + ((u + 1) & 3) * TILE, k);
@@ -616,6 +641,47 @@ void prefill_kernel(PrefillArgs a) {
   auto row_lse = [&](int cb) __attribute__((always_inline)) {
     return lt[cb] > 0.f ? m[cb] * a.scale + fast_log2(lt[cb]) * kLn2 : -INFINITY;
   };
+  if (a.acc_mode) {
+    // ring step: this shard's (o, lse) of every row, written (first step) or
+    // merged by log-sum-exp weight into the fp32 accumulators (o_acc, lse_acc);
+    // a workgroup owns its rows, so the read-merge-write needs no atomics
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      if (!valid[cb]) continue;
+      float* op = a.o_acc + (((int64_t)b * Sq + tok[cb]) * a.Hq + head[cb]) * D;
+      float* lp = a.lse_acc + ((int64_t)b * a.Hq + head[cb]) * Sq + tok[cb];
+      const float ln = row_lse(cb);
+      float wo = 0.f, wn = 1.f, rw = 1.f, lout = ln;
+      if (a.acc_mode == 2) {
+        const float lo_ = *lp;
+        const float mx = fmaxf(lo_, ln);
+        if (mx > -INFINITY) {
+          wo = __expf(lo_ - mx);
+          wn = __expf(ln - mx);
+          rw = 1.f / (wo + wn);
+          lout = mx + __logf(wo + wn);
+        } else {
+          wo = 1.f;   // nothing seen yet on either side: o stays 0
+          wn = 0.f;
+          lout = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          f32x4* dst = reinterpret_cast<f32x4*>(op + db * 32 + 8 * jq + 4 * hi);
+          f32x4 v = {quot(acc[db][cb][4 * jq], cb), quot(acc[db][cb][4 * jq + 1], cb),
+                     quot(acc[db][cb][4 * jq + 2], cb), quot(acc[db][cb][4 * jq + 3], cb)};
+          if (a.acc_mode == 2) v = (wo * (*dst) + wn * v) * rw;
+          *dst = v;
+        }
+      __builtin_amdgcn_s_waitcnt(0);   // both halves of the row have read lse before it changes
+      __builtin_amdgcn_wave_barrier();
+      if (hi == 0) *lp = lout;
+    }
+    return;
+  }
   if (n_split > 1) {
     // partial result of this split: fp32 o (normalised by its own row sum)
     // and lse, slot sp

@@ -50,6 +50,12 @@ struct PrefillArgs {
   int split_tiles, max_splits;
   float* o_part;
   float* lse_part;
+  // context-parallel ring step: keys at positions k_off .. k_off + S - 1;
+  // acc_mode 1 writes, 2 merges this shard's (o, lse) into the fp32
+  // accumulators o_acc [B, Sq, Hq, D] and lse_acc [B, Hq, Sq]
+  int k_off, acc_mode;
+  float* o_acc;
+  float* lse_acc;
 };
 
 struct DecodeArgs {

@@ -102,18 +102,25 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
                        const int32_t* cu_docs, int n_docs, float softmax_scale,
                        const int32_t* positions, double rope_base, hipStream_t stream,
                        int split_tiles = 0, int max_splits = 0, float* o_part = nullptr,
-                       float* lse_part = nullptr) {
+                       float* lse_part = nullptr, bool ring = false, int q_off = 0, int k_off = 0,
+                       int acc_mode = 0, float* o_acc = nullptr, float* lse_acc = nullptr) {
   if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
-  if (!q || !k || !v || !o) return LA_ERR_INVALID_ARG;
+  if (!q || !k || !v || (!o && !ring)) return LA_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return LA_ERR_INVALID_ARG;
-  if (Sq < 1 || Sq > S) return LA_ERR_INVALID_ARG;
+  if (Sq < 1 || (!ring && Sq > S)) return LA_ERR_INVALID_ARG;
+  if (ring) {
+    if (q_off < 0 || k_off < 0 || (long long)q_off + Sq > 0x7fffffffLL ||
+        (long long)k_off + S > 0x7fffffffLL)
+      return LA_ERR_INVALID_ARG;
+    if (!o_acc || !lse_acc || !aligned16(o_acc)) return LA_ERR_INVALID_ARG;
+  }
   if (cu_docs && n_docs < 1) return LA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return LA_ERR_INVALID_ARG;
   if (!supported_d(D) || !supported_g(Hq / Hkv)) return LA_ERR_UNSUPPORTED;
   const int es = elem_size(dt);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (!ring && !aligned16(o))) return LA_ERR_INVALID_ARG;
   if (!strides_ok(q_strides, 3, es) || !strides_ok(k_strides, 3, es) ||
-      !strides_ok(v_strides, 3, es) || !strides_ok(o_strides, 3, es))
+      !strides_ok(v_strides, 3, es) || (!ring && !strides_ok(o_strides, 3, es)))
     return LA_ERR_INVALID_ARG;
   // key/value rows of consecutive tokens may not overlap (tiles are fetched
   // with a byte range that ends at the last token's row)
@@ -137,10 +144,16 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
   a.qs_b = q_strides[0]; a.qs_s = q_strides[1]; a.qs_h = q_strides[2];
   a.ks_b = k_strides[0]; a.ks_s = k_strides[1]; a.ks_h = k_strides[2];
   a.vs_b = v_strides[0]; a.vs_s = v_strides[1]; a.vs_h = v_strides[2];
-  a.os_b = o_strides[0]; a.os_s = o_strides[1]; a.os_h = o_strides[2];
+  if (!ring) {
+    a.os_b = o_strides[0]; a.os_s = o_strides[1]; a.os_h = o_strides[2];
+  }
   a.cu_docs = cu_docs; a.n_docs = cu_docs ? n_docs : 1;
   a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv;
-  a.Sq = Sq; a.q_off = S - Sq;
+  a.Sq = Sq; a.q_off = ring ? q_off : S - Sq;
+  a.k_off = ring ? k_off : 0;
+  a.acc_mode = ring ? acc_mode : 0;
+  a.o_acc = o_acc;
+  a.lse_acc = lse_acc;
   a.n_qtiles = (int)n_qtiles;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -205,6 +218,40 @@ la_status gqa_prefill_split(const void* q, const void* k, const void* v, void* o
   return prefill_impl(q, k, v, o, lse, dt, B, Sq, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
                       o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base, stream,
                       split_tiles, max_splits, o_part, lse_part);
+}
+
+la_status gqa_prefill_ring_step(const void* q, const void* k, const void* v, float* o_acc,
+                                float* lse_acc, la_dtype dt, int B, int Sq, int q_off, int Skv,
+                                int k_off, int Hq, int Hkv, int D, const int64_t q_strides[3],
+                                const int64_t k_strides[3], const int64_t v_strides[3],
+                                const int32_t* cu_docs, int n_docs, float softmax_scale,
+                                const int32_t* positions, double rope_base, int first,
+                                hipStream_t stream) {
+  if (!(rope_base >= 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
+  return prefill_impl(q, k, v, nullptr, nullptr, dt, B, Sq, Skv, Hq, Hkv, D, q_strides, k_strides,
+                      v_strides, nullptr, cu_docs, n_docs, softmax_scale, positions, rope_base,
+                      stream, 0, 0, nullptr, nullptr, true, q_off, k_off, first ? 1 : 2, o_acc,
+                      lse_acc);
+}
+
+la_status gqa_prefill_ring_finalize(const float* o_acc, const float* lse_acc, void* o,
+                                    const int64_t o_strides[3], float* lse, la_dtype dt, int B,
+                                    int Sq, int Hq, int D, hipStream_t stream) {
+  if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
+  if (!o_acc || !lse_acc || !o) return LA_ERR_INVALID_ARG;
+  if (B < 1 || Sq < 1 || Hq < 1) return LA_ERR_INVALID_ARG;
+  if (!supported_d(D)) return LA_ERR_UNSUPPORTED;
+  if (!aligned16(o_acc) || !aligned16(o) || !strides_ok(o_strides, 3, elem_size(dt)))
+    return LA_ERR_INVALID_ARG;
+  la::PrefillArgs a{};
+  a.o = o; a.lse = lse;
+  a.os_b = o_strides[0]; a.os_s = o_strides[1]; a.os_h = o_strides[2];
+  a.B = B; a.Sq = Sq; a.Hq = Hq;
+  // the accumulators are the merge's single slot
+  a.max_splits = 1;
+  a.o_part = const_cast<float*>(o_acc);
+  a.lse_part = const_cast<float*>(lse_acc);
+  return launched(la::launch_prefill_merge(a, D, dt == LA_BF16 ? 0 : 1, stream));
 }
 
 la_status gqa_decode(const void* q, const int64_t q_strides[2], const void* k_cache,

@@ -190,6 +190,49 @@ la_status gqa_prefill_split(const void* q, const void* k, const void* v, void* o
                             int max_splits, float* o_part, float* lse_part, hipStream_t stream);
 
 /*
+ * gqa_prefill_ring_step — one step of context-parallel attention, as each
+ * device of a ring runs it (here on one GPU): the Sq query rows at positions
+ * q_off .. q_off + Sq - 1 against the Skv keys and values of one shard of the
+ * same sequence, at positions k_off .. k_off + Skv - 1, with the causal and
+ * document rules on those positions ([P1] "4D Parallelism": context
+ * parallelism over the 128K sequence; [P2, P4] for the attention itself).
+ * The shard's result for each row and head (softmax over the shard's visible
+ * keys, and its log-sum-exp; o = 0 and lse = -inf where it has none) is
+ * written (first != 0) or merged by log-sum-exp weight into the fp32
+ * accumulators, so that after the steps over all shards they hold the
+ * attention over all keys; gqa_prefill_ring_finalize turns them into o.
+ *
+ * q: [B, Sq, Hq, D] (rows of the query shard); k, v: [B, Skv, Hkv, D] (rows
+ *   of the key shard, keys rotated at their positions); strides as in
+ *   gqa_prefill. cu_docs: as in gqa_prefill, over the whole sequence's
+ *   positions (it must cover every position of both shards).
+ * o_acc: fp32 [B, Sq, Hq, D], lse_acc: fp32 [B, Hq, Sq] (contiguous,
+ *   caller-owned); their contents are read only when first == 0.
+ * rope_base: 0 means the queries arrive rotated; > 0 rotates them in the
+ *   kernel at positions (int32 [B, Sq], or NULL for q_off + i).
+ * Errors: those of gqa_prefill; INVALID_ARG for q_off, k_off < 0, Sq or
+ * Skv < 1, position overflow, null or misaligned accumulators.
+ */
+la_status gqa_prefill_ring_step(const void* q, const void* k, const void* v, float* o_acc,
+                                float* lse_acc, la_dtype dt, int B, int Sq, int q_off, int Skv,
+                                int k_off, int Hq, int Hkv, int D, const int64_t q_strides[3],
+                                const int64_t k_strides[3], const int64_t v_strides[3],
+                                const int32_t* cu_docs, int n_docs, float softmax_scale,
+                                const int32_t* positions, double rope_base, int first,
+                                hipStream_t stream);
+
+/*
+ * gqa_prefill_ring_finalize — o (type dt, [B, Sq, Hq, D], strides o_strides)
+ * and optional lse (fp32 [B, Hq, Sq]) from the ring accumulators; a row that
+ * saw no key gets o = 0 and lse = -inf.
+ * Errors: INVALID_ARG for null or misaligned pointers, sizes < 1, bad strides;
+ * UNSUPPORTED for D not in {64, 128} or an unknown dtype.
+ */
+la_status gqa_prefill_ring_finalize(const float* o_acc, const float* lse_acc, void* o,
+                                    const int64_t o_strides[3], float* lse, la_dtype dt, int B,
+                                    int Sq, int Hq, int D, hipStream_t stream);
+
+/*
  * gqa_decode — split-KV attention of one new token per sequence over its KV
  * cache; writes per-split partial results for gqa_decode_combine [P2].
  *

@@ -32,7 +32,8 @@ def lib():
 def test_header_declares_every_call():
     names = declared_functions()
     for n in ("rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk", "gqa_prefill_split",
-              "gqa_decode", "gqa_decode_combine", "la_status_str", "la_version"):
+              "gqa_prefill_ring_step", "gqa_prefill_ring_finalize", "gqa_decode", "gqa_decode_combine",
+              "la_status_str", "la_version"):
         assert n in names
 
 
@@ -136,6 +137,39 @@ def prefill_split(lib, base=0.0, **kw):
 ])
 def test_prefill_split_rejects(lib, kw, status):
     assert prefill_split(lib, **kw) == status
+
+
+def ring_step(lib, base=0.0, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, oa=FAKE, la=FAKE, dt=0, B=1, Sq=64, qo=128, Skv=64, ko=0,
+                Hq=16, Hkv=1, D=128, qs=S3, ks=S3, vs=S3, cu=None, nd=1, scale=0.0, first=1)
+    args.update(kw)
+    return lib.gqa_prefill_ring_step(args["q"], args["k"], args["v"], args["oa"], args["la"], args["dt"],
+                                     args["B"], args["Sq"], args["qo"], args["Skv"], args["ko"],
+                                     args["Hq"], args["Hkv"], args["D"], args["qs"], args["ks"],
+                                     args["vs"], args["cu"], args["nd"], args["scale"], None, base,
+                                     args["first"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Sq=0), INVALID), (dict(Skv=0), INVALID), (dict(qo=-1), INVALID), (dict(ko=-5), INVALID),
+    (dict(qo=0x7fffffff), INVALID), (dict(oa=None), INVALID), (dict(la=None), INVALID),
+    (dict(oa=FAKE + 4), INVALID), (dict(base=-1.0), INVALID), (dict(D=96), UNSUPPORTED),
+    (dict(Hq=12, Hkv=8), INVALID), (dict(ks=S3_BAD), INVALID), (dict(k=None), INVALID),
+])
+def test_ring_step_rejects(lib, kw, status):
+    assert ring_step(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(oa=None), INVALID), (dict(o=None), INVALID), (dict(Sq=0), INVALID), (dict(D=80), UNSUPPORTED),
+    (dict(dt=5), UNSUPPORTED), (dict(os_=S3_BAD), INVALID), (dict(o=FAKE + 2), INVALID),
+])
+def test_ring_finalize_rejects(lib, kw, status):
+    args = dict(oa=FAKE, la=FAKE, o=FAKE, os_=S3, lse=None, dt=0, B=1, Sq=8, Hq=4, D=128)
+    args.update(kw)
+    assert lib.gqa_prefill_ring_finalize(args["oa"], args["la"], args["o"], args["os_"], args["lse"],
+                                         args["dt"], args["B"], args["Sq"], args["Hq"], args["D"],
+                                         None) == status
 
 
 def rope(lib, **kw):

@@ -1,0 +1,146 @@
+"""gqa_prefill_ring_step / gqa_prefill_ring_finalize on the GPU: a sequence
+cut into shards, every query shard run against every key shard in ring order
+with its partials merged, gives the whole sequence's attention (oracle); the
+single-shard case equals gqa_prefill bit for bit; shards no row may see leave
+the accumulators as they were; exact document probe across shards."""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_helpers as H
+from oracle import reference as orc
+from workloads import draw_cu_docs, draw_prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+BASE = 500000.0
+
+
+def _dev(x):
+    return x.to(torch.device("cuda"))
+
+
+def _cu(cu, B=1):
+    return None if cu is None else _dev(torch.as_tensor(np.asarray(cu), dtype=torch.int32).reshape(B, -1))
+
+
+def _ring(q, kr, v, cu, bounds, rope_base):
+    """Every query shard against every key shard (ring order starting at its
+    own shard), then finalize; q, kr, v are the whole sequence on the device,
+    bounds the shard edges. Returns O, LSE of the whole sequence on the CPU."""
+    import gqa_attention_rope_02_amd as la
+    B, S, Hq, D = q.shape
+    O = torch.full_like(q, float("nan"))
+    L = torch.full((B, Hq, S), float("nan"), dtype=torch.float32, device=q.device)
+    P = len(bounds) - 1
+    cud = _cu(cu, B)
+    for i in range(P):
+        q0, q1 = bounds[i], bounds[i + 1]
+        Sq = q1 - q0
+        oa = torch.full((B, Sq, Hq, D), float("nan"), dtype=torch.float32, device=q.device)
+        lsa = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=q.device)
+        for step in range(P):
+            j = (i - step) % P
+            k0, k1 = bounds[j], bounds[j + 1]
+            la.gqa_prefill_ring_step(q[:, q0:q1], kr[:, k0:k1], v[:, k0:k1], q0, k0, oa, lsa,
+                                     first=(step == 0), cu_docs=cud, rope_base=rope_base)
+        o_blk = torch.empty(B, Sq, Hq, D, dtype=q.dtype, device=q.device)
+        l_blk = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
+        la.gqa_prefill_ring_finalize(oa, lsa, o_blk, l_blk)
+        O[:, q0:q1] = o_blk
+        L[:, :, q0:q1] = l_blk
+    torch.cuda.synchronize()
+    return O.cpu(), L.cpu()
+
+
+def _rot(x):
+    import gqa_attention_rope_02_amd as la
+    xd = _dev(x)
+    xr = torch.full_like(xd, float("nan"))
+    la.rope_qk(None, None, xd, xr, rope_base=BASE)
+    return xr
+
+
+@pytest.mark.parametrize("S,bounds,Hq,Hkv,D,dtype,seed,nd,fused", [
+    (512, [0, 128, 256, 384, 512], 32, 8, 128, "bf16", 101, 3, True),    # 4 equal shards
+    (700, [0, 250, 450, 700], 16, 1, 128, "bf16", 102, 4, True),         # 3 ragged shards, g=16
+    (600, [0, 100, 333, 600], 8, 8, 64, "bf16", 103, 2, False),          # g=1, D=64, rotated q
+    (400, [0, 200, 400], 32, 2, 128, "fp32", 104, 2, True),              # fp32 inputs
+])
+def test_ring_matches_oracle(S, bounds, Hq, Hkv, D, dtype, seed, nd, fused):
+    import gqa_attention_rope_02_amd as la
+    H.say("ring", dict(S=S, bounds=bounds, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, seed=seed))
+    q, k, v = draw_prefill_inputs(1, S, Hq, Hkv, D, dtype, seed)
+    cu = draw_cu_docs(S, seed, nd, 1)
+    kr = _rot(k)
+    if fused:
+        qd, rb = _dev(q), BASE
+    else:
+        qd = torch.empty_like(_dev(q))
+        la.rope_qk(_dev(q), qd, None, None, rope_base=BASE)
+        rb = 0.0
+    O, L = _ring(qd, kr, _dev(v), cu, bounds, rb)
+    Ow, Lw = orc.rope_attention(q, k, v, cu, BASE)
+    H.assert_close(O, Ow)
+    H.assert_close(L, Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+
+
+def test_ring_single_shard_equals_gqa_prefill():
+    """One shard holding every key: the step writes the fp32 result and the
+    finalize rounds it once, exactly as gqa_prefill's own epilogue does."""
+    import gqa_attention_rope_02_amd as la
+    S, Hq, Hkv, D = 640, 32, 8, 128
+    H.say("ring single shard")
+    q, k, v = draw_prefill_inputs(1, S, Hq, Hkv, D, "bf16", 105)
+    cu = draw_cu_docs(S, 105, 3, 1)
+    qd, kd, vd = _dev(q), _dev(k), _dev(v)
+    qr, kr = torch.empty_like(qd), torch.empty_like(kd)
+    la.rope_qk(qd, qr, kd, kr)
+    o = torch.empty_like(qd)
+    lse = torch.empty(1, Hq, S, dtype=torch.float32, device=qd.device)
+    la.gqa_prefill(qr, kr, vd, o, lse, _cu(cu))
+    O, L = _ring(qr, kr, vd, cu, [0, S], 0.0)
+    assert torch.equal(O, o.cpu()) and torch.equal(L, lse.cpu())
+
+
+def test_ring_step_with_an_unseen_shard_changes_nothing():
+    """Keys that lie after every query of the shard: the first step leaves
+    o = 0, lse = -inf; a merging step leaves the accumulators bit for bit."""
+    import gqa_attention_rope_02_amd as la
+    S, Hq, Hkv, D = 512, 16, 2, 128
+    H.say("ring unseen shard")
+    q, k, v = draw_prefill_inputs(1, S, Hq, Hkv, D, "bf16", 106)
+    qd, kr, vd = _dev(q), _rot(k), _dev(v)
+    oa = torch.full((1, 256, Hq, D), float("nan"), dtype=torch.float32, device=qd.device)
+    lsa = torch.full((1, Hq, 256), float("nan"), dtype=torch.float32, device=qd.device)
+    la.gqa_prefill_ring_step(qd[:, :256], kr[:, 256:], vd[:, 256:], 0, 256, oa, lsa, first=True,
+                             rope_base=BASE)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, torch.zeros_like(oa)) and bool(torch.isneginf(lsa).all())
+    la.gqa_prefill_ring_step(qd[:, :256], kr[:, :256], vd[:, :256], 0, 0, oa, lsa, first=False,
+                             rope_base=BASE)
+    o1, l1 = oa.clone(), lsa.clone()
+    la.gqa_prefill_ring_step(qd[:, :256], kr[:, 256:], vd[:, 256:], 0, 256, oa, lsa, first=False,
+                             rope_base=BASE)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, o1) and torch.equal(lsa, l1)
+
+
+def test_ring_document_probe_is_exact():
+    """q = 0, a V channel holding each key's document index and documents
+    that cross the shard edges: each row's merged channel is its document
+    index and exp(LSE) its count of visible keys, exactly."""
+    B, S, Hq, Hkv, D = 1, 480, 32, 8, 128
+    H.say("ring document probe")
+    cu = np.array([0, 90, 91, 300, S], dtype=np.int32)
+    doc = orc.document_of(cu, S)
+    q = torch.zeros(B, S, Hq, D, dtype=torch.bfloat16)
+    k = torch.randn(B, S, Hkv, D, generator=torch.Generator().manual_seed(107)).to(torch.bfloat16)
+    v = torch.zeros(B, S, Hkv, D, dtype=torch.bfloat16)
+    v[0, :, :, 3] = torch.as_tensor(doc, dtype=torch.bfloat16)[:, None]
+    O, L = _ring(_dev(q), _dev(k), _dev(v), cu, [0, 120, 240, 360, 480], 0.0)
+    rows = np.arange(S)
+    assert np.array_equal(O[0, :, :, 3].float().numpy(), np.broadcast_to(doc[:, None], (S, Hq)).astype(np.float32))
+    count = rows - cu[doc] + 1
+    assert np.array_equal(np.rint(np.exp(L[0].double().numpy())), np.broadcast_to(count, (Hq, S)))
