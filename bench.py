@@ -200,6 +200,43 @@ def time_chunk(st, Sq: int, steps: int, warmup: int, settle_s: float = 0.0, spli
                 gpu_ms_per_step=float(np.mean([e[0].elapsed_time(e[2]) for e in evs])))
 
 
+def time_ring(st, P: int, reps: int):
+    """Context-parallel attention as P devices of a ring would run it, all on
+    this GPU: the sequence in P equal shards; every query shard against every
+    key shard (its own first, then the ring order), partials merged into fp32
+    accumulators, then finalized. Queries rotated in the kernel, keys rotated
+    once beforehand (outside the timed region). Returns ms per whole ring."""
+    import torch
+    import gqa_attention_rope_02_amd as la
+    w = st["w"]
+    S, dev = w.S, st["q"].device
+    L = S // P
+    la.rope_qk(None, None, st["k"], st["kr"])
+    oa = torch.empty(w.B, L, w.Hq, w.D, dtype=torch.float32, device=dev)
+    lsa = torch.empty(w.B, w.Hq, L, dtype=torch.float32, device=dev)
+    lse_blk = torch.empty(w.B, w.Hq, L, dtype=torch.float32, device=dev)
+
+    def ring():
+        for i in range(P):
+            q0 = i * L
+            for step in range(P):
+                j = (i - step) % P
+                la.gqa_prefill_ring_step(st["q"][:, q0:q0 + L], st["kr"][:, j * L:(j + 1) * L],
+                                         st["v"][:, j * L:(j + 1) * L], q0, j * L, oa, lsa,
+                                         first=(step == 0), cu_docs=st["cu_d"], rope_base=w.rope_base)
+            la.gqa_prefill_ring_finalize(oa, lsa, st["o"][:, q0:q0 + L], lse_blk)
+
+    ring()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ring()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 # ---------------------------------------------------------------------- decode
 
 def setup_decode():
@@ -414,6 +451,14 @@ def main():
             "frac_kernel": round(fl3 / (t3["prefill_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "ms_per_step": round(t3["gpu_ms_per_step"], 4), "prefill_ms": round(t3["prefill_ms"], 4),
             "rope_ms": round(t3["rope_ms"], 4), "traffic": measured_traffic("gqa_prefill", "llama405b", phash)}
+        P = 8
+        tr = time_ring(st3, P, 2)
+        out["ring_405b"] = {
+            "workload": f"405b-shape context-parallel attention, S=32768 in {P} shards of {32768 // P}: "
+                        f"all {P * P} ring steps (gqa_prefill_ring_step) and {P} finalizes on one GPU",
+            "tflops": round(fl3 / (tr * 1e-3) / 1e12, 2),
+            "frac": round(fl3 / (tr * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "ms_per_ring": round(tr, 3)}
         if not run_8b:
             out.update(value=out["prefill_405b"]["tflops_path"], unit="TFLOP/s",
                        ms_per_step=out["prefill_405b"]["ms_per_step"],
