@@ -49,9 +49,13 @@ def rope_frequencies(D: int, base: float = 500000.0) -> np.ndarray:
     return np.power(np.float64(base), -2.0 * k / np.float64(D))
 
 
-def rope(x, positions, base: float = 500000.0) -> np.ndarray:
-    """Rotate channel pairs (2k, 2k+1) of x [..., S, H, D] by positions * theta_k.
+def rope(x, positions, base: float = 500000.0, pairing: str = "adjacent") -> np.ndarray:
+    """Rotate channel pairs of x [..., S, H, D] by positions * theta_k.
 
+    Pair k is channels (2k, 2k+1) ("adjacent", RoFormer's layout, which the
+    pages cite) or channels (k, k + D/2) ("half": the pages do not fix the
+    layout, and this is the other one in common use); either way the first
+    channel of the pair becomes x0 cos - x1 sin and the second x0 sin + x1 cos.
     ``positions`` has the shape of x's leading dims up to S (e.g. [B, S]);
     returns fp64 of x's shape.
     """
@@ -61,10 +65,16 @@ def rope(x, positions, base: float = 500000.0) -> np.ndarray:
     angle = pos[..., None] * rope_frequencies(D, base)        # [..., S, D/2]
     c = np.cos(angle)[..., None, :]                            # broadcast over H
     s = np.sin(angle)[..., None, :]
-    even, odd = x[..., 0::2], x[..., 1::2]
+    if pairing == "adjacent":
+        first, second = np.s_[..., 0::2], np.s_[..., 1::2]
+    elif pairing == "half":
+        first, second = np.s_[..., :D // 2], np.s_[..., D // 2:]
+    else:
+        raise ValueError(f"unknown pairing {pairing!r}")
+    x0, x1 = x[first], x[second]
     out = np.empty_like(x)
-    out[..., 0::2] = even * c - odd * s
-    out[..., 1::2] = even * s + odd * c
+    out[first] = x0 * c - x1 * s
+    out[second] = x0 * s + x1 * c
     return out
 
 
@@ -118,14 +128,15 @@ def attention(qr, kr, v, cu_docs=None, scale: Optional[float] = None,
 
 
 def rope_attention(q, k, v, cu_docs=None, base: float = 500000.0, positions=None,
-                   scale: Optional[float] = None, rows=None) -> Tuple[np.ndarray, np.ndarray]:
+                   scale: Optional[float] = None, rows=None,
+                   pairing: str = "adjacent") -> Tuple[np.ndarray, np.ndarray]:
     """The whole prefill path: RoPE on Q and K at ``positions`` (default: the
     token index), then masked GQA attention. Shapes as in ``attention``."""
     q = _f64(q)
     B, S = q.shape[:2]
     if positions is None:
         positions = np.broadcast_to(np.arange(S), (B, S))
-    return attention(rope(q, positions, base), rope(k, positions, base), v,
+    return attention(rope(q, positions, base, pairing), rope(k, positions, base, pairing), v,
                      cu_docs, scale, rows)
 
 

@@ -47,7 +47,7 @@ def _attention_variant(kv_map=None, strict=False, leak=False, scale_one=False, l
     return attention
 
 
-def _rope_half_split(x, positions, base=500000.0):
+def _rope_half_split(x, positions, base=500000.0, pairing="adjacent"):
     x = orc._f64(x)
     D = x.shape[-1]
     ang = np.asarray(positions, dtype=np.float64)[..., None] * orc.rope_frequencies(D, base)
@@ -56,8 +56,17 @@ def _rope_half_split(x, positions, base=500000.0):
     return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
 
 
-def _rope_wrong_sign(x, positions, base=500000.0):
-    return _real_rope(x, -np.asarray(positions), base)
+def _rope_wrong_sign(x, positions, base=500000.0, pairing="adjacent"):
+    return _real_rope(x, -np.asarray(positions), base, pairing)
+
+
+def _rope_half_backwards(x, positions, base=500000.0, pairing="adjacent"):
+    p = -np.asarray(positions) if pairing == "half" else positions
+    return _real_rope(x, p, base, pairing)
+
+
+def _rope_half_is_adjacent(x, positions, base=500000.0, pairing="adjacent"):
+    return _real_rope(x, positions, base, "adjacent")
 
 
 MUTATIONS = {
@@ -68,6 +77,8 @@ MUTATIONS = {
     "LSE without the max": ("attention", _attention_variant(lse_no_max=True)),
     "RoPE half-split pairs": ("rope", _rope_half_split),
     "RoPE rotates backwards": ("rope", _rope_wrong_sign),
+    "half-split RoPE rotates backwards": ("rope", _rope_half_backwards),
+    "half-split RoPE pairs adjacent channels": ("rope", _rope_half_is_adjacent),
     "theta uses k/D": ("rope_frequencies", lambda D, base=500000.0: _real_freq(2 * D, base)),
     "theta uses d_model": ("rope_frequencies", lambda D, base=500000.0: _real_freq(128 * D, base)),
 }
@@ -84,6 +95,9 @@ PIN_CALLS = [
     pins.test_zero_query_gives_mean_of_visible_values_and_log_count,
     pins.test_first_token_of_each_document_returns_its_value_row,
     pins.test_two_key_document_is_a_logistic_mix,
+    pins.test_rope_half_pairing_is_adjacent_pairing_under_a_channel_permutation,
+    pins.test_rope_half_unit_vector,
+    pins.test_attention_with_half_pairing_equals_permuted_adjacent,
 ]
 
 

@@ -162,6 +162,60 @@ def test_rope_unit_vectors_show_pairing_and_direction():
             np.testing.assert_allclose(r, want, rtol=0, atol=1e-15)
 
 
+def _to_adjacent(x):
+    """Channel permutation taking the half-split layout to the adjacent one:
+    half channel k goes to 2k and half channel k + D/2 to 2k + 1."""
+    x = np.asarray(x)
+    D = x.shape[-1]
+    out = np.empty_like(x)
+    out[..., 0::2], out[..., 1::2] = x[..., :D // 2], x[..., D // 2:]
+    return out
+
+
+def test_rope_half_pairing_is_adjacent_pairing_under_a_channel_permutation():
+    """Both layouts rotate the same pairs by the same angles; only where the
+    pair's channels sit differs. So rotating in the half layout equals moving
+    the channels to the adjacent layout, rotating there, and moving back."""
+    x = torch.randn(2, 6, 3, 16, generator=torch.Generator().manual_seed(11), dtype=torch.float64).numpy()
+    pos = np.array([[0, 1, 7, 1000, 65536, 131071], [3, 4, 5, 6, 7, 8]])
+    half = orc.rope(x, pos, 500000.0, "half")
+    adj = orc.rope(_to_adjacent(x), pos, 500000.0, "adjacent")
+    np.testing.assert_array_equal(_to_adjacent(half), adj)
+    assert np.array_equal(orc.rope(x, np.zeros((2, 6)), 500000.0, "half"), x)
+    with pytest.raises(ValueError):
+        orc.rope(x, pos, 500000.0, "interleaved")
+
+
+def test_rope_half_unit_vector():
+    """e_k (k < D/2) at position m goes to cos m theta_k in channel k and
+    sin m theta_k in channel k + D/2; e_{k+D/2} to (-sin, cos) there."""
+    D, m = 8, 5
+    th = orc.rope_frequencies(D, 500000.0)
+    for kk in range(D // 2):
+        c, s = math.cos(m * th[kk]), math.sin(m * th[kk])
+        for which, want_pair in ((0, (c, s)), (1, (-s, c))):
+            x = np.zeros((1, 1, 1, D))
+            x[..., kk + which * D // 2] = 1.0
+            r = orc.rope(x, np.array([[m]]), 500000.0, "half")[0, 0, 0]
+            want = np.zeros(D)
+            want[kk], want[kk + D // 2] = want_pair
+            np.testing.assert_allclose(r, want, rtol=0, atol=1e-15)
+
+
+def test_attention_with_half_pairing_equals_permuted_adjacent():
+    """Scores are dot products, unchanged when q and k get the same channel
+    permutation: half-pairing attention on (q, k) equals adjacent-pairing
+    attention on the permuted (q, k), and the pairings differ in general."""
+    q, k, v = _tiny(12, 1, 24, 4, 2, 16, "fp32")
+    cu = np.array([0, 9, 24])
+    Oh, Lh = orc.rope_attention(q, k, v, cu, 500000.0, pairing="half")
+    Oa, La = orc.rope_attention(_to_adjacent(q.numpy()), _to_adjacent(k.numpy()), v, cu, 500000.0)
+    np.testing.assert_allclose(Oh, Oa, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(Lh, La, rtol=0, atol=1e-12)
+    Ox, _ = orc.rope_attention(q, k, v, cu, 500000.0)
+    assert np.abs(Ox - Oh).max() > 1e-3
+
+
 def test_rope_frequency_closed_forms():
     for D in (64, 128):
         th = orc.rope_frequencies(D, 500000.0)
