@@ -8,8 +8,10 @@ PyTorch provides device memory and streams. Tensors must live on the GPU.
 Shapes (strides are taken from the tensors; the last dimension must be
 contiguous):
 
-* ``rope_qk(q_in, q_out, k_in, k_out, positions=None, rope_base=500000.0)``:
-  q [B,S,Hq,D], k [B,S,Hkv,D] (either pair may be None); positions int32 [B,S].
+* ``rope_qk(q_in, q_out, k_in, k_out, positions=None, rope_base=500000.0,
+  rope_pairing="adjacent")``: q [B,S,Hq,D], k [B,S,Hkv,D] (either pair may be None);
+  positions int32 [B,S]; rope_pairing "adjacent" (channels 2k, 2k+1) or "half"
+  (k, k+D/2), also taken by every call below that takes rope_base.
 * ``gqa_prefill(q, k, v, o, lse=None, cu_docs=None, softmax_scale=0.0)``:
   q/o [B,S,Hq,D], k/v [B,S,Hkv,D], cu_docs int32 [B, n_docs+1], lse fp32 [B,Hq,S].
 * ``gqa_prefill_rope(q, k, v, o, lse=None, cu_docs=None, softmax_scale=0.0,
@@ -116,7 +118,18 @@ def _same_shape(call, *pairs):
             raise ValueError(f"{call}: shape mismatch {tuple(a.shape)} vs {tuple(b.shape)}")
 
 
-def rope_qk(q_in, q_out, k_in=None, k_out=None, positions=None, rope_base: float = 500000.0):
+_PAIRING = {"adjacent": 0, "half": 1}
+
+
+def _pairing(p) -> int:
+    """rope_pairing: "adjacent" (channels 2k, 2k+1) or "half" (k, k + D/2)."""
+    if p not in _PAIRING:
+        raise ValueError(f"rope_pairing must be one of {sorted(_PAIRING)}, not {p!r}")
+    return _PAIRING[p]
+
+
+def rope_qk(q_in, q_out, k_in=None, k_out=None, positions=None, rope_base: float = 500000.0,
+            rope_pairing: str = "adjacent"):
     ref = q_in if q_in is not None else k_in
     B, S, _, D = ref.shape
     Hq = q_in.shape[2] if q_in is not None else 0
@@ -129,7 +142,8 @@ def rope_qk(q_in, q_out, k_in=None, k_out=None, positions=None, rope_base: float
     st = _lib.load().rope_qk(
         _dev(q_in), _dev(q_out), _strides(q_in, 3), _strides(q_out, 3),
         _dev(k_in), _dev(k_out), _strides(k_in, 3), _strides(k_out, 3),
-        _dtype(ref), B, S, Hq, Hkv, D, _i32(positions), float(rope_base), _stream())
+        _dtype(ref), B, S, Hq, Hkv, D, _i32(positions), float(rope_base), _pairing(rope_pairing),
+        _stream())
     _check(st, "rope_qk")
 
 
@@ -152,7 +166,7 @@ def gqa_prefill(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float = 0.0):
 
 
 def gqa_prefill_rope(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float = 0.0,
-                     positions=None, rope_base: float = 500000.0):
+                     positions=None, rope_base: float = 500000.0, rope_pairing: str = "adjacent"):
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     n_docs = cu_docs.shape[-1] - 1 if cu_docs is not None else 1
@@ -168,12 +182,13 @@ def gqa_prefill_rope(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float = 
     st = _lib.load().gqa_prefill_rope(
         _dev(q), _dev(k), _dev(v), _dev(o), _f32c(lse), _dtype(q), B, S, Hq, Hkv, D,
         _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
-        _i32(cu_docs), n_docs, float(softmax_scale), _i32(positions), float(rope_base), _stream())
+        _i32(cu_docs), n_docs, float(softmax_scale), _i32(positions), float(rope_base),
+        _pairing(rope_pairing), _stream())
     _check(st, "gqa_prefill_rope")
 
 
 def gqa_prefill_chunk(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float = 0.0,
-                      positions=None, rope_base: float = 0.0):
+                      positions=None, rope_base: float = 0.0, rope_pairing: str = "adjacent"):
     B, Sq, Hq, D = q.shape
     S, Hkv = k.shape[1], k.shape[2]
     n_docs = cu_docs.shape[-1] - 1 if cu_docs is not None else 1
@@ -189,7 +204,8 @@ def gqa_prefill_chunk(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float =
     st = _lib.load().gqa_prefill_chunk(
         _dev(q), _dev(k), _dev(v), _dev(o), _f32c(lse), _dtype(q), B, Sq, S, Hq, Hkv, D,
         _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
-        _i32(cu_docs), n_docs, float(softmax_scale), _i32(positions), float(rope_base), _stream())
+        _i32(cu_docs), n_docs, float(softmax_scale), _i32(positions), float(rope_base),
+        _pairing(rope_pairing), _stream())
     _check(st, "gqa_prefill_chunk")
 
 
@@ -202,7 +218,8 @@ def prefill_split_workspace(B: int, Sq: int, S: int, Hq: int, D: int, split_tile
 
 
 def gqa_prefill_split(q, k, v, o, split_tiles: int, o_part, lse_part, lse=None, cu_docs=None,
-                      softmax_scale: float = 0.0, positions=None, rope_base: float = 0.0):
+                      softmax_scale: float = 0.0, positions=None, rope_base: float = 0.0,
+                      rope_pairing: str = "adjacent"):
     B, Sq, Hq, D = q.shape
     S, Hkv = k.shape[1], k.shape[2]
     n_docs = cu_docs.shape[-1] - 1 if cu_docs is not None else 1
@@ -225,13 +242,14 @@ def gqa_prefill_split(q, k, v, o, split_tiles: int, o_part, lse_part, lse=None, 
         _dev(q), _dev(k), _dev(v), _dev(o), _f32c(lse), _dtype(q), B, Sq, S, Hq, Hkv, D,
         _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
         _i32(cu_docs), n_docs, float(softmax_scale), _i32(positions), float(rope_base),
-        int(split_tiles), int(max_splits), _dev(o_part), _dev(lse_part), _stream())
+        _pairing(rope_pairing), int(split_tiles), int(max_splits), _dev(o_part), _dev(lse_part),
+        _stream())
     _check(st, "gqa_prefill_split")
 
 
 def gqa_prefill_ring_step(q, k, v, q_off: int, k_off: int, o_acc, lse_acc, first: bool,
                           cu_docs=None, softmax_scale: float = 0.0, positions=None,
-                          rope_base: float = 0.0):
+                          rope_base: float = 0.0, rope_pairing: str = "adjacent"):
     B, Sq, Hq, D = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
     n_docs = cu_docs.shape[-1] - 1 if cu_docs is not None else 1
@@ -250,7 +268,8 @@ def gqa_prefill_ring_step(q, k, v, q_off: int, k_off: int, o_acc, lse_acc, first
     st = _lib.load().gqa_prefill_ring_step(
         _dev(q), _dev(k), _dev(v), _dev(o_acc), _dev(lse_acc), _dtype(q), B, Sq, int(q_off), Skv,
         int(k_off), Hq, Hkv, D, _strides(q, 3), _strides(k, 3), _strides(v, 3), _i32(cu_docs),
-        n_docs, float(softmax_scale), _i32(positions), float(rope_base), int(bool(first)), _stream())
+        n_docs, float(softmax_scale), _i32(positions), float(rope_base), _pairing(rope_pairing),
+        int(bool(first)), _stream())
     _check(st, "gqa_prefill_ring_step")
 
 

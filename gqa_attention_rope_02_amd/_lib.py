@@ -21,21 +21,21 @@ SIGNATURES = {
     "la_status_str": ([_i], ctypes.c_char_p),
     "la_version": ([], _i),
     "rope_qk": ([_vp, _vp, _c_i64_p, _c_i64_p, _vp, _vp, _c_i64_p, _c_i64_p, _i,
-                 _i, _i, _i, _i, _i, _vp, ctypes.c_double, _vp], _i),
+                 _i, _i, _i, _i, _i, _vp, ctypes.c_double, _i, _vp], _i),
     "gqa_prefill": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                      _c_i64_p, _c_i64_p, _c_i64_p, _c_i64_p, _vp, _i, ctypes.c_float, _vp], _i),
     "gqa_prefill_rope": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                           _c_i64_p, _c_i64_p, _c_i64_p, _c_i64_p, _vp, _i, ctypes.c_float,
-                          _vp, ctypes.c_double, _vp], _i),
+                          _vp, ctypes.c_double, _i, _vp], _i),
     "gqa_prefill_chunk": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                            _c_i64_p, _c_i64_p, _c_i64_p, _c_i64_p, _vp, _i, ctypes.c_float,
-                           _vp, ctypes.c_double, _vp], _i),
+                           _vp, ctypes.c_double, _i, _vp], _i),
     "gqa_prefill_split": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                            _c_i64_p, _c_i64_p, _c_i64_p, _c_i64_p, _vp, _i, ctypes.c_float,
-                           _vp, ctypes.c_double, _i, _i, _vp, _vp, _vp], _i),
+                           _vp, ctypes.c_double, _i, _i, _i, _vp, _vp, _vp], _i),
     "gqa_prefill_ring_step": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                                _c_i64_p, _c_i64_p, _c_i64_p, _vp, _i, ctypes.c_float, _vp,
-                               ctypes.c_double, _i, _vp], _i),
+                               ctypes.c_double, _i, _i, _vp], _i),
     "gqa_prefill_ring_finalize": ([_vp, _vp, _vp, _c_i64_p, _vp, _i, _i, _i, _i, _i, _vp], _i),
     "gqa_decode": ([_vp, _c_i64_p, _vp, _vp, _c_i64_p, _vp, _i, _i, _i, _i, _i, _i, _i,
                     ctypes.c_float, _vp, _vp, _vp], _i),

@@ -496,7 +496,9 @@ void prefill_kernel(PrefillArgs a) {
   issue(2);
   if (rope_q) {
     // RoPE of this lane's query channels 16ks + 8hi + 0..7, i.e. the pairs
-    // k = 8ks + 4hi + p: the angle position * theta_k is formed and reduced
+    // k = 8ks + 4hi + p (adjacent pairs (2k, 2k+1)) or, for half-split pairs
+    // (k, k + D/2), k = 16ks + 8hi + i for ks < KS/2 with the same channels of
+    // ks + KS/2 as partners: the angle position * theta_k is formed and reduced
     // in fp64 in revolutions (theta_k / 2pi from the host), its sine and
     // cosine taken in fp32 (v_sin/v_cos take revolutions), the pair rotated
     // in fp32 and rounded to bf16. Runs while the first K/V tiles load.
@@ -508,6 +510,16 @@ void prefill_kernel(PrefillArgs a) {
         r[2 * p + 1] = to_bf16(fmaf(x[2 * p], sv[p], x[2 * p + 1] * cv[p]));
       }
       return r;
+    };
+    // half-split pairs: elements e0 + 0..3 of x (first half) and y (second
+    // half, same positions), rotated into r and t
+    auto rotate_half = [&](const float* x, const float* y, int e0, const f32x4& cv, const f32x4& sv,
+                           bf16x8& r, bf16x8& t) __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        r[e0 + p] = to_bf16(fmaf(x[e0 + p], cv[p], -y[e0 + p] * sv[p]));
+        t[e0 + p] = to_bf16(fmaf(x[e0 + p], sv[p], y[e0 + p] * cv[p]));
+      }
     };
     if constexpr (TQ * (D / 2) * 4 <= TILE) {
       // The g lanes of a token share its angles: the workgroup forms the
@@ -534,11 +546,23 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
         const int tt = (wave * 32 * kCB + cb * 32 + lc) / G;
+        auto tab = [&](int c, int which) __attribute__((always_inline)) {   // 4 pairs from chunk c
+          return *reinterpret_cast<const f32x4*>(lds + (which ? 7 : 3) * TILE + tt * ROW +
+                                                  16 * (c ^ (tt & (CH - 1))));
+        };
+        if (a.rope_half) {
+          // channel 16ks + 8hi + i of the first half pairs with the same
+          // channel of the second half (ks + KS/2): pairs 16ks + 8hi + i
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int off = tt * ROW + 16 * ((2 * ks + hi) ^ (tt & (CH - 1)));
-          qreg[cb][ks] = rotate(qraw[cb][ks], *reinterpret_cast<const f32x4*>(lds + 3 * TILE + off),
-                                *reinterpret_cast<const f32x4*>(lds + 7 * TILE + off));
+          for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              rotate_half(qraw[cb][ks], qraw[cb][ks + KS / 2], 4 * h, tab(4 * ks + 2 * hi + h, 0),
+                          tab(4 * ks + 2 * hi + h, 1), qreg[cb][ks], qreg[cb][ks + KS / 2]);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            qreg[cb][ks] = rotate(qraw[cb][ks], tab(2 * ks + hi, 0), tab(2 * ks + hi, 1));
         }
       }
     } else {
@@ -546,19 +570,34 @@ void prefill_kernel(PrefillArgs a) {
       for (int cb = 0; cb < kCB; ++cb) {
         const int t = min(tok[cb], Sq - 1);
         const double pos = a.positions ? (double)a.positions[(int64_t)b * Sq + t] : (double)(t + qo);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          f32x4 cv, sv;
+        // cos and sin of pairs k0 + hi_step * hi + 0..3
+        auto angles = [&](int k0, int hi_step, f32x4& cv, f32x4& sv) __attribute__((always_inline)) {
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const int k0 = 8 * ks + p;
-            const double th = hi ? a.theta_rev[k0 + 4] : a.theta_rev[k0];
+            const double th = hi ? a.theta_rev[k0 + hi_step + p] : a.theta_rev[k0 + p];
             const double rev = pos * th;
             const float fr = (float)(rev - rint(rev));   // in [-1/2, 1/2]
             cv[p] = __builtin_amdgcn_cosf(fr);
             sv[p] = __builtin_amdgcn_sinf(fr);
           }
-          qreg[cb][ks] = rotate(qraw[cb][ks], cv, sv);
+        };
+        if (a.rope_half) {
+#pragma unroll
+          for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              f32x4 cv, sv;
+              angles(16 * ks + 4 * h, 8, cv, sv);
+              rotate_half(qraw[cb][ks], qraw[cb][ks + KS / 2], 4 * h, cv, sv, qreg[cb][ks],
+                          qreg[cb][ks + KS / 2]);
+            }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            f32x4 cv, sv;
+            angles(8 * ks, 4, cv, sv);
+            qreg[cb][ks] = rotate(qraw[cb][ks], cv, sv);
+          }
         }
       }
     }

@@ -21,6 +21,7 @@ struct RopeArgs {
 // fp64: RoPE angles in revolutions
 struct RopeAngles {
   double theta_rev[64];
+  int half;   // pair k is channels (k, k + D/2) instead of (2k, 2k+1)
 };
 
 struct PrefillArgs {
@@ -43,7 +44,8 @@ struct PrefillArgs {
   // RoPE of the queries inside the kernel (gqa_prefill_rope); rope_q = 0: the
   // queries arrive rotated
   int rope_q;
-  const int32_t* positions;   // [B, S] or null (position = s)
+  int rope_half;              // pair k is channels (k, k + D/2) instead of (2k, 2k+1)
+  const int32_t* positions;   // [B, Sq] or null (position = q_off + row)
   double theta_rev[64];       // theta_k / (2 pi), k < D/2: angles in revolutions
   // split key ranges (split_tiles > 0): partials in o_part fp32
   // [max_splits, B, Sq, Hq, D] and lse_part fp32 [max_splits, B, Hq, Sq]

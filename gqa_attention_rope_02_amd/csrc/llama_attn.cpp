@@ -57,7 +57,7 @@ la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
                   const int64_t q_out_strides[3], const void* k_in, void* k_out,
                   const int64_t k_in_strides[3], const int64_t k_out_strides[3], la_dtype dt,
                   int B, int S, int Hq, int Hkv, int D, const int32_t* positions,
-                  double rope_base, hipStream_t stream) {
+                  double rope_base, int rope_pairing, hipStream_t stream) {
   if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
   const bool has_q = q_in != nullptr || q_out != nullptr;
   const bool has_k = k_in != nullptr || k_out != nullptr;
@@ -66,6 +66,7 @@ la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
   if (has_k && (k_in == nullptr || k_out == nullptr)) return LA_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || (has_q && Hq < 1) || (has_k && Hkv < 1)) return LA_ERR_INVALID_ARG;
   if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
+  if (rope_pairing != 0 && rope_pairing != 1) return LA_ERR_INVALID_ARG;
   if ((long long)B * S > 0x7fffffffLL) return LA_ERR_INVALID_ARG;
   if (!supported_d(D)) return LA_ERR_UNSUPPORTED;
   const int es = elem_size(dt);
@@ -87,6 +88,7 @@ la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
   }
   la::RopeAngles ang{};
   theta_revolutions(rope_base, D, ang.theta_rev);
+  ang.half = rope_pairing;
   return launched(la::launch_rope_pair(qa, ka, ang, D, dt == LA_BF16 ? 0 : 1, stream));
 }
 
@@ -100,12 +102,13 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
                        const int64_t q_strides[3], const int64_t k_strides[3],
                        const int64_t v_strides[3], const int64_t o_strides[3],
                        const int32_t* cu_docs, int n_docs, float softmax_scale,
-                       const int32_t* positions, double rope_base, hipStream_t stream,
-                       int split_tiles = 0, int max_splits = 0, float* o_part = nullptr,
+                       const int32_t* positions, double rope_base, int rope_pairing,
+                       hipStream_t stream, int split_tiles = 0, int max_splits = 0, float* o_part = nullptr,
                        float* lse_part = nullptr, bool ring = false, int q_off = 0, int k_off = 0,
                        int acc_mode = 0, float* o_acc = nullptr, float* lse_acc = nullptr) {
   if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
   if (!q || !k || !v || (!o && !ring)) return LA_ERR_INVALID_ARG;
+  if (rope_pairing != 0 && rope_pairing != 1) return LA_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return LA_ERR_INVALID_ARG;
   if (Sq < 1 || (!ring && Sq > S)) return LA_ERR_INVALID_ARG;
   if (ring) {
@@ -159,6 +162,7 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
   a.scale_log2 = scale * 1.4426950408889634f;
   if (rope_base > 0.0) {
     a.rope_q = 1;
+    a.rope_half = rope_pairing;
     a.positions = positions;
     theta_revolutions(rope_base, D, a.theta_rev);
   }
@@ -181,7 +185,7 @@ la_status gqa_prefill(const void* q, const void* k, const void* v, void* o, floa
                       const int32_t* cu_docs, int n_docs, float softmax_scale,
                       hipStream_t stream) {
   return prefill_impl(q, k, v, o, lse, dt, B, S, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
-                      o_strides, cu_docs, n_docs, softmax_scale, nullptr, 0.0, stream);
+                      o_strides, cu_docs, n_docs, softmax_scale, nullptr, 0.0, 0, stream);
 }
 
 la_status gqa_prefill_rope(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -189,10 +193,12 @@ la_status gqa_prefill_rope(const void* q, const void* k, const void* v, void* o,
                            const int64_t q_strides[3], const int64_t k_strides[3],
                            const int64_t v_strides[3], const int64_t o_strides[3],
                            const int32_t* cu_docs, int n_docs, float softmax_scale,
-                           const int32_t* positions, double rope_base, hipStream_t stream) {
+                           const int32_t* positions, double rope_base, int rope_pairing,
+                           hipStream_t stream) {
   if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
   return prefill_impl(q, k, v, o, lse, dt, B, S, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
-                      o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base, stream);
+                      o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base, rope_pairing,
+                      stream);
 }
 
 la_status gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -200,10 +206,12 @@ la_status gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o
                             const int64_t q_strides[3], const int64_t k_strides[3],
                             const int64_t v_strides[3], const int64_t o_strides[3],
                             const int32_t* cu_docs, int n_docs, float softmax_scale,
-                            const int32_t* positions, double rope_base, hipStream_t stream) {
+                            const int32_t* positions, double rope_base, int rope_pairing,
+                            hipStream_t stream) {
   if (!(rope_base >= 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
   return prefill_impl(q, k, v, o, lse, dt, B, Sq, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
-                      o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base, stream);
+                      o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base, rope_pairing,
+                      stream);
 }
 
 la_status gqa_prefill_split(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -211,13 +219,14 @@ la_status gqa_prefill_split(const void* q, const void* k, const void* v, void* o
                             const int64_t q_strides[3], const int64_t k_strides[3],
                             const int64_t v_strides[3], const int64_t o_strides[3],
                             const int32_t* cu_docs, int n_docs, float softmax_scale,
-                            const int32_t* positions, double rope_base, int split_tiles,
-                            int max_splits, float* o_part, float* lse_part, hipStream_t stream) {
+                            const int32_t* positions, double rope_base, int rope_pairing,
+                            int split_tiles, int max_splits, float* o_part, float* lse_part,
+                            hipStream_t stream) {
   if (!(rope_base >= 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
   if (split_tiles < 1) return LA_ERR_INVALID_ARG;
   return prefill_impl(q, k, v, o, lse, dt, B, Sq, S, Hq, Hkv, D, q_strides, k_strides, v_strides,
-                      o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base, stream,
-                      split_tiles, max_splits, o_part, lse_part);
+                      o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base, rope_pairing,
+                      stream, split_tiles, max_splits, o_part, lse_part);
 }
 
 la_status gqa_prefill_ring_step(const void* q, const void* k, const void* v, float* o_acc,
@@ -225,13 +234,13 @@ la_status gqa_prefill_ring_step(const void* q, const void* k, const void* v, flo
                                 int k_off, int Hq, int Hkv, int D, const int64_t q_strides[3],
                                 const int64_t k_strides[3], const int64_t v_strides[3],
                                 const int32_t* cu_docs, int n_docs, float softmax_scale,
-                                const int32_t* positions, double rope_base, int first,
-                                hipStream_t stream) {
+                                const int32_t* positions, double rope_base, int rope_pairing,
+                                int first, hipStream_t stream) {
   if (!(rope_base >= 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
   return prefill_impl(q, k, v, nullptr, nullptr, dt, B, Sq, Skv, Hq, Hkv, D, q_strides, k_strides,
                       v_strides, nullptr, cu_docs, n_docs, softmax_scale, positions, rope_base,
-                      stream, 0, 0, nullptr, nullptr, true, q_off, k_off, first ? 1 : 2, o_acc,
-                      lse_acc);
+                      rope_pairing, stream, 0, 0, nullptr, nullptr, true, q_off, k_off,
+                      first ? 1 : 2, o_acc, lse_acc);
 }
 
 la_status gqa_prefill_ring_finalize(const float* o_acc, const float* lse_acc, void* o,

@@ -3,8 +3,9 @@
 // theta_k = base^(-2k/d), k in [0, d/2-1]; base 500,000 per "The Llama 3 Herd
 // of Models", "A Deliberately Standard Dense Transformer").
 //
-// A thread owns one 16-byte chunk c of a head row (channels 8c..8c+7, i.e.
-// the pairs 4c..4c+3) in every HG-th head of Q and K (Q's heads then K's, as
+// A thread owns the pairs 4c..4c+3 of a head row (channels 8c..8c+7, one
+// 16-byte chunk, for adjacent pairs (2k, 2k+1); channels 4c..4c+3 and
+// D/2 + 4c..D/2 + 4c+3 for half-split pairs (k, k + D/2)) in every HG-th head of Q and K (Q's heads then K's, as
 // one list) of one token; the D/8 threads of a chunk row cover a head row
 // contiguously. A workgroup forms the angles position * theta_k of its tokens
 // once, in revolutions (theta_k / 2pi comes from the host in fp64), reduces
@@ -57,6 +58,40 @@ __device__ __forceinline__ void store_row(T* p, const float* y) {
   }
 }
 
+// Half-split layout: the thread's four pairs are channels 4c..4c+3 and
+// D/2 + 4c..D/2 + 4c+3; a Row8 holds the first four then the second four.
+template <typename T>
+__device__ __forceinline__ Row8<T> load_row_half(const T* p, int half_d) {
+  Row8<T> r;
+  if constexpr (sizeof(T) == 2) {
+    typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<b4*>(r.v) = *reinterpret_cast<const b4*>(p);
+    *reinterpret_cast<b4*>(r.v + 4) = *reinterpret_cast<const b4*>(p + half_d);
+  } else {
+    *reinterpret_cast<f32x4*>(r.v) = *reinterpret_cast<const f32x4*>(p);
+    *reinterpret_cast<f32x4*>(r.v + 4) = *reinterpret_cast<const f32x4*>(p + half_d);
+  }
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_row_half(T* p, int half_d, const float* y) {
+  if constexpr (sizeof(T) == 2) {
+    typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+    b4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = to_bf16(y[i]);
+      b[i] = to_bf16(y[4 + i]);
+    }
+    *reinterpret_cast<b4*>(p) = a;
+    *reinterpret_cast<b4*>(p + half_d) = b;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = f32x4{y[0], y[1], y[2], y[3]};
+    *reinterpret_cast<f32x4*>(p + half_d) = f32x4{y[4], y[5], y[6], y[7]};
+  }
+}
+
 // (y0, y1) = (x0 c - x1 s, x0 s + x1 c) in fp32, with c = ch + cl and
 // s = sh + sl split into fp32 high and low parts of the fp64 values: the
 // rounding error of the first product is recovered exactly by an FMA and the
@@ -94,7 +129,7 @@ struct Rows {
   __device__ T* out(int v) const { return v < Hq ? qout + v * qos : kout + (v - Hq) * kos; }
 };
 
-template <typename T, int D, int HG>
+template <typename T, int D, int HG, bool HALF>
 __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs qa, RopeArgs ka, RopeAngles ang) {
   constexpr int CH = D / 8;              // 16-byte chunks (4 pairs) per head row
   constexpr int TT = kThreads / CH / HG; // tokens per workgroup
@@ -113,10 +148,13 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs qa, RopeArgs ka
   Rows<T> rw;
   rw.Hq = qa.in ? qa.H : 0;
   rw.H = rw.Hq + (ka.in ? ka.H : 0);
-  rw.qin = qa.in ? static_cast<const T*>(qa.in) + b * qa.is_b + s * qa.is_s + 8 * c : nullptr;
-  rw.qout = qa.in ? static_cast<T*>(qa.out) + b * qa.os_b + s * qa.os_s + 8 * c : nullptr;
-  rw.kin = ka.in ? static_cast<const T*>(ka.in) + b * ka.is_b + s * ka.is_s + 8 * c : nullptr;
-  rw.kout = ka.in ? static_cast<T*>(ka.out) + b * ka.os_b + s * ka.os_s + 8 * c : nullptr;
+  // this thread's channels start at 8c (adjacent pairs 4c..4c+3) or at 4c
+  // and D/2 + 4c (half-split pairs 4c..4c+3)
+  const int ch0 = HALF ? 4 * c : 8 * c;
+  rw.qin = qa.in ? static_cast<const T*>(qa.in) + b * qa.is_b + s * qa.is_s + ch0 : nullptr;
+  rw.qout = qa.in ? static_cast<T*>(qa.out) + b * qa.os_b + s * qa.os_s + ch0 : nullptr;
+  rw.kin = ka.in ? static_cast<const T*>(ka.in) + b * ka.is_b + s * ka.is_s + ch0 : nullptr;
+  rw.kout = ka.in ? static_cast<T*>(ka.out) + b * ka.os_b + s * ka.os_s + ch0 : nullptr;
   rw.qis = qa.is_h; rw.qos = qa.os_h; rw.kis = ka.is_h; rw.kos = ka.os_h;
   const int H = live ? rw.H : 0;
 
@@ -125,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs qa, RopeArgs ka
   Row8<T> r[kBatch];
 #pragma unroll
   for (int i = 0; i < kBatch; ++i)
-    if (g + i * HG < H) r[i] = load_row<T>(rw.in(g + i * HG));
+    if (g + i * HG < H) r[i] = HALF ? load_row_half<T>(rw.in(g + i * HG), D / 2) : load_row<T>(rw.in(g + i * HG));
 
   // sine and cosine of every (token, pair) of the workgroup, once, into LDS
   for (int e = threadIdx.x; e < TT * (D / 2); e += kThreads) {
@@ -158,15 +196,27 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeArgs qa, RopeArgs ka
       const int v = v0 + i * HG;
       if (v >= H) break;
       float y[8];
+      if constexpr (HALF) {
+        float yp[2];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) rotate_pair(r[i].v[2 * p], r[i].v[2 * p + 1], ch[p], cl[p], sh[p], sl[p], y + 2 * p);
-      store_row<T>(rw.out(v), y);
+        for (int p = 0; p < 4; ++p) {
+          rotate_pair(r[i].v[p], r[i].v[4 + p], ch[p], cl[p], sh[p], sl[p], yp);
+          y[p] = yp[0];
+          y[4 + p] = yp[1];
+        }
+        store_row_half<T>(rw.out(v), D / 2, y);
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) rotate_pair(r[i].v[2 * p], r[i].v[2 * p + 1], ch[p], cl[p], sh[p], sl[p], y + 2 * p);
+        store_row<T>(rw.out(v), y);
+      }
     }
     const int v1 = v0 + kBatch * HG;
     if (v1 >= H) break;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i)
-      if (v1 + i * HG < H) r[i] = load_row<T>(rw.in(v1 + i * HG));
+      if (v1 + i * HG < H)
+        r[i] = HALF ? load_row_half<T>(rw.in(v1 + i * HG), D / 2) : load_row<T>(rw.in(v1 + i * HG));
   }
 }
 
@@ -175,8 +225,11 @@ hipError_t launch_hg(const RopeArgs& q, const RopeArgs& k, const RopeAngles& ang
   const RopeArgs& any = q.in ? q : k;
   constexpr int tpb = kThreads / (D / 8) / HG;
   const long long ntok = (long long)any.B * any.S;
-  hipLaunchKernelGGL((rope_kernel<T, D, HG>), dim3((unsigned)((ntok + tpb - 1) / tpb)), dim3(kThreads), 0,
-                     st, q, k, ang);
+  const dim3 grid((unsigned)((ntok + tpb - 1) / tpb));
+  if (ang.half)
+    hipLaunchKernelGGL((rope_kernel<T, D, HG, true>), grid, dim3(kThreads), 0, st, q, k, ang);
+  else
+    hipLaunchKernelGGL((rope_kernel<T, D, HG, false>), grid, dim3(kThreads), 0, st, q, k, ang);
   return hipGetLastError();
 }
 

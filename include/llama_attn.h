@@ -32,8 +32,12 @@
  *     not read on the host.
  *   - Head mapping: query head h reads KV head h / (Hq / Hkv) (contiguous
  *     groups) [P2, P4].
- *   - RoPE pairs adjacent channels (2k, 2k+1) and rotates them by the angle
- *     position * theta_k, theta_k = rope_base^(-2k/D), k = 0..D/2-1 [P1].
+ *   - RoPE rotates channel pair k by the angle position * theta_k,
+ *     theta_k = rope_base^(-2k/D), k = 0..D/2-1 [P1]. Every call that takes
+ *     rope_base also takes rope_pairing: 0 pairs adjacent channels (2k, 2k+1)
+ *     (RoFormer's layout, which [P1] cites), 1 pairs channel k with k + D/2
+ *     (the half-split layout; the pages do not fix the layout). Any other
+ *     value is INVALID_ARG.
  *   - Supported: D in {64, 128}; Hq / Hkv in {1, 2, 4, 8, 16}.
  */
 #ifndef LLAMA_ATTN_H
@@ -81,7 +85,7 @@ la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
                   const void* k_in, void* k_out, const int64_t k_in_strides[3],
                   const int64_t k_out_strides[3],
                   la_dtype dt, int B, int S, int Hq, int Hkv, int D,
-                  const int32_t* positions, double rope_base, hipStream_t stream);
+                  const int32_t* positions, double rope_base, int rope_pairing, hipStream_t stream);
 
 /*
  * gqa_prefill — grouped-query causal attention with the cross-document mask,
@@ -132,7 +136,7 @@ la_status gqa_prefill_rope(const void* q, const void* k, const void* v, void* o,
                            const int64_t q_strides[3], const int64_t k_strides[3],
                            const int64_t v_strides[3], const int64_t o_strides[3],
                            const int32_t* cu_docs, int n_docs, float softmax_scale,
-                           const int32_t* positions, double rope_base, hipStream_t stream);
+                           const int32_t* positions, double rope_base, int rope_pairing, hipStream_t stream);
 
 /*
  * gqa_prefill_chunk — prefill of a block of new tokens after a cached prefix
@@ -160,7 +164,7 @@ la_status gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o
                             const int64_t q_strides[3], const int64_t k_strides[3],
                             const int64_t v_strides[3], const int64_t o_strides[3],
                             const int32_t* cu_docs, int n_docs, float softmax_scale,
-                            const int32_t* positions, double rope_base, hipStream_t stream);
+                            const int32_t* positions, double rope_base, int rope_pairing, hipStream_t stream);
 
 /*
  * gqa_prefill_split — gqa_prefill_chunk with long key ranges split across
@@ -186,7 +190,7 @@ la_status gqa_prefill_split(const void* q, const void* k, const void* v, void* o
                             const int64_t q_strides[3], const int64_t k_strides[3],
                             const int64_t v_strides[3], const int64_t o_strides[3],
                             const int32_t* cu_docs, int n_docs, float softmax_scale,
-                            const int32_t* positions, double rope_base, int split_tiles,
+                            const int32_t* positions, double rope_base, int rope_pairing, int split_tiles,
                             int max_splits, float* o_part, float* lse_part, hipStream_t stream);
 
 /*
@@ -218,7 +222,7 @@ la_status gqa_prefill_ring_step(const void* q, const void* k, const void* v, flo
                                 int k_off, int Hq, int Hkv, int D, const int64_t q_strides[3],
                                 const int64_t k_strides[3], const int64_t v_strides[3],
                                 const int32_t* cu_docs, int n_docs, float softmax_scale,
-                                const int32_t* positions, double rope_base, int first,
+                                const int32_t* positions, double rope_base, int rope_pairing, int first,
                                 hipStream_t stream);
 
 /*

@@ -78,46 +78,47 @@ def test_prefill_rejects(lib, kw, status):
     assert prefill(lib, **kw) == status
 
 
-def prefill_rope(lib, base=5e5, **kw):
+def prefill_rope(lib, base=5e5, pairing=0, **kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dt=0, B=1, S=16, Hq=16, Hkv=1, D=128,
                 qs=S3, ks=S3, vs=S3, os_=S3, cu=None, nd=1, scale=0.0)
     args.update(kw)
     return lib.gqa_prefill_rope(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dt"],
                                 args["B"], args["S"], args["Hq"], args["Hkv"], args["D"], args["qs"],
                                 args["ks"], args["vs"], args["os_"], args["cu"], args["nd"],
-                                args["scale"], None, base, None)
+                                args["scale"], None, base, pairing, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(base=0.0), INVALID), (dict(base=-1.0), INVALID), (dict(base=float("inf")), INVALID),
     (dict(base=float("nan")), INVALID), (dict(q=None), INVALID), (dict(D=96), UNSUPPORTED),
     (dict(Hq=12, Hkv=8), INVALID), (dict(qs=S3_BAD), INVALID), (dict(cu=FAKE, nd=0), INVALID),
+    (dict(pairing=2), INVALID), (dict(pairing=-1), INVALID),
 ])
 def test_prefill_rope_rejects(lib, kw, status):
     assert prefill_rope(lib, **kw) == status
 
 
-def prefill_chunk(lib, base=0.0, **kw):
+def prefill_chunk(lib, base=0.0, pairing=0, **kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dt=0, B=1, Sq=4, S=16, Hq=16, Hkv=1,
                 D=128, qs=S3, ks=S3, vs=S3, os_=S3, cu=None, nd=1, scale=0.0)
     args.update(kw)
     return lib.gqa_prefill_chunk(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dt"],
                                  args["B"], args["Sq"], args["S"], args["Hq"], args["Hkv"], args["D"],
                                  args["qs"], args["ks"], args["vs"], args["os_"], args["cu"],
-                                 args["nd"], args["scale"], None, base, None)
+                                 args["nd"], args["scale"], None, base, pairing, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(Sq=0), INVALID), (dict(Sq=17), INVALID), (dict(S=0), INVALID),
     (dict(base=-1.0), INVALID), (dict(base=float("inf")), INVALID), (dict(base=float("nan")), INVALID),
     (dict(q=None), INVALID), (dict(D=96), UNSUPPORTED), (dict(Hq=12, Hkv=8), INVALID),
-    (dict(qs=S3_BAD), INVALID), (dict(cu=FAKE, nd=0), INVALID),
+    (dict(qs=S3_BAD), INVALID), (dict(cu=FAKE, nd=0), INVALID), (dict(pairing=3), INVALID),
 ])
 def test_prefill_chunk_rejects(lib, kw, status):
     assert prefill_chunk(lib, **kw) == status
 
 
-def prefill_split(lib, base=0.0, **kw):
+def prefill_split(lib, base=0.0, pairing=0, **kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dt=0, B=1, Sq=4, S=1000, Hq=16, Hkv=1,
                 D=128, qs=S3, ks=S3, vs=S3, os_=S3, cu=None, nd=1, scale=0.0, st=4, ms=4, op=FAKE,
                 lp=FAKE)
@@ -125,7 +126,7 @@ def prefill_split(lib, base=0.0, **kw):
     return lib.gqa_prefill_split(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dt"],
                                  args["B"], args["Sq"], args["S"], args["Hq"], args["Hkv"], args["D"],
                                  args["qs"], args["ks"], args["vs"], args["os_"], args["cu"],
-                                 args["nd"], args["scale"], None, base, args["st"], args["ms"],
+                                 args["nd"], args["scale"], None, base, pairing, args["st"], args["ms"],
                                  args["op"], args["lp"], None)
 
 
@@ -133,13 +134,13 @@ def prefill_split(lib, base=0.0, **kw):
     (dict(st=0), INVALID), (dict(st=-2), INVALID), (dict(ms=3), INVALID),   # 16 tiles / 4 -> 4 needed
     (dict(ms=70000), INVALID), (dict(op=None), INVALID), (dict(lp=None), INVALID),
     (dict(op=FAKE + 4), INVALID), (dict(Sq=1001), INVALID), (dict(base=-1.0), INVALID),
-    (dict(D=96), UNSUPPORTED), (dict(q=None), INVALID),
+    (dict(D=96), UNSUPPORTED), (dict(q=None), INVALID), (dict(pairing=2), INVALID),
 ])
 def test_prefill_split_rejects(lib, kw, status):
     assert prefill_split(lib, **kw) == status
 
 
-def ring_step(lib, base=0.0, **kw):
+def ring_step(lib, base=0.0, pairing=0, **kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, oa=FAKE, la=FAKE, dt=0, B=1, Sq=64, qo=128, Skv=64, ko=0,
                 Hq=16, Hkv=1, D=128, qs=S3, ks=S3, vs=S3, cu=None, nd=1, scale=0.0, first=1)
     args.update(kw)
@@ -147,7 +148,7 @@ def ring_step(lib, base=0.0, **kw):
                                      args["B"], args["Sq"], args["qo"], args["Skv"], args["ko"],
                                      args["Hq"], args["Hkv"], args["D"], args["qs"], args["ks"],
                                      args["vs"], args["cu"], args["nd"], args["scale"], None, base,
-                                     args["first"], None)
+                                     pairing, args["first"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -155,6 +156,7 @@ def ring_step(lib, base=0.0, **kw):
     (dict(qo=0x7fffffff), INVALID), (dict(oa=None), INVALID), (dict(la=None), INVALID),
     (dict(oa=FAKE + 4), INVALID), (dict(base=-1.0), INVALID), (dict(D=96), UNSUPPORTED),
     (dict(Hq=12, Hkv=8), INVALID), (dict(ks=S3_BAD), INVALID), (dict(k=None), INVALID),
+    (dict(pairing=2), INVALID),
 ])
 def test_ring_step_rejects(lib, kw, status):
     assert ring_step(lib, **kw) == status
@@ -173,18 +175,19 @@ def test_ring_finalize_rejects(lib, kw, status):
 
 
 def rope(lib, **kw):
-    args = dict(qi=FAKE, qo=FAKE, ki=FAKE, ko=FAKE, dt=0, B=1, S=4, Hq=8, Hkv=2, D=128, base=5e5)
+    args = dict(qi=FAKE, qo=FAKE, ki=FAKE, ko=FAKE, dt=0, B=1, S=4, Hq=8, Hkv=2, D=128, base=5e5,
+                pairing=0)
     args.update(kw)
     return lib.rope_qk(args["qi"], args["qo"], S3, S3, args["ki"], args["ko"], S3, S3, args["dt"],
                        args["B"], args["S"], args["Hq"], args["Hkv"], args["D"], None,
-                       args["base"], None)
+                       args["base"], args["pairing"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(qi=None, qo=None, ki=None, ko=None), INVALID), (dict(qo=None), INVALID),
     (dict(ko=None), INVALID), (dict(S=0), INVALID), (dict(base=0.0), INVALID),
     (dict(base=float("inf")), INVALID), (dict(D=80), UNSUPPORTED), (dict(dt=3), UNSUPPORTED),
-    (dict(qo=FAKE + 8), INVALID),
+    (dict(qo=FAKE + 8), INVALID), (dict(pairing=2), INVALID), (dict(pairing=-1), INVALID),
 ])
 def test_rope_rejects(lib, kw, status):
     assert rope(lib, **kw) == status

@@ -13,7 +13,7 @@ from workloads import draw_cu_docs, draw_positions, draw_prefill_inputs
 pytestmark = pytest.mark.gpu
 
 
-def _fused(q, k, v, cu, positions=None, rope_base=500000.0, softmax_scale=0.0):
+def _fused(q, k, v, cu, positions=None, rope_base=500000.0, softmax_scale=0.0, pairing="adjacent"):
     """rope_qk on k only, then gqa_prefill_rope on the raw q; CPU outputs."""
     import gqa_attention_rope_02_amd as la
     dev = torch.device("cuda")
@@ -21,11 +21,12 @@ def _fused(q, k, v, cu, positions=None, rope_base=500000.0, softmax_scale=0.0):
     B, S, Hq, D = q.shape
     kr = torch.full_like(kd, float("nan"))
     pos = None if positions is None else torch.as_tensor(np.asarray(positions), dtype=torch.int32).to(dev)
-    la.rope_qk(None, None, kd, kr, positions=pos, rope_base=rope_base)
+    la.rope_qk(None, None, kd, kr, positions=pos, rope_base=rope_base, rope_pairing=pairing)
     o = torch.full_like(qd, float("nan"))
     lse = torch.full((B, Hq, S), float("nan"), dtype=torch.float32, device=dev)
     cud = None if cu is None else torch.as_tensor(np.asarray(cu), dtype=torch.int32).reshape(B, -1).to(dev)
-    la.gqa_prefill_rope(qd, kr, vd, o, lse, cud, softmax_scale, positions=pos, rope_base=rope_base)
+    la.gqa_prefill_rope(qd, kr, vd, o, lse, cud, softmax_scale, positions=pos, rope_base=rope_base,
+                        rope_pairing=pairing)
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
 
@@ -86,3 +87,21 @@ def test_prefill_rope_position_zero_leaves_queries_unrotated():
     la.gqa_prefill_rope(qd, kd, vd, o2, positions=pos)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,seed,positions", [
+    (1, 400, 32, 8, 128, 78, False),    # g=4: the shared angle table
+    (1, 300, 8, 4, 128, 79, True),      # g=2: angles per lane
+    (1, 260, 16, 1, 64, 80, True),      # g=16, D=64
+])
+def test_prefill_rope_half_pairing_matches_oracle(B, S, Hq, Hkv, D, seed, positions):
+    """Half-split pairing through the fused path (keys by rope_qk, queries in
+    the kernel) against the oracle's half layout."""
+    H.say("prefill_rope half", dict(B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, seed=seed))
+    q, k, v = draw_prefill_inputs(B, S, Hq, Hkv, D, "bf16", seed)
+    cu = draw_cu_docs(S, seed, 3, 1)
+    pos = draw_positions(B, S, 131071 - S, seed) if positions else None
+    O, L = _fused(q, k, v, cu, pos, pairing="half")
+    Ow, Lw = orc.rope_attention(q, k, v, cu, 500000.0, pos, pairing="half")
+    H.assert_close(O, Ow)
+    H.assert_close(L, Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")

@@ -11,16 +11,16 @@ from workloads import draw_positions, draw_prefill_inputs
 pytestmark = pytest.mark.gpu
 
 
-def _rope_gpu(q, k, positions=None, base=500000.0, inplace=False):
+def _rope_gpu(q, k, positions=None, base=500000.0, inplace=False, pairing="adjacent"):
     import gqa_attention_rope_02_amd as la
     qd, kd = q.cuda(), k.cuda()
     pos = None if positions is None else torch.as_tensor(positions, dtype=torch.int32).cuda()
     if inplace:
-        la.rope_qk(qd, qd, kd, kd, positions=pos, rope_base=base)
+        la.rope_qk(qd, qd, kd, kd, positions=pos, rope_base=base, rope_pairing=pairing)
         qo, ko = qd, kd
     else:
         qo, ko = torch.full_like(qd, float("nan")), torch.full_like(kd, float("nan"))
-        la.rope_qk(qd, qo, kd, ko, positions=pos, rope_base=base)
+        la.rope_qk(qd, qo, kd, ko, positions=pos, rope_base=base, rope_pairing=pairing)
     torch.cuda.synchronize()
     return qo.cpu(), ko.cpu()
 
@@ -79,3 +79,28 @@ def test_rope_strided_views_of_packed_qkv():
     assert np.all(np.abs(out[:, :, :Hq].double().numpy() - want_q) <= H.bf16_ulp(want_q))
     assert np.all(np.abs(out[:, :, Hq:Hq + Hkv].double().numpy() - want_k) <= H.bf16_ulp(want_k))
     assert torch.isnan(out[:, :, Hq + Hkv:].float()).all()     # V slot untouched
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,maxpos,dtype,base", [
+    (1, 150, 16, 2, 128, None, "bf16", 500000.0), (2, 60, 8, 8, 64, 131071, "bf16", 500000.0),
+    (1, 70, 32, 8, 128, 131071, "bf16", 5000000.0), (1, 50, 8, 2, 64, 4000, "fp32", 500000.0),
+])
+def test_rope_half_split_pairing(B, S, Hq, Hkv, D, maxpos, dtype, base):
+    """rope_pairing="half" (channel k with k + D/2) against the oracle's half
+    layout: within 1 bf16 ulp (fp32: a few fp32 ulps of the row's scale);
+    base 5,000,000 too (the long-context base the pages also name)."""
+    H.say("rope half", B, S, Hq, Hkv, D, maxpos, dtype, base)
+    q, k, _ = draw_prefill_inputs(B, S, Hq, Hkv, D, dtype, 23)
+    positions = None if maxpos is None else draw_positions(B, S, maxpos, 23)
+    pos = np.broadcast_to(np.arange(S), (B, S)) if positions is None else positions
+    qo, ko = _rope_gpu(q, k, positions, base, pairing="half")
+    for got, x in ((qo, q), (ko, k)):
+        want = orc.rope(x, pos, base, "half")
+        err = np.abs(got.double().numpy() - want)
+        if dtype == "bf16":
+            assert np.all(err <= H.bf16_ulp(want)), f"max err/ulp {np.max(err / H.bf16_ulp(want)):.3f}"
+        else:
+            assert np.all(err <= 8 * H.fp32_ulp(np.abs(x.double().numpy()).max()) + 1e-7)
+    # the two layouts differ
+    qa, _ = _rope_gpu(q, k, positions, base)
+    assert not torch.equal(qa, qo)
