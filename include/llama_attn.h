@@ -136,7 +136,8 @@ la_status gqa_prefill_rope(const void* q, const void* k, const void* v, void* o,
                            const int64_t q_strides[3], const int64_t k_strides[3],
                            const int64_t v_strides[3], const int64_t o_strides[3],
                            const int32_t* cu_docs, int n_docs, float softmax_scale,
-                           const int32_t* positions, double rope_base, int rope_pairing, hipStream_t stream);
+                           const int32_t* positions, double rope_base, int rope_pairing,
+                           hipStream_t stream);
 
 /*
  * gqa_prefill_chunk — prefill of a block of new tokens after a cached prefix
@@ -164,7 +165,8 @@ la_status gqa_prefill_chunk(const void* q, const void* k, const void* v, void* o
                             const int64_t q_strides[3], const int64_t k_strides[3],
                             const int64_t v_strides[3], const int64_t o_strides[3],
                             const int32_t* cu_docs, int n_docs, float softmax_scale,
-                            const int32_t* positions, double rope_base, int rope_pairing, hipStream_t stream);
+                            const int32_t* positions, double rope_base, int rope_pairing,
+                            hipStream_t stream);
 
 /*
  * gqa_prefill_split — gqa_prefill_chunk with long key ranges split across
@@ -190,7 +192,8 @@ la_status gqa_prefill_split(const void* q, const void* k, const void* v, void* o
                             const int64_t q_strides[3], const int64_t k_strides[3],
                             const int64_t v_strides[3], const int64_t o_strides[3],
                             const int32_t* cu_docs, int n_docs, float softmax_scale,
-                            const int32_t* positions, double rope_base, int rope_pairing, int split_tiles,
+                            const int32_t* positions, double rope_base, int rope_pairing,
+                            int split_tiles,
                             int max_splits, float* o_part, float* lse_part, hipStream_t stream);
 
 /*
@@ -222,7 +225,8 @@ la_status gqa_prefill_ring_step(const void* q, const void* k, const void* v, flo
                                 int k_off, int Hq, int Hkv, int D, const int64_t q_strides[3],
                                 const int64_t k_strides[3], const int64_t v_strides[3],
                                 const int32_t* cu_docs, int n_docs, float softmax_scale,
-                                const int32_t* positions, double rope_base, int rope_pairing, int first,
+                                const int32_t* positions, double rope_base, int rope_pairing,
+                                int first,
                                 hipStream_t stream);
 
 /*
