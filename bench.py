@@ -265,14 +265,46 @@ def setup_decode():
     return st
 
 
-def time_decode(st, steps: int, warmup: int, settle_s: float = 0.0):
+PAGE_SIZE = 64
+
+
+def page_decode_cache(st):
+    """The decode workload's caches as a pool of PAGE_SIZE-slot pages, each
+    page head-major ([n_pages, Hkv, PAGE_SIZE, D] in memory, passed as the
+    [n_pages, PAGE_SIZE, Hkv, D] view the call takes), in a seeded random
+    order, one block table row per sequence; the contiguous caches are freed."""
+    import torch
+    w, lens, dev = st["w"], st["lens"], st["q"].device
+    need = [-(-int(L) // PAGE_SIZE) for L in lens]
+    n_pages = int(sum(need))
+    order = np.random.default_rng(w.seed).permutation(n_pages)
+    table = np.zeros((w.B, -(-st["Lmax"] // PAGE_SIZE)), dtype=np.int32)
+    n = 0
+    for b in range(w.B):
+        table[b, :need[b]] = order[n:n + need[b]]
+        n += need[b]
+    del st["kc"], st["vc"]
+    torch.cuda.empty_cache()
+    g = torch.Generator(device=dev).manual_seed(w.seed + 1)
+    kp = torch.empty(n_pages, w.Hkv, PAGE_SIZE, w.D, dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    vp = torch.empty_like(kp).normal_(generator=g)
+    st["kp"], st["vp"] = kp.permute(0, 2, 1, 3), vp.permute(0, 2, 1, 3)
+    st["table"] = torch.as_tensor(table).to(dev)
+    torch.cuda.synchronize()
+
+
+def time_decode(st, steps: int, warmup: int, settle_s: float = 0.0, paged: bool = False):
     import torch
     import gqa_attention_rope_02_amd as la
 
     def step(evs=None):
         if evs:
             evs[0].record()
-        la.gqa_decode(st["q"], st["kc"], st["vc"], st["sl"], KV_CHUNK, st["op"], st["lp"])
+        if paged:
+            la.gqa_decode_paged(st["q"], st["kp"], st["vp"], st["table"], st["sl"], KV_CHUNK, st["op"],
+                                st["lp"], st["Lmax"])
+        else:
+            la.gqa_decode(st["q"], st["kc"], st["vc"], st["sl"], KV_CHUNK, st["op"], st["lp"])
         if evs:
             evs[1].record()
         la.gqa_decode_combine(st["op"], st["lp"], st["sl"], KV_CHUNK, st["o"])
@@ -492,6 +524,14 @@ def main():
                          "traffic": measured_traffic("gqa_decode", "decode405b", dhash),
                          "launch_ms": round(td["decode_ms"], 4)},
             "combine_ms": round(td["combine_ms"], 4)}
+        page_decode_cache(sd)
+        tp = time_decode(sd, args.steps, args.warmup, args.settle, paged=True)
+        gbp = nbytes / (tp["decode_ms"] * 1e-3) / 1e9
+        out["decode_405b_paged"] = {
+            "workload": f"the same decode over a paged cache: {PAGE_SIZE}-slot head-major pages of a pool "
+                        "in random order, one block table per sequence (gqa_decode_paged)",
+            "gbs": round(gbp, 1), "frac": round(gbp / PEAK_HBM_GBS, 4),
+            "decode_ms": round(tp["decode_ms"], 4), "ms_per_step": round(tp["ms_per_step"], 4)}
         if not (run_8b or run_405):
             out.update(value=round(gbs, 1), unit="GB/s", ms_per_step=round(td["ms_per_step"], 4),
                        config={"workload": out["decode_405b"]["workload"]},

@@ -35,6 +35,9 @@ contiguous):
 * ``gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk, o_part, lse_part,
   softmax_scale=0.0)``: q [B,Hq,D], caches [B,Hkv,Lmax,D], seq_lens int32 [B],
   o_part fp32 [B,Hq,max_splits,D], lse_part fp32 [B,Hq,max_splits].
+* ``gqa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, kv_chunk, o_part, lse_part,
+  Lmax, softmax_scale=0.0)``: as gqa_decode over a paged cache: pools [n_pages, page_size,
+  Hkv, D] (any page/slot/head strides), block_table int32 [B, pages per sequence].
 * ``gqa_decode_combine(o_part, lse_part, seq_lens, kv_chunk, o, lse=None)``:
   o [B,Hq,D] (bf16 or fp32), lse fp32 [B,Hq].
 """
@@ -47,7 +50,7 @@ from . import _lib
 
 __all__ = ["LlamaAttnError", "rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk",
            "gqa_prefill_split", "prefill_split_workspace", "gqa_prefill_ring_step",
-           "gqa_prefill_ring_finalize", "gqa_decode",
+           "gqa_prefill_ring_finalize", "gqa_decode", "gqa_decode_paged",
            "gqa_decode_combine", "version", "LA_BF16", "LA_FP32"]
 
 LA_BF16, LA_FP32 = 0, 1
@@ -301,6 +304,28 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk: int, o_part, lse_part,
         _i32(seq_lens), B, Hq, Hkv, D, Lmax, int(kv_chunk), max_splits, float(softmax_scale),
         _f32c(o_part), _f32c(lse_part), _stream())
     _check(st, "gqa_decode")
+
+
+def gqa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, kv_chunk: int, o_part, lse_part,
+                     Lmax: int, softmax_scale: float = 0.0):
+    B, Hq, D = q.shape
+    n_pages, page_size, Hkv, Dk = k_pages.shape
+    if k_pages.stride() != v_pages.stride() or tuple(k_pages.shape) != tuple(v_pages.shape):
+        raise ValueError("gqa_decode_paged: k_pages and v_pages must share shape and strides")
+    max_splits = o_part.shape[2]
+    if Dk != D or tuple(o_part.shape) != (B, Hq, max_splits, D) \
+            or tuple(lse_part.shape) != (B, Hq, max_splits) or tuple(seq_lens.shape) != (B,) \
+            or block_table.dim() != 2 or block_table.shape[0] != B or block_table.stride(1) != 1:
+        raise ValueError("gqa_decode_paged: inconsistent shapes")
+    ps = k_pages.stride()
+    if ps[-1] != 1:
+        raise ValueError("the last (head_dim) dimension must be contiguous")
+    page_strides = _lib.i64_array((ps[0], ps[2], ps[1]))   # (page, head, slot)
+    st = _lib.load().gqa_decode_paged(
+        _dev(q), _strides(q, 2), _dev(k_pages), _dev(v_pages), page_strides, page_size,
+        _i32(block_table), block_table.stride(0), _i32(seq_lens), B, Hq, Hkv, D, int(Lmax),
+        int(kv_chunk), max_splits, float(softmax_scale), _dev(o_part), _dev(lse_part), _stream())
+    _check(st, "gqa_decode_paged")
 
 
 def gqa_decode_combine(o_part, lse_part, seq_lens, kv_chunk: int, o, lse=None):

@@ -39,6 +39,8 @@ SIGNATURES = {
     "gqa_prefill_ring_finalize": ([_vp, _vp, _vp, _c_i64_p, _vp, _i, _i, _i, _i, _i, _vp], _i),
     "gqa_decode": ([_vp, _c_i64_p, _vp, _vp, _c_i64_p, _vp, _i, _i, _i, _i, _i, _i, _i,
                     ctypes.c_float, _vp, _vp, _vp], _i),
+    "gqa_decode_paged": ([_vp, _c_i64_p, _vp, _vp, _c_i64_p, _i, _vp, _i, _vp, _i, _i, _i, _i,
+                          _i, _i, _i, ctypes.c_float, _vp, _vp, _vp], _i),
     "gqa_decode_combine": ([_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _c_i64_p, _vp, _i, _vp], _i),
 }
 

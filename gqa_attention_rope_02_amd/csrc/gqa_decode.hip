@@ -23,6 +23,9 @@
 //   waves never wait on each other; a buffer descriptor ends at the split's
 //   last valid row, so rows past it read as zero, and the stream continues
 //   across splits and runs, so it never drains between them;
+// * a paged cache (a pool of pages of 2^k slots and a block table per
+//   sequence) only changes a tile's address: its page comes from the table,
+//   read one tile ahead of the tile's issue;
 // * the g query heads of the group are the 16 columns of the MFMA tiles:
 //   S^T = K Q^T on the 16x16x32 MFMA, O^T += V^T P^T on the 16x16x16 MFMA with
 //   V^T read by the transposing ds_read_b64_tr_b16; every K/V byte loaded
@@ -88,7 +91,7 @@ struct Item {
   int b, kvh, s, ns, L, k0, k1, nt;   // ns: splits of sequence b; nt: tiles of the item
 };
 
-template <int D, int G>
+template <int D, int G, bool PAGED>
 __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   constexpr int CH = D / 8;            // 16-byte chunks per row
   constexpr int ROW = D * 2;           // bytes per row
@@ -220,13 +223,22 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   // ---- load cursor over the wave's tile stream --------------------------------
   int li = i0, lt = 0;
   Item lit = item_at(i0);
+  // paged cache: the page of the cursor's tile, loaded one issue ahead so its
+  // latency overlaps a tile's work (a 16-key tile never crosses a page)
+  const int page_mask = (1 << a.page_shift) - 1;
+  int pg = 0;
+  auto page_of = [&](const Item& it, int t) -> int {
+    return a.block_table[(int64_t)it.b * a.bt_stride + ((it.k0 + t * kKT) >> a.page_shift)];
+  };
+  if constexpr (PAGED) pg = page_of(lit, 0);
   auto issue = [&](int st) {
     const __bf16* kb = static_cast<const __bf16*>(a.k);
     const __bf16* vb = static_cast<const __bf16*>(a.v);
     int bytes = 0;   // past the stream end: loads that read nothing keep the count uniform
     if (li < i1) {
       const int key = lit.k0 + lt * kKT;
-      const int64_t base = lit.b * a.cs_b + lit.kvh * a.cs_h + (int64_t)key * a.cs_l;
+      const int64_t base = PAGED ? (int64_t)pg * a.cs_b + lit.kvh * a.cs_h + (int64_t)(key & page_mask) * a.cs_l
+                                 : lit.b * a.cs_b + lit.kvh * a.cs_h + (int64_t)key * a.cs_l;
       kb += base;
       vb += base;
       const int rows = min(kKT, lit.k1 - key);
@@ -236,6 +248,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         lt = 0;
         if (li < i1) next_item(lit);
       }
+      if constexpr (PAGED)
+        if (li < i1) pg = page_of(lit, lt);
     }
     char* dst = my + st * 2 * TB;
 #pragma unroll
@@ -387,7 +401,10 @@ hipError_t launch_dt(const DecodeArgs& a, hipStream_t st) {
   }
   // persistent grid: one workgroup per CU (the LDS ring takes most of a CU's LDS)
   const unsigned grid = (unsigned)g_num_cu;
-  hipLaunchKernelGGL((decode_kernel<D, G>), dim3(grid), dim3(64 * kWaves), 0, st, a);
+  if (a.block_table)
+    hipLaunchKernelGGL((decode_kernel<D, G, true>), dim3(grid), dim3(64 * kWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, G, false>), dim3(grid), dim3(64 * kWaves), 0, st, a);
   return hipGetLastError();
 }
 

@@ -72,6 +72,11 @@ struct DecodeArgs {
   float scale;
   float* o_part;              // [B, Hq, max_splits, D]
   float* lse_part;            // [B, Hq, max_splits]
+  // paged cache (block_table non-null): key j of sequence b sits in page
+  // block_table[b * bt_stride + (j >> page_shift)], slot j & (2^page_shift - 1);
+  // cs_b is then the page stride
+  const int32_t* block_table;
+  int bt_stride, page_shift;
 };
 
 struct CombineArgs {

@@ -263,11 +263,13 @@ la_status gqa_prefill_ring_finalize(const float* o_acc, const float* lse_acc, vo
   return launched(la::launch_prefill_merge(a, D, dt == LA_BF16 ? 0 : 1, stream));
 }
 
-la_status gqa_decode(const void* q, const int64_t q_strides[2], const void* k_cache,
-                     const void* v_cache, const int64_t cache_strides[3],
-                     const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int Lmax,
-                     int kv_chunk, int max_splits, float softmax_scale, float* o_part,
-                     float* lse_part, hipStream_t stream) {
+namespace {
+
+la_status decode_check(const void* q, const int64_t q_strides[2], const void* k_cache,
+                       const void* v_cache, const int64_t cache_strides[3],
+                       const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int Lmax,
+                       int kv_chunk, int max_splits, float softmax_scale, float* o_part,
+                       float* lse_part) {
   if (!q || !k_cache || !v_cache || !seq_lens || !o_part || !lse_part) return LA_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || Lmax < 1 || max_splits < 1) return LA_ERR_INVALID_ARG;
   if (kv_chunk < 64 || kv_chunk % 64 != 0) return LA_ERR_INVALID_ARG;
@@ -286,8 +288,15 @@ la_status gqa_decode(const void* q, const int64_t q_strides[2], const void* k_ca
   // (32-bit buffer range)
   if (cache_strides[2] < D) return LA_ERR_INVALID_ARG;
   if (cache_strides[2] > (1LL << 24)) return LA_ERR_UNSUPPORTED;
-  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+  return LA_OK;
+}
 
+la::DecodeArgs decode_args(const void* q, const int64_t q_strides[2], const void* k_cache,
+                           const void* v_cache, const int64_t cache_strides[3],
+                           const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int Lmax,
+                           int kv_chunk, int max_splits, float softmax_scale, float* o_part,
+                           float* lse_part) {
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
   la::DecodeArgs a{};
   a.q = q; a.qs_b = q_strides[0]; a.qs_h = q_strides[1];
   a.k = k_cache; a.v = v_cache;
@@ -297,6 +306,51 @@ la_status gqa_decode(const void* q, const int64_t q_strides[2], const void* k_ca
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.o_part = o_part; a.lse_part = lse_part;
+  return a;
+}
+
+}  // namespace
+
+la_status gqa_decode(const void* q, const int64_t q_strides[2], const void* k_cache,
+                     const void* v_cache, const int64_t cache_strides[3],
+                     const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int Lmax,
+                     int kv_chunk, int max_splits, float softmax_scale, float* o_part,
+                     float* lse_part, hipStream_t stream) {
+  const la_status st = decode_check(q, q_strides, k_cache, v_cache, cache_strides, seq_lens, B, Hq,
+                                    Hkv, D, Lmax, kv_chunk, max_splits, softmax_scale, o_part,
+                                    lse_part);
+  if (st != LA_OK) return st;
+  const la::DecodeArgs a = decode_args(q, q_strides, k_cache, v_cache, cache_strides, seq_lens, B,
+                                       Hq, Hkv, D, Lmax, kv_chunk, max_splits, softmax_scale,
+                                       o_part, lse_part);
+  return launched(la::launch_decode(a, D, Hq / Hkv, stream));
+}
+
+la_status gqa_decode_paged(const void* q, const int64_t q_strides[2], const void* k_pages,
+                           const void* v_pages, const int64_t page_strides[3], int page_size,
+                           const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
+                           int B, int Hq, int Hkv, int D, int Lmax, int kv_chunk, int max_splits,
+                           float softmax_scale, float* o_part, float* lse_part,
+                           hipStream_t stream) {
+  if (!block_table || !k_pages || !v_pages) return LA_ERR_INVALID_ARG;
+  if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+    return LA_ERR_INVALID_ARG;
+  if (Lmax < 1 || bt_stride < (Lmax + page_size - 1) / page_size) return LA_ERR_INVALID_ARG;
+  if (!strides_ok(page_strides, 3, 2)) return LA_ERR_INVALID_ARG;
+  // the checks and arguments of the contiguous call, with the page stride in
+  // place of the sequence stride
+  const int64_t cache_strides[3] = {page_strides[0], page_strides[1], page_strides[2]};
+  la_status st = decode_check(q, q_strides, k_pages, v_pages, cache_strides, seq_lens, B, Hq, Hkv,
+                              D, Lmax, kv_chunk, max_splits, softmax_scale, o_part, lse_part);
+  if (st != LA_OK) return st;
+  la::DecodeArgs a = decode_args(q, q_strides, k_pages, v_pages, cache_strides, seq_lens, B, Hq,
+                                 Hkv, D, Lmax, kv_chunk, max_splits, softmax_scale, o_part,
+                                 lse_part);
+  a.block_table = block_table;
+  a.bt_stride = bt_stride;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  a.page_shift = shift;
   return launched(la::launch_decode(a, D, Hq / Hkv, stream));
 }
 

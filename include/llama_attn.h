@@ -276,6 +276,32 @@ la_status gqa_decode(const void* q, const int64_t q_strides[2],
                      float* o_part, float* lse_part, hipStream_t stream);
 
 /*
+ * gqa_decode_paged — gqa_decode over a paged KV cache (the serving layout:
+ * fixed-size pages from a shared pool, a block table per sequence) [P2].
+ *
+ * k_pages, v_pages: bf16 pools of pages, page p holding page_size slots of
+ *   every KV head, with strides page_strides = (page, h, slot) shared by both
+ *   (D <= slot stride <= 2^24).
+ * block_table: int32 [B, bt_stride] on the device: key j of sequence b (slot
+ *   j of its logical cache) is slot j % page_size of page
+ *   block_table[b][j / page_size]; entries for j < seq_lens[b] must name
+ *   pages of the pool (caller's contract, not checked).
+ * page_size: a power of two >= 16 (a 16-key tile never crosses a page);
+ *   bt_stride >= ceil(Lmax / page_size).
+ * Everything else (q, seq_lens, splits, o_part/lse_part workspace, the merge
+ * by gqa_decode_combine) as gqa_decode; the results equal gqa_decode's on the
+ * same logical cache bit for bit.
+ * Errors: those of gqa_decode; INVALID_ARG for a null table or pool, a
+ * page_size that is not a power of two >= 16, bt_stride too small.
+ */
+la_status gqa_decode_paged(const void* q, const int64_t q_strides[2], const void* k_pages,
+                           const void* v_pages, const int64_t page_strides[3], int page_size,
+                           const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
+                           int B, int Hq, int Hkv, int D, int Lmax, int kv_chunk, int max_splits,
+                           float softmax_scale, float* o_part, float* lse_part,
+                           hipStream_t stream);
+
+/*
  * gqa_decode_combine — merge the split partials of gqa_decode by their
  * log-sum-exp weights: with M = max_s lse_s and w_s = exp(lse_s - M),
  * o = sum_s w_s o_s / sum_s w_s and lse = M + ln(sum_s w_s), over the slots

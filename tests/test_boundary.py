@@ -32,8 +32,8 @@ def lib():
 def test_header_declares_every_call():
     names = declared_functions()
     for n in ("rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk", "gqa_prefill_split",
-              "gqa_prefill_ring_step", "gqa_prefill_ring_finalize", "gqa_decode", "gqa_decode_combine",
-              "la_status_str", "la_version"):
+              "gqa_prefill_ring_step", "gqa_prefill_ring_finalize", "gqa_decode", "gqa_decode_paged",
+              "gqa_decode_combine", "la_status_str", "la_version"):
         assert n in names
 
 
@@ -172,6 +172,24 @@ def test_ring_finalize_rejects(lib, kw, status):
     assert lib.gqa_prefill_ring_finalize(args["oa"], args["la"], args["o"], args["os_"], args["lse"],
                                          args["dt"], args["B"], args["Sq"], args["Hq"], args["D"],
                                          None) == status
+
+
+def decode_paged(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, ps=16, bt=FAKE, bts=63, sl=FAKE, B=2, Hq=16, Hkv=1, D=128,
+                Lmax=1000, chunk=256, ms=4, op=FAKE, lp=FAKE)
+    args.update(kw)
+    return lib.gqa_decode_paged(args["q"], S2, args["k"], args["v"], S3, args["ps"], args["bt"],
+                                args["bts"], args["sl"], args["B"], args["Hq"], args["Hkv"], args["D"],
+                                args["Lmax"], args["chunk"], args["ms"], 0.0, args["op"], args["lp"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), INVALID), (dict(k=None), INVALID), (dict(ps=8), INVALID), (dict(ps=48), INVALID),
+    (dict(ps=0), INVALID), (dict(bts=62), INVALID), (dict(chunk=100), INVALID), (dict(ms=3), INVALID),
+    (dict(D=96), UNSUPPORTED), (dict(B=2000), UNSUPPORTED), (dict(q=None), INVALID),
+])
+def test_decode_paged_rejects(lib, kw, status):
+    assert decode_paged(lib, **kw) == status
 
 
 def rope(lib, **kw):
