@@ -21,6 +21,10 @@ and every step is the textbook definition, written out:
    of the same "Deliberately Standard Dense Transformer" entry).
 4. Exact softmax per row: m_i = max_j s_ij, p_ij = exp(s_ij - m_i) / l_i with
    l_i = sum_j exp(s_ij - m_i); O_i = sum_j p_ij v_j, LSE_i = m_i + ln l_i.
+5. Backward (the training step's gradient pass under the same masks): the
+   chain rule through steps 2-4 for a given output gradient dO; the pages fix
+   the forward only, so the gradients are the plain derivatives of it, pinned
+   by finite differences and by a library's automatic differentiation.
 
 Rows are processed in blocks only to bound memory; each row's softmax is
 computed in one pass over all of its keys, and keys outside the union of the
@@ -218,6 +222,49 @@ def decode(q_rot, k_cache, v_cache, seq_lens, scale: Optional[float] = None
             O[b, heads] = (e @ vb[kv, :L]) / l
             LSE[b, heads] = (m + np.log(l))[:, 0]
     return O, LSE
+
+
+def attention_backward(qr, kr, v, dO, cu_docs=None, scale: Optional[float] = None
+                       ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of L = sum(dO * O) for ``attention`` (rotated queries and
+    keys, same mask and GQA head mapping): the chain rule through the softmax
+    written out. With P the row-softmax of S = qr kr^T * scale over the
+    visible keys and O = P v:
+      dv_j  = sum_i P_ij dO_i                  (summed over the g query heads
+                                                 of the KV head as well)
+      dP_ij = dO_i . v_j
+      dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)  (the softmax Jacobian)
+      dq_i  = scale sum_j dS_ij kr_j
+      dkr_j = scale sum_i dS_ij qr_i           (summed over the g heads)
+    qr, dO [B,S,Hq,D]; kr, v [B,S,Hkv,D]. Returns (dq, dk, dv) in fp64 with
+    the shapes of qr, kr, v; gradients with respect to the unrotated queries
+    and keys follow by rotating back (``rope`` at the negated positions).
+    """
+    qr, kr, v, dO = _f64(qr), _f64(kr), _f64(v), _f64(dO)
+    B, S, Hq, D = qr.shape
+    Hkv = kr.shape[2]
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    cu = np.asarray([0, S] if cu_docs is None else cu_docs, dtype=np.int64)
+    doc = document_of(cu, S)
+    i = np.arange(S)
+    visible = (i[None, :] <= i[:, None]) & (doc[None, :] == doc[:, None])   # [query, key]
+    dq = np.zeros_like(qr)
+    dk = np.zeros_like(kr)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // g
+            s = np.where(visible, qr[b, :, h] @ kr[b, :, kv].T * scale, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            P = e / e.sum(axis=1, keepdims=True)
+            dv[b, :, kv] += P.T @ dO[b, :, h]
+            dP = dO[b, :, h] @ v[b, :, kv].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dq[b, :, h] = scale * dS @ kr[b, :, kv]
+            dk[b, :, kv] += scale * dS.T @ qr[b, :, h]
+    return dq, dk, dv
 
 
 def decode_partials(q_rot, k_cache, v_cache, seq_lens, kv_chunk: int, max_splits: int,

@@ -69,7 +69,42 @@ def _rope_half_is_adjacent(x, positions, base=500000.0, pairing="adjacent"):
     return _real_rope(x, positions, base, "adjacent")
 
 
+def _backward_variant(no_row_term=False, overwrite_heads=False, dq_unscaled=False, dk_from_keys=False):
+    """A copy of the oracle's attention_backward with one slip switched on."""
+    def attention_backward(qr, kr, v, dO, cu_docs=None, scale=None):
+        qr, kr, v, dO = (orc._f64(x) for x in (qr, kr, v, dO))
+        B, S, Hq, D = qr.shape
+        g = Hq // kr.shape[2]
+        sc = 1.0 / math.sqrt(D) if scale is None else scale
+        cu = np.asarray([0, S] if cu_docs is None else cu_docs)
+        doc = orc.document_of(cu, S)
+        i = np.arange(S)
+        vis = (i[None, :] <= i[:, None]) & (doc[None, :] == doc[:, None])
+        dq, dk, dv = np.zeros_like(qr), np.zeros_like(kr), np.zeros_like(v)
+        for b in range(B):
+            for h in range(Hq):
+                kv = h // g
+                s = np.where(vis, qr[b, :, h] @ kr[b, :, kv].T * sc, -np.inf)
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                P = e / e.sum(axis=1, keepdims=True)
+                dP = dO[b, :, h] @ v[b, :, kv].T
+                dS = P * dP if no_row_term else P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                if overwrite_heads:
+                    dv[b, :, kv] = P.T @ dO[b, :, h]
+                    dk[b, :, kv] = sc * dS.T @ qr[b, :, h]
+                else:
+                    dv[b, :, kv] += P.T @ dO[b, :, h]
+                    dk[b, :, kv] += sc * dS.T @ (kr[b, :, kv] if dk_from_keys else qr[b, :, h])
+                dq[b, :, h] = (1.0 if dq_unscaled else sc) * dS @ kr[b, :, kv]
+        return dq, dk, dv
+    return attention_backward
+
+
 MUTATIONS = {
+    "backward drops the softmax row term": ("attention_backward", _backward_variant(no_row_term=True)),
+    "backward keeps one head per KV head": ("attention_backward", _backward_variant(overwrite_heads=True)),
+    "backward dq without the scale": ("attention_backward", _backward_variant(dq_unscaled=True)),
+    "backward dk from the keys": ("attention_backward", _backward_variant(dk_from_keys=True)),
     "kv head h % Hkv": ("attention", _attention_variant(kv_map=lambda h, g, Hkv: h % Hkv)),
     "strict causal j < i": ("attention", _attention_variant(strict=True)),
     "mask leaks across documents": ("attention", _attention_variant(leak=True)),
@@ -98,6 +133,8 @@ PIN_CALLS = [
     pins.test_rope_half_pairing_is_adjacent_pairing_under_a_channel_permutation,
     pins.test_rope_half_unit_vector,
     pins.test_attention_with_half_pairing_equals_permuted_adjacent,
+    pins.test_backward_matches_finite_differences,
+    pins.test_backward_matches_autograd_of_sdpa,
 ]
 
 
