@@ -139,6 +139,37 @@ def time_prefill(st, steps: int, warmup: int, settle_s: float = 0.0):
                 prefill_ms_median=float(np.median(attn_ms)))
 
 
+def time_backward(st, steps: int, warmup: int, settle_s: float = 0.0):
+    """gqa_attention_backward on the workload (rotated q and k, the forward's o
+    and lse computed once beforehand, seeded N(0,1) output gradient)."""
+    import torch
+    import gqa_attention_rope_02_amd as la
+    from workloads import draw_grad_output
+    w = st["w"]
+    la.rope_qk(st["q"], st["qr"], st["k"], st["kr"])
+    la.gqa_prefill(st["qr"], st["kr"], st["v"], st["o"], st["lse"], st["cu_d"])
+    dout = draw_grad_output(w.B, w.S, w.Hq, w.D, w.dtype, w.seed).to(st["q"].device)
+    dq, dk, dv = torch.empty_like(st["q"]), torch.empty_like(st["k"]), torch.empty_like(st["v"])
+    delta = torch.empty_like(st["lse"])
+
+    def step():
+        la.gqa_attention_backward(st["qr"], st["kr"], st["v"], st["o"], dout, st["lse"], dq, dk, dv,
+                                  delta, st["cu_d"])
+
+    settle(step, settle_s)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in evs]
+    return dict(backward_ms=float(np.mean(ms)), backward_ms_median=float(np.median(ms)))
+
+
 def prefill_flops(w, cu) -> float:
     return 4.0 * w.D * w.Hq * w.B * allowed_pairs(cu)
 
@@ -397,7 +428,7 @@ def main():
     ap.add_argument("--settle", type=float, default=0.3,
                     help="seconds of untimed whole steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "llama8b", "llama405b", "decode405b", "copy"],
+    ap.add_argument("--only", choices=["prefill", "decode", "llama8b", "llama405b", "decode405b", "copy", "backward"],
                     default=None, help="run one part: both prefills, the decode, one workload, "
                                        "or only the copy used to scale HBM counters")
     ap.add_argument("--with-128k", action="store_true", help="also time the S=131072 prefill")
@@ -429,6 +460,15 @@ def main():
         if args.only == "copy":
             out.update(value=out["copy_calibration"]["gbs"], unit="GB/s",
                        config={"workload": "plain device copy of 1 GiB"})
+
+    if args.only == "backward":
+        st, _ = setup_prefill("llama8b")
+        tb = time_backward(st, args.steps, args.warmup, args.settle)
+        flb = 10.0 * st["w"].D * st["w"].Hq * st["w"].B * allowed_pairs(st["cu"])
+        tf = flb / (tb["backward_ms"] * 1e-3) / 1e12
+        out.update(value=round(tf, 2), unit="TFLOP/s", ms_per_step=round(tb["backward_ms"], 4),
+                   config={"workload": "llama-3.1-8b attention layer backward (gqa_attention_backward)"},
+                   frac=round(tf / PEAK_BF16_TFLOPS, 4))
 
     if run_8b:
         st, host = setup_prefill("llama8b")
@@ -466,6 +506,16 @@ def main():
             "chunk_ms": round(tc["chunk_ms"], 4), "rope_ms": round(tc["rope_ms"], 4),
             "unsplit_chunk_ms": round(tu["chunk_ms"], 4),
             "unsplit_tflops_kernel": round(flc / (tu["chunk_ms"] * 1e-3) / 1e12, 2)}
+        tb = time_backward(st, max(args.steps // 4, 5), max(args.warmup // 2, 2), args.settle)
+        flb = 10.0 * w.D * w.Hq * w.B * allowed_pairs(cu)
+        out["backward_8b"] = {
+            "workload": "llama-3.1-8b attention layer backward: gqa_attention_backward (delta, "
+                        "key-stationary dk/dv, query-stationary dq) on the prefill's shapes and documents",
+            "flops": flb, "flops_note": "5 products per visible pair (10 D per pair and head); "
+                                        "the kernels run 7 (S and dP are recomputed for dq)",
+            "tflops": round(flb / (tb["backward_ms"] * 1e-3) / 1e12, 2),
+            "frac": round(flb / (tb["backward_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "backward_ms": round(tb["backward_ms"], 4)}
         if not args.no_cpu_baseline:
             log("timing the fp64 oracle on a row sample ...")
             out["cpu_baseline"] = cpu_baseline(host, w, cu)

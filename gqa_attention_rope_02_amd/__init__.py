@@ -12,6 +12,9 @@ contiguous):
   rope_pairing="adjacent")``: q [B,S,Hq,D], k [B,S,Hkv,D] (either pair may be None);
   positions int32 [B,S]; rope_pairing "adjacent" (channels 2k, 2k+1) or "half"
   (k, k+D/2), also taken by every call below that takes rope_base.
+* ``rope_qk_backward(dq_in, dq_out, dk_in=None, dk_out=None, positions=None,
+  rope_base=500000.0, rope_pairing="adjacent")``: the transpose of rope_qk (rotation
+  by minus the angles): gradients for rotated q/k to gradients for the inputs.
 * ``gqa_prefill(q, k, v, o, lse=None, cu_docs=None, softmax_scale=0.0)``:
   q/o [B,S,Hq,D], k/v [B,S,Hkv,D], cu_docs int32 [B, n_docs+1], lse fp32 [B,Hq,S].
 * ``gqa_prefill_rope(q, k, v, o, lse=None, cu_docs=None, softmax_scale=0.0,
@@ -32,6 +35,11 @@ contiguous):
   q_off.. against a key shard k/v [B,Skv,Hkv,D] at positions k_off..; writes (first) or
   merges the shard's result into o_acc fp32 [B,Sq,Hq,D], lse_acc fp32 [B,Hq,Sq].
 * ``gqa_prefill_ring_finalize(o_acc, lse_acc, o, lse=None)``: o [B,Sq,Hq,D] from them.
+* ``gqa_attention_backward(q, k, v, o, dout, lse, dq, dk, dv, delta=None, cu_docs=None,
+  softmax_scale=0.0, workspace="auto")``: gradients of gqa_prefill (bf16): q, o, dout, dq
+  [B,S,Hq,D]; k, v, dk, dv [B,S,Hkv,D]; lse fp32 [B,Hq,S] from the forward; delta fp32
+  [B,Hq,S] workspace (allocated when None); workspace: ``backward_workspace(B, S, Hkv, D)``
+  (allocated when "auto"; None runs without cutting long query ranges).
 * ``gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk, o_part, lse_part,
   softmax_scale=0.0)``: q [B,Hq,D], caches [B,Hkv,Lmax,D], seq_lens int32 [B],
   o_part fp32 [B,Hq,max_splits,D], lse_part fp32 [B,Hq,max_splits].
@@ -48,7 +56,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["LlamaAttnError", "rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk",
+__all__ = ["LlamaAttnError", "rope_qk", "rope_qk_backward", "gqa_attention_backward", "backward_workspace", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk",
            "gqa_prefill_split", "prefill_split_workspace", "gqa_prefill_ring_step",
            "gqa_prefill_ring_finalize", "gqa_decode", "gqa_decode_paged",
            "gqa_decode_combine", "version", "LA_BF16", "LA_FP32"]
@@ -148,6 +156,66 @@ def rope_qk(q_in, q_out, k_in=None, k_out=None, positions=None, rope_base: float
         _dtype(ref), B, S, Hq, Hkv, D, _i32(positions), float(rope_base), _pairing(rope_pairing),
         _stream())
     _check(st, "rope_qk")
+
+
+def rope_qk_backward(dq_in, dq_out, dk_in=None, dk_out=None, positions=None,
+                     rope_base: float = 500000.0, rope_pairing: str = "adjacent"):
+    ref = dq_in if dq_in is not None else dk_in
+    B, S, _, D = ref.shape
+    Hq = dq_in.shape[2] if dq_in is not None else 0
+    Hkv = dk_in.shape[2] if dk_in is not None else 0
+    _same_shape("rope_qk_backward", (dq_in, dq_out), (dk_in, dk_out))
+    if dq_in is not None and dk_in is not None and (dk_in.shape[:2] != dq_in.shape[:2] or dk_in.shape[3] != D):
+        raise ValueError("rope_qk_backward: dq and dk must share B, S and D")
+    if positions is not None and tuple(positions.shape) != (B, S):
+        raise ValueError("rope_qk_backward: positions must be [B, S]")
+    st = _lib.load().rope_qk_backward(
+        _dev(dq_in), _dev(dq_out), _strides(dq_in, 3), _strides(dq_out, 3),
+        _dev(dk_in), _dev(dk_out), _strides(dk_in, 3), _strides(dk_out, 3),
+        _dtype(ref), B, S, Hq, Hkv, D, _i32(positions), float(rope_base), _pairing(rope_pairing),
+        _stream())
+    _check(st, "rope_qk_backward")
+
+
+BWD_PIECES = 4   # LA_BWD_PIECES
+
+
+def backward_workspace(B: int, S: int, Hkv: int, D: int, device=None):
+    """The fp32 workspace gqa_attention_backward cuts long query ranges with."""
+    return torch.empty((BWD_PIECES, B, S, Hkv, 2, D), dtype=torch.float32, device=device)
+
+
+def gqa_attention_backward(q, k, v, o, dout, lse, dq, dk, dv, delta=None, cu_docs=None,
+                           softmax_scale: float = 0.0, workspace="auto"):
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    n_docs = cu_docs.shape[-1] - 1 if cu_docs is not None else 1
+    _same_shape("gqa_attention_backward", (q, o), (q, dout), (q, dq), (k, v), (k, dk), (k, dv))
+    if tuple(k.shape) != (B, S, Hkv, D):
+        raise ValueError("gqa_attention_backward: k/v must be [B, S, Hkv, D]")
+    if tuple(lse.shape) != (B, Hq, S):
+        raise ValueError("gqa_attention_backward: lse must be [B, Hq, S]")
+    if delta is None:
+        delta = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    if tuple(delta.shape) != (B, Hq, S):
+        raise ValueError("gqa_attention_backward: delta must be [B, Hq, S]")
+    if cu_docs is not None and (cu_docs.dim() != 2 or cu_docs.shape[0] != B):
+        raise ValueError("gqa_attention_backward: cu_docs must be [B, n_docs + 1]")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("gqa_attention_backward: workspace must be a tensor, None or 'auto'")
+        workspace = backward_workspace(B, S, Hkv, D, q.device)
+    if workspace is not None and (workspace.numel() != BWD_PIECES * B * S * Hkv * 2 * D
+                                  or workspace.dtype != torch.float32):
+        raise ValueError("gqa_attention_backward: workspace must be fp32 with "
+                         "BWD_PIECES*B*S*Hkv*2*D elements")
+    st = _lib.load().gqa_attention_backward(
+        _dev(q), _dev(k), _dev(v), _dev(o), _dev(dout), _f32c(lse), _f32c(delta),
+        _dev(dq), _dev(dk), _dev(dv), _dtype(q), B, S, Hq, Hkv, D,
+        _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3), _strides(dout, 3),
+        _strides(dq, 3), _strides(dk, 3), _strides(dv, 3),
+        _i32(cu_docs), n_docs, float(softmax_scale), _f32c(workspace), _stream())
+    _check(st, "gqa_attention_backward")
 
 
 def gqa_prefill(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float = 0.0):

@@ -22,6 +22,10 @@ SIGNATURES = {
     "la_version": ([], _i),
     "rope_qk": ([_vp, _vp, _c_i64_p, _c_i64_p, _vp, _vp, _c_i64_p, _c_i64_p, _i,
                  _i, _i, _i, _i, _i, _vp, ctypes.c_double, _i, _vp], _i),
+    "rope_qk_backward": ([_vp, _vp, _c_i64_p, _c_i64_p, _vp, _vp, _c_i64_p, _c_i64_p, _i,
+                          _i, _i, _i, _i, _i, _vp, ctypes.c_double, _i, _vp], _i),
+    "gqa_attention_backward": ([_vp] * 10 + [_i, _i, _i, _i, _i, _i] + [_c_i64_p] * 8
+                               + [_vp, _i, ctypes.c_float, _vp, _vp], _i),
     "gqa_prefill": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                      _c_i64_p, _c_i64_p, _c_i64_p, _c_i64_p, _vp, _i, ctypes.c_float, _vp], _i),
     "gqa_prefill_rope": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libllama_attn.so")
-SOURCES = ["rope_qk.hip", "gqa_prefill.hip", "gqa_decode.hip", "llama_attn.cpp"]
+SOURCES = ["rope_qk.hip", "gqa_prefill.hip", "gqa_decode.hip", "gqa_backward.hip", "llama_attn.cpp"]
 ARCH = os.environ.get("LLAMA_ATTN_ARCH", "gfx950")
 
 

@@ -75,6 +75,41 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
   *reinterpret_cast<f32x4*>(p) = r;
 }
 
+// -------------------------------------------------------------------- LDS
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+using lds_void = __attribute__((address_space(3))) void;
+using lds_i16x4 = __attribute__((address_space(3))) i16x4;
+
+constexpr int kRsrcWord3 = 0x00020000;   // buffer descriptor word 3 (raw, no swizzle)
+
+// Physical 16-byte chunk of logical chunk c in row r of a tile read as rows
+// (ds_read_b128 of one chunk per lane).
+template <int CH>
+__device__ __forceinline__ int k_chunk(int c, int r) { return c ^ (r & (CH - 1)); }
+// Tiles also read with the transposing ds_read_b64_tr_b16: rows 1 apart are
+// spread by 4 chunks (64 bytes), so one transposing read of 32 lanes (4
+// consecutive rows x two 32-byte halves of a 32-column block) touches every
+// bank of the 256-byte row once. An XOR with a row-only term is its own
+// inverse, which the loaders rely on.
+template <int CH>
+__device__ __forceinline__ int v_chunk(int c, int r) { return c ^ (CH == 16 ? 4 * (r & 3) : 2 * (r & 3)); }
+
+// One 16-byte-per-lane load from `base` into LDS: lane i's 16 bytes at byte
+// offset `voff` land at dst + 16 i; bytes at or past `bytes_valid` read as zero.
+__device__ __forceinline__ void load_lds16(const void* base, int bytes_valid, int voff, char* dst) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes_valid, kRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+// The same with 4 bytes per lane (lane i's dword lands at dst + 4 i).
+__device__ __forceinline__ void load_lds4(const void* base, int bytes_valid, int voff, char* dst) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes_valid, kRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, voff, 0, 0, 0);
+}
+
 // -------------------------------------------------------------------- MFMA
 
 // D(32x32) += A(32x16) * B(16x32). Lane l holds A[l%32][8*(l/32)+i] and
@@ -105,6 +140,17 @@ __device__ __forceinline__ int doc_start(const int32_t* row, int n, int t) {
     if (row[mid] <= t) lo = mid; else hi = mid;
   }
   return row[lo];
+}
+
+// One past the last token of the document holding token t: the first entry of
+// row[0..n] above t (row non-decreasing, row[n] > t).
+__device__ __forceinline__ int doc_end(const int32_t* row, int n, int t) {
+  int lo = 0, hi = n;  // invariant: row[lo] <= t < row[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (row[mid] <= t) lo = mid; else hi = mid;
+  }
+  return row[hi];
 }
 
 }  // namespace la

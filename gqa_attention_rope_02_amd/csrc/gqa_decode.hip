@@ -45,24 +45,7 @@ constexpr int kKT = 16;       // keys per wave tile
 constexpr int kNS = 4;        // LDS ring stages per wave
 constexpr int kWaves = 4;     // waves per workgroup
 constexpr float kLazy = 8.f;  // log2 headroom of the lazily moved softmax reference
-constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kMaxB = kDecodeMaxBatch;   // sequences per call (tables in LDS)
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-using lds_void = __attribute__((address_space(3))) void;
-using lds_i16x4 = __attribute__((address_space(3))) i16x4;
-
-template <int CH>
-__device__ __forceinline__ int k_chunk(int c, int r) { return c ^ (r & (CH - 1)); }
-template <int CH>
-__device__ __forceinline__ int v_chunk(int c, int r) { return c ^ (CH == 16 ? 4 * (r & 3) : 2 * (r & 3)); }
-
-__device__ __forceinline__ void load_lds16(const void* base, int bytes_valid, int voff, char* dst) {
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes_valid, kRsrcWord3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, 0, 0, 0);
-}
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

@@ -73,34 +73,10 @@ constexpr int kNW = 8;        // waves per workgroup
 constexpr int kCB = kCols / kNW / 32;   // 32-column blocks per wave
 constexpr int kKT = 64;       // keys per tile
 constexpr float kLazyW = 256.f;   // bound on a weight under the lazily moved softmax reference
-constexpr int kRsrcWord3 = 0x00020000;
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8; a field at its maximum does not wait)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kLgkm0 = 15 | (3 << 14) | (7 << 4);
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-using lds_void = __attribute__((address_space(3))) void;
-using lds_i16x4 = __attribute__((address_space(3))) i16x4;
-
-// Physical 16-byte chunk of logical chunk c in row r of a K tile / V tile.
-template <int CH>
-__device__ __forceinline__ int k_chunk(int c, int r) { return c ^ (r & (CH - 1)); }
-// V: rows 1 apart are spread by 4 chunks (64 bytes), so one transposing read
-// of 32 lanes (4 consecutive rows x two 32-byte halves of a 32-column block)
-// touches every bank of the 256-byte row once. An XOR with a row-only term is
-// its own inverse, which the loader relies on.
-template <int CH>
-__device__ __forceinline__ int v_chunk(int c, int r) { return c ^ (CH == 16 ? 4 * (r & 3) : 2 * (r & 3)); }
-
-// One 16-byte-per-lane load from `base` into LDS: lane i's 16 bytes at byte
-// offset `voff` land at dst + 16 i; bytes at or past `bytes_valid` read as zero.
-__device__ __forceinline__ void load_lds16(const void* base, int bytes_valid, int voff, char* dst) {
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes_valid, kRsrcWord3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff, 0, 0, 0);
-}
 
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

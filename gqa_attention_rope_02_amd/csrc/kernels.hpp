@@ -89,6 +89,37 @@ struct CombineArgs {
   float* lse;                 // [B, Hq] or null
 };
 
+// Gradient pass (bf16 tensors): q, k rotated; o, lse from the forward; dout
+// the output gradient; delta fp32 [B, Hq, S] a workspace (rowsum(dout o)).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;           // [B, Hq, S], natural log
+  float* delta;               // [B, Hq, S]
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t qs_b, qs_s, qs_h;
+  int64_t ks_b, ks_s, ks_h;
+  int64_t vs_b, vs_s, vs_h;
+  int64_t os_b, os_s, os_h;
+  int64_t gs_b, gs_s, gs_h;   // dout
+  int64_t dqs_b, dqs_s, dqs_h;
+  int64_t dks_b, dks_s, dks_h;
+  int64_t dvs_b, dvs_s, dvs_h;
+  const int32_t* cu_docs;     // [B, n_docs + 1] or null
+  int n_docs;
+  int B, S, Hq, Hkv;
+  float scale, scale_log2;
+  // key blocks with long query ranges split into kBwdPieces pieces, each
+  // writing fp32 partial dk, dv to its slot of dkv_part
+  // [kBwdPieces, B, S, Hkv, 2, D] (null: no split)
+  float* dkv_part;
+};
+
 // Launchers: return hipSuccess or the launch error. dt: 0 = bf16, 1 = fp32.
 hipError_t launch_rope_pair(const RopeArgs& q, const RopeArgs& k, const RopeAngles& ang, int D, int dt,
                             hipStream_t st);
@@ -99,6 +130,13 @@ constexpr int kDecodeMaxBatch = 1024;
 
 hipError_t launch_decode(const DecodeArgs& a, int D, int G, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int D, int dt, hipStream_t st);
+
+hipError_t launch_backward(const BwdArgs& a, int D, int G, hipStream_t st);
+// Keys per workgroup of the key-stationary gradient kernel (dk, dv) and
+// tokens per workgroup of the query-stationary one (dq).
+constexpr int kBwdKeysPerBlock = 128;
+constexpr int kBwdPieces = 4;
+constexpr int bwd_dq_tokens_per_block(int G) { return 256 / G; }
 
 // Tokens of one sequence handled by one prefill workgroup for group size G.
 constexpr int prefill_tokens_per_block(int G) { return 256 / G; }

@@ -3,6 +3,7 @@
 // the caller's stream. The library allocates nothing and keeps no state.
 #include "llama_attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -53,11 +54,15 @@ const char* la_status_str(la_status s) {
 
 int la_version(void) { return kVersion; }
 
-la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
-                  const int64_t q_out_strides[3], const void* k_in, void* k_out,
-                  const int64_t k_in_strides[3], const int64_t k_out_strides[3], la_dtype dt,
-                  int B, int S, int Hq, int Hkv, int D, const int32_t* positions,
-                  double rope_base, int rope_pairing, hipStream_t stream) {
+namespace {
+
+// rope_qk and rope_qk_backward: direction +1 rotates by the position's angles,
+// -1 by their negatives (the transpose of the rotation)
+la_status rope_impl(const void* q_in, void* q_out, const int64_t q_in_strides[3],
+                    const int64_t q_out_strides[3], const void* k_in, void* k_out,
+                    const int64_t k_in_strides[3], const int64_t k_out_strides[3], la_dtype dt,
+                    int B, int S, int Hq, int Hkv, int D, const int32_t* positions,
+                    double rope_base, int rope_pairing, int direction, hipStream_t stream) {
   if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
   const bool has_q = q_in != nullptr || q_out != nullptr;
   const bool has_k = k_in != nullptr || k_out != nullptr;
@@ -88,8 +93,33 @@ la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
   }
   la::RopeAngles ang{};
   theta_revolutions(rope_base, D, ang.theta_rev);
+  if (direction < 0)
+    for (int kk = 0; kk < D / 2; ++kk) ang.theta_rev[kk] = -ang.theta_rev[kk];
   ang.half = rope_pairing;
   return launched(la::launch_rope_pair(qa, ka, ang, D, dt == LA_BF16 ? 0 : 1, stream));
+}
+
+}  // namespace
+
+la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
+                  const int64_t q_out_strides[3], const void* k_in, void* k_out,
+                  const int64_t k_in_strides[3], const int64_t k_out_strides[3], la_dtype dt,
+                  int B, int S, int Hq, int Hkv, int D, const int32_t* positions,
+                  double rope_base, int rope_pairing, hipStream_t stream) {
+  return rope_impl(q_in, q_out, q_in_strides, q_out_strides, k_in, k_out, k_in_strides,
+                   k_out_strides, dt, B, S, Hq, Hkv, D, positions, rope_base, rope_pairing, 1,
+                   stream);
+}
+
+la_status rope_qk_backward(const void* dq_in, void* dq_out, const int64_t dq_in_strides[3],
+                           const int64_t dq_out_strides[3], const void* dk_in, void* dk_out,
+                           const int64_t dk_in_strides[3], const int64_t dk_out_strides[3],
+                           la_dtype dt, int B, int S, int Hq, int Hkv, int D,
+                           const int32_t* positions, double rope_base, int rope_pairing,
+                           hipStream_t stream) {
+  return rope_impl(dq_in, dq_out, dq_in_strides, dq_out_strides, dk_in, dk_out, dk_in_strides,
+                   dk_out_strides, dt, B, S, Hq, Hkv, D, positions, rope_base, rope_pairing, -1,
+                   stream);
 }
 
 namespace {
@@ -372,6 +402,68 @@ la_status gqa_decode_combine(const float* o_part, const float* lse_part, const i
   a.o = o; a.os_b = o_strides[0]; a.os_h = o_strides[1];
   a.lse = lse;
   return launched(la::launch_combine(a, D, dt == LA_BF16 ? 0 : 1, stream));
+}
+
+namespace {
+
+// the rows of q and dout are fetched as blocks of whole token rows: each
+// token's heads lie within its token stride, and block offsets fit in 32 bits
+bool bwd_rows_ok(const int64_t* st, int H, int D) {
+  return st[2] >= D && st[1] >= (int64_t)H * st[2] && 64 * st[1] + 16 * st[2] < (1LL << 29);
+}
+
+}  // namespace
+
+la_status gqa_attention_backward(const void* q, const void* k, const void* v, const void* o,
+                                 const void* dout, const float* lse, float* delta, void* dq,
+                                 void* dk, void* dv, la_dtype dt, int B, int S, int Hq, int Hkv,
+                                 int D, const int64_t q_strides[3], const int64_t k_strides[3],
+                                 const int64_t v_strides[3], const int64_t o_strides[3],
+                                 const int64_t dout_strides[3], const int64_t dq_strides[3],
+                                 const int64_t dk_strides[3], const int64_t dv_strides[3],
+                                 const int32_t* cu_docs, int n_docs, float softmax_scale,
+                                 float* dkv_workspace, hipStream_t stream) {
+  if (dt != LA_BF16) return LA_ERR_UNSUPPORTED;
+  if (dkv_workspace && !aligned16(dkv_workspace)) return LA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return LA_ERR_INVALID_ARG;
+  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return LA_ERR_INVALID_ARG;
+  if (cu_docs && n_docs < 1) return LA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return LA_ERR_INVALID_ARG;
+  if (!supported_d(D) || !supported_g(Hq / Hkv)) return LA_ERR_UNSUPPORTED;
+  if (!std::isfinite(softmax_scale)) return LA_ERR_INVALID_ARG;
+  for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(p)) return LA_ERR_INVALID_ARG;
+  for (const int64_t* st : {q_strides, k_strides, v_strides, o_strides, dout_strides, dq_strides,
+                            dk_strides, dv_strides})
+    if (!strides_ok(st, 3, 2)) return LA_ERR_INVALID_ARG;
+  if (!bwd_rows_ok(q_strides, Hq, D) || !bwd_rows_ok(dout_strides, Hq, D)) return LA_ERR_INVALID_ARG;
+  if (k_strides[1] < D || v_strides[1] < D) return LA_ERR_INVALID_ARG;
+  if (64 * k_strides[1] >= (1LL << 30) || 64 * v_strides[1] >= (1LL << 30)) return LA_ERR_INVALID_ARG;
+  const int G = Hq / Hkv;
+  if ((long long)G * S >= (1LL << 28)) return LA_ERR_INVALID_ARG;
+  const long long nkb = (S + la::kBwdKeysPerBlock - 1) / la::kBwdKeysPerBlock;
+  const long long tq = la::bwd_dq_tokens_per_block(G);
+  if ((long long)B * Hkv * std::max(nkb, (S + tq - 1) / tq) > 0x7fffffffLL) return LA_ERR_INVALID_ARG;
+  if ((long long)B * S * Hq > (1LL << 40)) return LA_ERR_INVALID_ARG;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+
+  la::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.delta = delta;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.qs_b = q_strides[0]; a.qs_s = q_strides[1]; a.qs_h = q_strides[2];
+  a.ks_b = k_strides[0]; a.ks_s = k_strides[1]; a.ks_h = k_strides[2];
+  a.vs_b = v_strides[0]; a.vs_s = v_strides[1]; a.vs_h = v_strides[2];
+  a.os_b = o_strides[0]; a.os_s = o_strides[1]; a.os_h = o_strides[2];
+  a.gs_b = dout_strides[0]; a.gs_s = dout_strides[1]; a.gs_h = dout_strides[2];
+  a.dqs_b = dq_strides[0]; a.dqs_s = dq_strides[1]; a.dqs_h = dq_strides[2];
+  a.dks_b = dk_strides[0]; a.dks_s = dk_strides[1]; a.dks_h = dk_strides[2];
+  a.dvs_b = dv_strides[0]; a.dvs_s = dv_strides[1]; a.dvs_h = dv_strides[2];
+  a.cu_docs = cu_docs; a.n_docs = cu_docs ? n_docs : 1;
+  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dkv_part = dkv_workspace;
+  return launched(la::launch_backward(a, D, G, stream));
 }
 
 }  // extern "C"

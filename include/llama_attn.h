@@ -59,6 +59,9 @@ typedef enum {
 
 typedef enum { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
 
+/* Pieces of a key block's query range in gqa_attention_backward. */
+#define LA_BWD_PIECES 4
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* la_status_str(la_status s);
 
@@ -317,6 +320,66 @@ la_status gqa_decode_combine(const float* o_part, const float* lse_part,
                              int kv_chunk, int max_splits,
                              void* o, const int64_t o_strides[2], float* lse,
                              la_dtype dt, hipStream_t stream);
+
+/*
+ * rope_qk_backward — the transpose of rope_qk: rotates each channel pair by
+ * minus the angle that rope_qk uses (same positions, rope_base, pairing), so
+ * that gradients with respect to rotated queries and keys become gradients
+ * with respect to the unrotated ones (the rotation is orthogonal) [P1].
+ * Arguments, layouts and errors as rope_qk, with dq/dk in place of q/k.
+ */
+la_status rope_qk_backward(const void* dq_in, void* dq_out, const int64_t dq_in_strides[3],
+                           const int64_t dq_out_strides[3],
+                           const void* dk_in, void* dk_out, const int64_t dk_in_strides[3],
+                           const int64_t dk_out_strides[3],
+                           la_dtype dt, int B, int S, int Hq, int Hkv, int D,
+                           const int32_t* positions, double rope_base, int rope_pairing,
+                           hipStream_t stream);
+
+/*
+ * gqa_attention_backward — gradients of gqa_prefill (the training step's
+ * backward pass) under the same mask and head mapping [P2, P4]: for a loss L
+ * with dL/do = dout,
+ *   dv_j = sum_i P_ij dout_i,  dS_ij = P_ij (dout_i . v_j - dout_i . o_i),
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+ * P_ij being the forward's softmax weights (exp(scale q_i . k_j - lse_i) on
+ * visible pairs) and the sums over i for a KV head running over its Hq/Hkv
+ * query heads. q, k are the ROTATED queries and keys and dq, dk the gradients
+ * with respect to them (rope_qk_backward maps them to the unrotated inputs).
+ *
+ * q, o, dout, dq: [B, S, Hq, D]; k, v, dk, dv: [B, S, Hkv, D]; bf16 only,
+ * strides (b, s, h) per tensor. The token stride of q and dout is at least
+ * Hq times their head stride, which is at least D (each token's heads lie in
+ * its row). o and lse are the forward's outputs for these q, k, v (lse fp32
+ * [B, Hq, S] contiguous, natural log). delta: caller-owned fp32 workspace
+ * [B, Hq, S] (contiguous), overwritten with dout_i . o_i. cu_docs, n_docs,
+ * softmax_scale as gqa_prefill. dq, dk, dv are written, not accumulated.
+ * dkv_workspace: optional caller-owned fp32 buffer of
+ * LA_BWD_PIECES * B * S * Hkv * 2 * D elements (16-byte aligned; contents
+ * need no initialisation). With it, keys whose visible queries span more
+ * than 48 blocks of 64 (token, head) columns have their query range cut into
+ * LA_BWD_PIECES pieces run by separate workgroups; each piece writes its
+ * fp32 partial dk, dv there and a final pass sums the pieces in a fixed
+ * order (the result does not depend on scheduling). NULL: no cut (one
+ * workgroup per 128 keys, which leaves the long ranges of causal attention
+ * on a few workgroups).
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; P and dS rounded to
+ * bf16 before the products that use them.
+ * Errors: UNSUPPORTED for dt != LA_BF16 or D / group size outside the
+ * supported set; INVALID_ARG for null pointers, sizes < 1, Hq % Hkv != 0,
+ * bad strides or alignment, or sizes whose offsets overflow the kernels'
+ * 32-bit block offsets.
+ */
+la_status gqa_attention_backward(const void* q, const void* k, const void* v, const void* o,
+                                 const void* dout, const float* lse, float* delta,
+                                 void* dq, void* dk, void* dv, la_dtype dt,
+                                 int B, int S, int Hq, int Hkv, int D,
+                                 const int64_t q_strides[3], const int64_t k_strides[3],
+                                 const int64_t v_strides[3], const int64_t o_strides[3],
+                                 const int64_t dout_strides[3], const int64_t dq_strides[3],
+                                 const int64_t dk_strides[3], const int64_t dv_strides[3],
+                                 const int32_t* cu_docs, int n_docs, float softmax_scale,
+                                 float* dkv_workspace, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,176 @@
+"""gqa_attention_backward and rope_qk_backward on the GPU against the oracle.
+
+The forward (gqa_prefill on the GPU) supplies o and lse; dq, dk, dv are
+compared with the oracle's fp64 gradients of the same bf16 inputs. The
+gradients' scale varies with the shape (dk and dv sum over every query of a
+document and over the g heads of a KV head), so the bar is taken relative to
+the largest reference magnitude: max-abs error at most 2e-2 and mean-abs at
+most 2e-3 of max|ref|, the parity bar of the forward's outputs (whose values
+are of order 1) carried over to the gradients' own scale.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_helpers as H
+from oracle import reference as orc
+from workloads import draw_cu_docs, draw_grad_output, draw_positions, draw_prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+BASE = 500000.0
+REL_MAX = 2e-2
+REL_MEAN = 2e-3
+
+
+def _dev(x):
+    return x.to(torch.device("cuda"))
+
+
+def assert_grad_close(got, want, what):
+    got = got.double().numpy()
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    scale = float(np.abs(want).max())
+    d = np.abs(got - want)
+    mx, mn = float(d.max()) / scale, float(d.mean()) / scale
+    print(f"[grad] {what}: max|ref| {scale:.3e} rel max-abs {mx:.3e} rel mean-abs {mn:.3e}", flush=True)
+    assert mx <= REL_MAX and mn <= REL_MEAN, f"{what}: rel max-abs {mx:.3e} rel mean-abs {mn:.3e}"
+
+
+def run_backward(qr, kr, v, dout, cu, softmax_scale=0.0, workspace="auto"):
+    """gqa_prefill then gqa_attention_backward on device tensors; (dq, dk, dv) on the CPU."""
+    import gqa_attention_rope_02_amd as la
+    B, S, Hq, D = qr.shape
+    cud = None if cu is None else _dev(torch.as_tensor(np.asarray(cu), dtype=torch.int32).reshape(B, -1))
+    o = torch.full_like(qr, float("nan"))
+    lse = torch.full((B, Hq, S), float("nan"), dtype=torch.float32, device=qr.device)
+    la.gqa_prefill(qr, kr, v, o, lse, cud, softmax_scale)
+    dq = torch.full_like(qr, float("nan"))
+    dk = torch.full_like(kr, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    delta = torch.full((B, Hq, S), float("nan"), dtype=torch.float32, device=qr.device)
+    if workspace == "nan":      # slots a piece leaves unwritten show up as NaN
+        workspace = la.backward_workspace(B, S, kr.shape[2], D, qr.device).fill_(float("nan"))
+    la.gqa_attention_backward(qr, kr, v, o, dout, lse, dq, dk, dv, delta, cud, softmax_scale, workspace)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def _check_case(B, S, Hq, Hkv, D, seed, cus, softmax_scale=0.0, workspace="nan"):
+    q, k, v = draw_prefill_inputs(B, S, Hq, Hkv, D, "bf16", seed)
+    dout = draw_grad_output(B, S, Hq, D, "bf16", seed)
+    cu = None
+    if cus is not None:
+        width = max(c.size for c in cus)
+        cu = np.stack([np.concatenate([c, np.full(width - c.size, S, dtype=np.int32)]) for c in cus])
+    dq, dk, dv = run_backward(_dev(q), _dev(k), _dev(v), _dev(dout), cu, softmax_scale, workspace)
+    sc = None if softmax_scale == 0.0 else softmax_scale
+    for b in range(B):
+        Wq, Wk, Wv = orc.attention_backward(q[b:b + 1], k[b:b + 1], v[b:b + 1], dout[b:b + 1],
+                                            None if cu is None else cu[b], sc)
+        assert_grad_close(dq[b:b + 1], Wq, "dq")
+        assert_grad_close(dk[b:b + 1], Wk, "dk")
+        assert_grad_close(dv[b:b + 1], Wv, "dv")
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,seed,nd", [
+    (1, 700, 32, 8, 128, 201, 3),     # 8B heads, ragged length, documents
+    (1, 520, 16, 1, 128, 202, 2),     # g = 16
+    (2, 300, 8, 8, 64, 203, 3),       # g = 1, D = 64, two sequences
+    (1, 257, 8, 2, 128, 204, None),   # one document, one token past a block
+    (1, 450, 128, 8, 128, 205, 4),    # 405B heads (g = 16)
+    (1, 390, 16, 4, 128, 206, 6),     # many short documents
+    (1, 1500, 32, 8, 128, 210, 1),    # long query ranges cut into pieces (g = 4)
+])
+def test_backward_matches_oracle(B, S, Hq, Hkv, D, seed, nd):
+    H.say("backward", dict(B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, seed=seed, nd=nd))
+    cus = None if nd is None else [draw_cu_docs(S, seed + 100 * b, nd, 6) for b in range(B)]
+    _check_case(B, S, Hq, Hkv, D, seed, cus)
+
+
+def test_backward_without_workspace():
+    """No workspace: every key block's whole query range on one workgroup
+    (the ranges here are long enough to be cut when a workspace is given)."""
+    H.say("backward without workspace")
+    _check_case(1, 520, 16, 1, 128, 211, [draw_cu_docs(520, 211, 2, 6)], workspace=None)
+
+
+def test_backward_empty_documents_and_explicit_scale():
+    """Empty documents (repeated offsets) and a softmax scale that is not 1/sqrt(D)."""
+    S = 333
+    H.say("backward empty documents")
+    cu = np.array([0, 0, 50, 50, 51, 200, 200, S], dtype=np.int32)
+    _check_case(1, S, 16, 2, 128, 207, [cu], softmax_scale=0.05)
+
+
+def test_backward_single_token_gives_dv_dout_and_zero_dq_dk():
+    """S = 1: the only weight is 1, so dv = dout and dS = dout.v - dout.o = 0
+    (o = v): dq and dk vanish up to the rounding of the two dot products,
+    which are summed in different orders (about 1e-6 of |dout| |v|)."""
+    import gqa_attention_rope_02_amd as la
+    H.say("backward single token")
+    q, k, v = draw_prefill_inputs(2, 1, 32, 8, 128, "bf16", 208)
+    dout = draw_grad_output(2, 1, 32, 128, "bf16", 208)
+    dq, dk, dv = run_backward(_dev(q), _dev(k), _dev(v), _dev(dout), None)
+    assert dq.abs().max().item() < 1e-4 and dk.abs().max().item() < 1e-4
+    want = dout.float().reshape(2, 1, 8, 4, 128).sum(dim=3)
+    assert torch.allclose(dv.float(), want, rtol=1e-2, atol=1e-2)
+
+
+def test_rope_backward_is_the_transpose():
+    """rope_qk_backward against the oracle's rotation by the negated angles,
+    and undoing rope_qk (both pairings, explicit positions)."""
+    import gqa_attention_rope_02_amd as la
+    B, S, Hq, Hkv, D = 1, 200, 8, 2, 128
+    H.say("rope backward")
+    q, k, _ = draw_prefill_inputs(B, S, Hq, Hkv, D, "fp32", 209)
+    pos = draw_positions(B, S, 131071, 209)
+    pd = _dev(torch.as_tensor(pos))
+    for pairing in ("adjacent", "half"):
+        qo, ko = torch.empty_like(_dev(q)), torch.empty_like(_dev(k))
+        la.rope_qk_backward(_dev(q), qo, _dev(k), ko, positions=pd, rope_base=BASE, rope_pairing=pairing)
+        Wq = orc.rope(q, -pos.astype(np.int64), BASE, pairing)
+        Wk = orc.rope(k, -pos.astype(np.int64), BASE, pairing)
+        assert np.abs(qo.cpu().double().numpy() - Wq).max() < 1e-5
+        assert np.abs(ko.cpu().double().numpy() - Wk).max() < 1e-5
+        qr = torch.empty_like(qo)
+        la.rope_qk(qo, qr, None, None, positions=pd, rope_base=BASE, rope_pairing=pairing)
+        assert (qr.cpu() - q).abs().max().item() < 1e-5
+
+
+@pytest.mark.parametrize("name", ["llama8b", "llama405b"])
+def test_backward_full_size(name):
+    """The workloads' full shapes, in the launch configuration the benchmark
+    times. The mask keeps documents apart, so every gradient of a document is
+    that of the document alone: documents of up to 1100 tokens are compared
+    with the oracle run on their slice. Every document, long ones included, is
+    checked against two identities of the gradients (the weights of a row sum
+    to one): per KV head, the dv of a document's keys sum to the dout of its
+    queries over the head's group, and the dk sum to zero (each row of dS sums
+    to zero); both within 2^-7 of the sum of magnitudes (every term within a
+    few bf16 roundings)."""
+    from workloads import CONFIGS
+    w = CONFIGS[name]
+    H.say("backward full size", name)
+    q, k, v = draw_prefill_inputs(w.B, w.S, w.Hq, w.Hkv, w.D, w.dtype, w.seed)
+    dout = draw_grad_output(w.B, w.S, w.Hq, w.D, w.dtype, w.seed)
+    cu = draw_cu_docs(w.S, w.seed, w.n_docs, w.n_docs_max)
+    dq, dk, dv = run_backward(_dev(q), _dev(k), _dev(v), _dev(dout), cu[None, :])
+    g = w.Hq // w.Hkv
+    checked = 0
+    for a, b in zip(cu[:-1], cu[1:]):
+        if b == a:
+            continue
+        sdv = dv[0, a:b].double().sum(dim=0)                               # [Hkv, D]
+        sdo = dout[0, a:b].double().reshape(b - a, w.Hkv, g, w.D).sum(dim=(0, 2))
+        assert ((sdv - sdo).abs() <= 2 ** -7 * dv[0, a:b].double().abs().sum(dim=0) + 1e-6).all()
+        sdk = dk[0, a:b].double().sum(dim=0)
+        assert (sdk.abs() <= 2 ** -7 * dk[0, a:b].double().abs().sum(dim=0) + 1e-6).all()
+        if b - a <= 1100:
+            Wq, Wk, Wv = orc.attention_backward(q[:, a:b], k[:, a:b], v[:, a:b], dout[:, a:b])
+            assert_grad_close(dq[:, a:b], Wq, f"dq doc [{a},{b})")
+            assert_grad_close(dk[:, a:b], Wk, f"dk doc [{a},{b})")
+            assert_grad_close(dv[:, a:b], Wv, f"dv doc [{a},{b})")
+            checked += 1
+    assert checked >= 3

@@ -106,6 +106,19 @@ def test_sdpa_library_route(seed, S, Hq, Hkv, D, ndocs):
 
 # ---------------------------------------------------------------- backward
 
+def test_rope_at_negated_positions_undoes_rope():
+    """The rotation is orthogonal and its inverse is the rotation by minus the
+    angle: rope at -m after rope at m returns the input (both pairings), and
+    it preserves every pair's norm."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((1, 9, 3, 16))
+    pos = rng.integers(0, 131072, size=(1, 9))
+    for pairing in ("adjacent", "half"):
+        y = orc.rope(x, pos, 500000.0, pairing)
+        np.testing.assert_allclose(orc.rope(y, -pos, 500000.0, pairing), x, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+
+
 def test_backward_matches_finite_differences():
     """Central differences of L = sum(dO * O) through ``attention`` (the
     forward oracle) on a tiny GQA problem with two documents: every gradient

@@ -8,6 +8,7 @@ HIP path take their inputs from here, and nothing else is shared between them.
 
 from .configs import CONFIGS, Workload, get  # noqa: F401
 from .gen import (  # noqa: F401
+    draw_grad_output,
     draw_cu_docs,
     draw_decode_inputs,
     draw_prefill_inputs,

@@ -61,6 +61,13 @@ def draw_prefill_inputs(B: int, S: int, Hq: int, Hkv: int, D: int, dtype: str,
     return q, k, v
 
 
+def draw_grad_output(B: int, S: int, Hq: int, D: int, dtype: str, seed: int) -> torch.Tensor:
+    """The output gradient dL/dO of a backward pass: standard normal [B, S, Hq, D]
+    (its own stream: seed + 7919)."""
+    gen = torch.Generator("cpu").manual_seed(seed + 7919)
+    return _randn((B, S, Hq, D), gen, dtype)
+
+
 def draw_decode_inputs(B: int, Hq: int, Hkv: int, D: int, seq_lens, dtype: str,
                        seed: int) -> Tuple[torch.Tensor, List[torch.Tensor], List[torch.Tensor]]:
     """Decode inputs on the CPU.
