@@ -207,19 +207,29 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   int li = i0, lt = 0;
   Item lit = item_at(i0);
   // paged cache: the page of the cursor's tile, loaded one issue ahead so its
-  // latency overlaps a tile's work (a 16-key tile never crosses a page)
+  // latency overlaps a tile's work (a 16-key tile never crosses a page). The
+  // loaded id stays in a VGPR until that issue takes it to a scalar register:
+  // vector loads complete in issue order, so the wait there covers only the
+  // loads issued before it, not the tiles in flight after it.
   const int page_mask = (1 << a.page_shift) - 1;
-  int pg = 0;
+  int pgv = 0;
   auto page_of = [&](const Item& it, int t) -> int {
     return a.block_table[(int64_t)it.b * a.bt_stride + ((it.k0 + t * kKT) >> a.page_shift)];
   };
-  if constexpr (PAGED) pg = page_of(lit, 0);
+  if constexpr (PAGED) pgv = page_of(lit, 0);
   auto issue = [&](int st) {
     const __bf16* kb = static_cast<const __bf16*>(a.k);
     const __bf16* vb = static_cast<const __bf16*>(a.v);
     int bytes = 0;   // past the stream end: loads that read nothing keep the count uniform
     if (li < i1) {
       const int key = lit.k0 + lt * kKT;
+      int pg = 0;
+      if constexpr (PAGED) {
+        // the id's VGPR is read here only; the empty asm keeps the compiler
+        // from moving the read (and its wait) up to the load
+        asm volatile("" : "+v"(pgv));
+        pg = __builtin_amdgcn_readfirstlane(pgv);
+      }
       const int64_t base = PAGED ? (int64_t)pg * a.cs_b + lit.kvh * a.cs_h + (int64_t)(key & page_mask) * a.cs_l
                                  : lit.b * a.cs_b + lit.kvh * a.cs_h + (int64_t)key * a.cs_l;
       kb += base;
@@ -232,7 +242,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         if (li < i1) next_item(lit);
       }
       if constexpr (PAGED)
-        if (li < i1) pg = page_of(lit, lt);
+        if (li < i1) pgv = page_of(lit, lt);
     }
     char* dst = my + st * 2 * TB;
 #pragma unroll
@@ -251,80 +261,89 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   float m = -INFINITY, l = 0.f;
   int ci = i0, ct = 0, run_s0 = 0;
   Item cit = item_at(i0);
-  for (int p = 0; ci < i1; ++p) {
-    if (ct == 0 && (ci == i0 || cit.s == 0)) {   // a run of this (b, kvh) starts
-      const bool ok = lc < G;
-      const __bf16* qp = static_cast<const __bf16*>(a.q) + cit.b * a.qs_b +
-                         (cit.kvh * G + (ok ? lc : 0)) * a.qs_h + 8 * lg;
+  // the loop is unrolled over the kNS stages, so every stage's LDS offset is a
+  // constant: the compiler can then tell a stage being filled from the one
+  // being read and waits only for the loads of the tile it reads (with a
+  // run-time stage index it waits for every load in flight before each read)
+  while (ci < i1) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qreg[ks] = ok ? load8(qp + 32 * ks) : zero_bf16x8();
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-      m = -INFINITY;
-      l = 0.f;
-      run_s0 = cit.s;
-    }
-    // tile p has landed once no more than the loads of tiles p+1 .. p+kNS-2 are pending
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NLD * (kNS - 2)) : "memory");
-    issue((p + kNS - 1) % kNS);
+    for (int u = 0; u < kNS; ++u) {
+      if (ci < i1) {   // uniform: once the stream ends, the remaining steps are skipped
+        if (ct == 0 && (ci == i0 || cit.s == 0)) {   // a run of this (b, kvh) starts
+          const bool ok = lc < G;
+          const __bf16* qp = static_cast<const __bf16*>(a.q) + cit.b * a.qs_b +
+                             (cit.kvh * G + (ok ? lc : 0)) * a.qs_h + 8 * lg;
+    #pragma unroll
+          for (int ks = 0; ks < KS; ++ks) qreg[ks] = ok ? load8(qp + 32 * ks) : zero_bf16x8();
+    #pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+          m = -INFINITY;
+          l = 0.f;
+          run_s0 = cit.s;
+        }
+        // tile p has landed once no more than the loads of tiles p+1 .. p+kNS-2 are pending
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NLD * (kNS - 2)) : "memory");
+        issue((u + kNS - 1) % kNS);
 
-    const char* lk = my + (p % kNS) * 2 * TB;
-    const char* lv = lk + TB;
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lk + k_lane + 16 * k_chunk<CH>(4 * ks + lg, lc));
-      s = mfma16k32(ka, qreg[ks], s);
-    }
-    // lane holds S^T[key = key0 + 4lg + j][col = lc]. Keys past the item's
-    // end (only in its last tile) are masked without a branch: the scores are
-    // read here right after their MFMA, and the compiler pads that read with
-    // the wait the matrix core needs only on a single path.
-    const int kbase = cit.k0 + ct * kKT + 4 * lg;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] = kbase + j < cit.k1 ? s[j] : -INFINITY;
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = max_xor32(max_xor16(mx));
-    const bool mv = mx * a.scale_log2 > m * a.scale_log2 + kLazy;
-    if (__any(mv)) {   // rare after a run's first tile
-      const float al = mv ? fast_exp2((m - mx) * a.scale_log2) : 1.f;   // 0 when m = -inf
-      m = mv ? mx : m;
-      l *= al;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= al;
-    }
-    const float mc = m * a.scale_log2;   // finite: the tile holds at least one key
-    bf16x2 p01, p23;
-    p01[0] = to_bf16(fast_exp2(fmaf(s[0], a.scale_log2, -mc)));
-    p01[1] = to_bf16(fast_exp2(fmaf(s[1], a.scale_log2, -mc)));
-    p23[0] = to_bf16(fast_exp2(fmaf(s[2], a.scale_log2, -mc)));
-    p23[1] = to_bf16(fast_exp2(fmaf(s[3], a.scale_log2, -mc)));
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    l = __builtin_amdgcn_fdot2_f32_bf16(p01, one, l, false);
-    l = __builtin_amdgcn_fdot2_f32_bf16(p23, one, l, false);
-    const bf16x4 pv = {p01[0], p01[1], p23[0], p23[1]};
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lv + v_lane[db]));
-      acc[db] = mfma16k16(__builtin_bit_cast(bf16x4, r), pv, acc[db]);
-    }
+        const char* lk = my + u * 2 * TB;
+        const char* lv = lk + TB;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lk + k_lane + 16 * k_chunk<CH>(4 * ks + lg, lc));
+          s = mfma16k32(ka, qreg[ks], s);
+        }
+        // lane holds S^T[key = key0 + 4lg + j][col = lc]. Keys past the item's
+        // end (only in its last tile) are masked without a branch: the scores are
+        // read here right after their MFMA, and the compiler pads that read with
+        // the wait the matrix core needs only on a single path.
+        const int kbase = cit.k0 + ct * kKT + 4 * lg;
+    #pragma unroll
+        for (int j = 0; j < 4; ++j) s[j] = kbase + j < cit.k1 ? s[j] : -INFINITY;
+        float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        mx = max_xor32(max_xor16(mx));
+        const bool mv = mx * a.scale_log2 > m * a.scale_log2 + kLazy;
+        if (__any(mv)) {   // rare after a run's first tile
+          const float al = mv ? fast_exp2((m - mx) * a.scale_log2) : 1.f;   // 0 when m = -inf
+          m = mv ? mx : m;
+          l *= al;
+    #pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] *= al;
+        }
+        const float mc = m * a.scale_log2;   // finite: the tile holds at least one key
+        bf16x2 p01, p23;
+        p01[0] = to_bf16(fast_exp2(fmaf(s[0], a.scale_log2, -mc)));
+        p01[1] = to_bf16(fast_exp2(fmaf(s[1], a.scale_log2, -mc)));
+        p23[0] = to_bf16(fast_exp2(fmaf(s[2], a.scale_log2, -mc)));
+        p23[1] = to_bf16(fast_exp2(fmaf(s[3], a.scale_log2, -mc)));
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        l = __builtin_amdgcn_fdot2_f32_bf16(p01, one, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(p23, one, l, false);
+        const bf16x4 pv = {p01[0], p01[1], p23[0], p23[1]};
+    #pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lv + v_lane[db]));
+          acc[db] = mfma16k16(__builtin_bit_cast(bf16x4, r), pv, acc[db]);
+        }
 
-    if (++ct == cit.nt) {   // item done
-      if (ci + 1 == i1 || cit.s + 1 == cit.ns) {   // run done: its partial goes to slot run_s0
-        const float lt2 = add_xor32(add_xor16(l));
-        if (lc < G) {
-          const int64_t row = ((int64_t)cit.b * a.Hq + cit.kvh * G + lc) * a.max_splits;
-          float* op = a.o_part + (row + run_s0) * D;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            *reinterpret_cast<f32x4*>(op + 16 * db + 4 * lg) = acc[db] / lt2;
-          if (lg == 0) a.lse_part[row + run_s0] = m * a.scale + fast_log2(lt2) * kLn2;
-          for (int s2 = run_s0 + 1 + lg; s2 <= cit.s; s2 += 4) a.lse_part[row + s2] = -INFINITY;
+        if (++ct == cit.nt) {   // item done
+          if (ci + 1 == i1 || cit.s + 1 == cit.ns) {   // run done: its partial goes to slot run_s0
+            const float lt2 = add_xor32(add_xor16(l));
+            if (lc < G) {
+              const int64_t row = ((int64_t)cit.b * a.Hq + cit.kvh * G + lc) * a.max_splits;
+              float* op = a.o_part + (row + run_s0) * D;
+    #pragma unroll
+              for (int db = 0; db < DB; ++db)
+                *reinterpret_cast<f32x4*>(op + 16 * db + 4 * lg) = acc[db] / lt2;
+              if (lg == 0) a.lse_part[row + run_s0] = m * a.scale + fast_log2(lt2) * kLn2;
+              for (int s2 = run_s0 + 1 + lg; s2 <= cit.s; s2 += 4) a.lse_part[row + s2] = -INFINITY;
+            }
+          }
+          ++ci;
+          ct = 0;
+          if (ci < i1) next_item(cit);
         }
       }
-      ++ci;
-      ct = 0;
-      if (ci < i1) next_item(cit);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // loads past the stream end
