@@ -16,16 +16,17 @@
 //
 // How (gfx950), three launches on the caller's stream:
 // * delta: one row per 16 lanes (D = 128), fp32 dot products of the bf16 rows.
-// * dk/dv, key-stationary: one workgroup = (sequence, KV head, 128 keys), four
-//   waves of 32 keys, one wave per SIMD. A lane keeps its key's K and V rows as
-//   MFMA operands and its key's dk, dv rows as accumulators for the whole
-//   loop; the queries that can see the keys go by in blocks of 64 columns
-//   (token, query head) staged in LDS (Q, dO, lse, delta; two stages, loaded
-//   straight from HBM with buffer_load ... lds). Per 32 columns and 32 keys:
-//   S = Q K^T and dP = dO V^T (lane = key, so the weights come out in the
-//   layout of the next products' B operand), then dV^T += dO^T P and
-//   dK^T += Q^T dS on the 32x32x16 bf16 MFMA, dO^T and Q^T read from the same
-//   LDS rows with the transposing ds_read_b64_tr_b16.
+// * dk/dv, key-stationary: one workgroup = (sequence, KV head, 128 keys),
+//   eight waves, two per SIMD sharing a group of 32 keys. The (token, query
+//   head) columns that can see the keys go by in blocks of 64 staged in LDS
+//   (Q, dO, lse, delta; two stages, loaded straight from HBM with
+//   buffer_load ... lds). Per block, with the key on the lane: one wave of the
+//   pair forms S = Q K^T, P, and dV^T += dO^T P; the other forms dP = dO V^T
+//   and, with the first wave's P passed through LDS, dS = P (dP - delta) and
+//   dK^T += Q^T dS (32x32x16 bf16 MFMA; dO^T and Q^T read from the same LDS
+//   rows with the transposing ds_read_b64_tr_b16). Each wave thus holds one
+//   operand row (K or V) and one accumulator (dV or dK), which fits two waves
+//   per SIMD, so one wave's waits are filled by the other's work.
 // * dq, query-stationary (the forward's shape): one workgroup = (sequence,
 //   KV head, 256 / g tokens x g heads), eight waves of 32 columns; Q and dO
 //   rows in registers, key tiles of 64 K and V rows staged in LDS (two
@@ -44,8 +45,9 @@ namespace la {
 namespace {
 
 constexpr int kNC = 64;                  // columns per block (dk/dv kernel)
-constexpr int kKvWaves = 4;
-constexpr int kKvKeys = 32 * kKvWaves;   // keys per workgroup (dk/dv kernel)
+constexpr int kKvGroups = 4;             // 32-key groups per workgroup (dk/dv kernel)
+constexpr int kKvWaves = 2 * kKvGroups;  // two waves per group
+constexpr int kKvKeys = 32 * kKvGroups;  // keys per workgroup (dk/dv kernel)
 constexpr int kQWaves = 8;
 constexpr int kQCols = 32 * kQWaves;     // columns per workgroup (dq kernel)
 constexpr int kKT = 64;                  // keys per tile (dq kernel)
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- dk, dv
 
 template <int D, int G>
-__global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_kernel(BwdArgs a) {
   constexpr int KS = D / 16, DB = D / 32, CH = D / 8, ROW = 2 * D;
   constexpr int TB = kNC / G;                 // tokens per column block
@@ -125,12 +127,19 @@ void dkdv_kernel(BwdArgs a) {
   constexpr int STAGE = 2 * QT + 2 * kNC * 4;
   constexpr int RPI = 64 / CH;                // rows per 1 KB load
   constexpr int NLW = kNC / RPI / kKvWaves;   // 1 KB loads per wave per Q or dO block
+  constexpr int NCB = kNC / 32;               // 32-column blocks per block
+  constexpr int PB = NCB * 16 * 64 * 4;       // P of one key group: [cb][i/4][lane] f32x4
   static_assert(NLW >= 1 && NLW * RPI * kKvWaves == kNC, "block loads must cover the rows");
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE + kKvGroups * PB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lc = lane & 31, hi = lane >> 5;
+  // waves w and w + 4 (one SIMD) share a group of 32 keys: role 0 forms S and
+  // P and accumulates dV, role 1 forms dP and, from role 0's P, dS, and
+  // accumulates dK
+  const int grp = wave & (kKvGroups - 1);
+  const int role = wave / kKvGroups;
 
   const int bid = blockIdx.x;
   const int kvh = bid % a.Hkv;
@@ -138,11 +147,11 @@ void dkdv_kernel(BwdArgs a) {
   const int b = r % a.B;
   const int k0 = (r / a.B) * kKvKeys;          // key blocks in order: the first sees the most queries
   const int S = a.S;
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + grp * 32;
   const int j = kw0 + lc;                     // this lane's key
   const int32_t* cu = a.cu_docs ? a.cu_docs + (int64_t)b * (a.n_docs + 1) : nullptr;
 
-  // document ends: of this lane's key, of the wave's first and last keys, of
+  // document ends: of this lane's key, of the group's first and last keys, of
   // the block's last key (queries at or past it see none of the block's keys)
   int dend = S, w_dend_first = S, w_dend_last = S, q_end = S;
   if (cu) {
@@ -157,17 +166,15 @@ void dkdv_kernel(BwdArgs a) {
   // the lane's key is visible to the tokens t with 0 <= t - j < lim
   const unsigned lim = j < S ? (unsigned)(dend - j) : 0u;
 
-  // K and V rows of the key as B operands: K[j][16ks + 8hi + i]
-  bf16x8 kreg[KS], vreg[KS];
+  // the key's K row (role 0) or V row (role 1) as B operand: [j][16ks + 8hi + i]
+  bf16x8 kv[KS];
   {
     const int jc = min(j, S - 1);
-    const __bf16* kp = static_cast<const __bf16*>(a.k) + b * a.ks_b + jc * a.ks_s + kvh * a.ks_h + 8 * hi;
-    const __bf16* vp = static_cast<const __bf16*>(a.v) + b * a.vs_b + jc * a.vs_s + kvh * a.vs_h + 8 * hi;
+    const __bf16* p = role == 0
+        ? static_cast<const __bf16*>(a.k) + b * a.ks_b + jc * a.ks_s + kvh * a.ks_h + 8 * hi
+        : static_cast<const __bf16*>(a.v) + b * a.vs_b + jc * a.vs_s + kvh * a.vs_h + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kreg[ks] = load8(kp + 16 * ks);
-      vreg[ks] = load8(vp + 16 * ks);
-    }
+    for (int ks = 0; ks < KS; ++ks) kv[ks] = load8(p + 16 * ks);
   }
 
   // query columns: tokens k0 .. q_end - 1, column c of a block = (token
@@ -215,15 +222,13 @@ void dkdv_kernel(BwdArgs a) {
   int v_lane[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) v_lane[db] = v_lane_off<D>(lane, db);
+  char* pbuf = lds + 2 * STAGE + grp * PB;    // the group's P, role 0 -> role 1
 
-  f32x16 dk[DB], dv[DB];
+  f32x16 acc[DB];                             // dV^T (role 0) or dK^T (role 1)
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk[db][i] = 0.f;
-      dv[db][i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
   if (n_blk > 0) issue(blk0);
   for (int n = 0; n < n_blk; ++n) {
@@ -232,93 +237,100 @@ void dkdv_kernel(BwdArgs a) {
     if (n + 1 < n_blk) issue(blk0 + n + 1);
     const char* st = lds + (n & 1) * STAGE;
     const int tb0 = k0 + (blk0 + n) * TB;
-    // nothing of this block visible to the wave's keys
-    if (kw0 > tb0 + TB - 1 || tb0 >= w_dend_last) continue;
+    // nothing of this block visible to the group's keys: both roles skip the
+    // work (never the barriers)
+    const bool skip = kw0 > tb0 + TB - 1 || tb0 >= w_dend_last;
     // every pair visible: all keys at or before every token, all tokens
-    // before the first key's document end
+    // before the first key's document end; t - j is then in [0, S) for every
+    // pair and the mask test passes with the limit at its maximum
     const bool full = kw0 + 31 <= tb0 && tb0 + TB <= w_dend_first;
-    // on such blocks t - j is in [0, S) for every pair, so the mask test
-    // below passes everywhere with the limit at its maximum (no branch)
     const unsigned lim_b = full ? ~0u : lim;
-    f32x16 s[kNC / 32], dp[kNC / 32];
+    // S = Q K^T (role 0) or dP = dO V^T (role 1), lane = key j; element i of
+    // column block cb is column 32cb + 8(i/4) + 4hi + i%4
+    f32x16 sd[NCB];
+    if (!skip) {
+      const char* src = st + role * QT;
 #pragma unroll
-    for (int cb = 0; cb < kNC / 32; ++cb)
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[cb][i] = 0.f;
-        dp[cb][i] = 0.f;
+        for (int i = 0; i < 16; ++i) sd[cb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch = 16 * v_chunk<CH>(2 * ks + hi, lc);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          sd[cb] = mfma32(*reinterpret_cast<const bf16x8*>(src + (32 * cb + lc) * ROW + ch), kv[ks], sd[cb]);
       }
+      if (role == 0) {
+        // P = exp(s scale - lse) on visible pairs, to LDS for role 1
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch = 16 * v_chunk<CH>(2 * ks + hi, lc);
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < kNC / 32; ++cb) {
-        const int arow = (32 * cb + lc) * ROW;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(st + arow + ch);
-        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(st + QT + arow + ch);
-        s[cb] = mfma32(qa, kreg[ks], s[cb]);
-        dp[cb] = mfma32(ga, vreg[ks], dp[cb]);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int c0 = 32 * cb + 8 * q4 + 4 * hi;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + 2 * QT + 4 * c0);
+            f32x4 pv;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int t = tb0 + (c0 + u) / G;
+              const float e = fast_exp2(fmaf(sd[cb][4 * q4 + u], a.scale_log2, -l4[u] * kLog2e));
+              pv[u] = (unsigned)(t - j) < lim_b ? e : 0.f;
+              sd[cb][4 * q4 + u] = pv[u];
+            }
+            *reinterpret_cast<f32x4*>(pbuf + ((cb * 4 + q4) * 64 + lane) * 16) = pv;
+          }
       }
     }
+    __syncthreads();   // role 0's P is in LDS
+    if (!skip) {
+      if (role == 1) {
+        // dS = P (dP - delta)
 #pragma unroll
-    for (int cb = 0; cb < kNC / 32; ++cb) {
-      // lane = key j; element i is column 32cb + 8(i/4) + 4hi + i%4
-      f32x16 p, ds;
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int c0 = 32 * cb + 8 * q4 + 4 * hi;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + 2 * QT + 4 * c0);
-        const f32x4 e4 = *reinterpret_cast<const f32x4*>(st + 2 * QT + kNC * 4 + 4 * c0);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int c0 = 32 * cb + 8 * q4 + 4 * hi;
+            const f32x4 e4 = *reinterpret_cast<const f32x4*>(st + 2 * QT + kNC * 4 + 4 * c0);
+            const f32x4 pv = *reinterpret_cast<const f32x4*>(pbuf + ((cb * 4 + q4) * 64 + lane) * 16);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = 4 * q4 + u;
-          const int t = tb0 + (c0 + u) / G;
-          float pv = fast_exp2(fmaf(s[cb][i], a.scale_log2, -l4[u] * kLog2e));
-          pv = (unsigned)(t - j) < lim_b ? pv : 0.f;
-          p[i] = pv;
-          ds[i] = pv * (dp[cb][i] - e4[u]);
-        }
+            for (int u = 0; u < 4; ++u) sd[cb][4 * q4 + u] = pv[u] * (sd[cb][4 * q4 + u] - e4[u]);
+          }
       }
+      // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1), the A operand read
+      // transposed from the other tile
+      const char* tsrc = st + (1 - role) * QT;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 pb = pack8(p, 8 * h2);
-        const bf16x8 sb = pack8(ds, 8 * h2);
-        const int roff = 16 * (2 * cb + h2) * ROW;
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 gt = read_tr_rows<D>(st + QT + roff + v_lane[db]);
-          const bf16x8 qt = read_tr_rows<D>(st + roff + v_lane[db]);
-          dv[db] = mfma32(gt, pb, dv[db]);
-          dk[db] = mfma32(qt, sb, dk[db]);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 x = pack8(sd[cb], 8 * h2);
+          const int roff = 16 * (2 * cb + h2) * ROW;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = mfma32(read_tr_rows<D>(tsrc + roff + v_lane[db]), x, acc[db]);
         }
-      }
     }
   }
 
-  // lane = key j, element i of block db is d = 32db + 8(i/4) + 4hi + i%4
+  // lane = key j, element i of block db is d = 32db + 8(i/4) + 4hi + i%4;
+  // role 0 holds dv, role 1 dk (times the scale)
+  const float f = role == 0 ? 1.f : a.scale;
   if (split && j < S) {
-    float* part = a.dkv_part + ((((int64_t)piece * a.B + b) * S + j) * a.Hkv + kvh) * 2 * D;
+    float* part = a.dkv_part + ((((int64_t)piece * a.B + b) * S + j) * a.Hkv + kvh) * 2 * D + (role == 0 ? D : 0);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * db + 8 * q4 + 4 * hi;
-        store4(part + d0, a.scale * dk[db][4 * q4], a.scale * dk[db][4 * q4 + 1], a.scale * dk[db][4 * q4 + 2],
-               a.scale * dk[db][4 * q4 + 3]);
-        store4(part + D + d0, dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]);
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        store4(part + 32 * db + 8 * q4 + 4 * hi, f * acc[db][4 * q4], f * acc[db][4 * q4 + 1],
+               f * acc[db][4 * q4 + 2], f * acc[db][4 * q4 + 3]);
   } else if (j < S) {
-    __bf16* kd = static_cast<__bf16*>(a.dk) + b * a.dks_b + j * a.dks_s + kvh * a.dks_h;
-    __bf16* vd = static_cast<__bf16*>(a.dv) + b * a.dvs_b + j * a.dvs_s + kvh * a.dvs_h;
+    __bf16* out = role == 0 ? static_cast<__bf16*>(a.dv) + b * a.dvs_b + j * a.dvs_s + kvh * a.dvs_h
+                            : static_cast<__bf16*>(a.dk) + b * a.dks_b + j * a.dks_s + kvh * a.dks_h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * db + 8 * q4 + 4 * hi;
-        store4(kd + d0, a.scale * dk[db][4 * q4], a.scale * dk[db][4 * q4 + 1], a.scale * dk[db][4 * q4 + 2],
-               a.scale * dk[db][4 * q4 + 3]);
-        store4(vd + d0, dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]);
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        store4(out + 32 * db + 8 * q4 + 4 * hi, f * acc[db][4 * q4], f * acc[db][4 * q4 + 1],
+               f * acc[db][4 * q4 + 2], f * acc[db][4 * q4 + 3]);
   }
 }
 
