@@ -211,6 +211,50 @@ def test_rope_rejects(lib, kw, status):
     assert rope(lib, **kw) == status
 
 
+def rope_back(lib, **kw):
+    args = dict(qi=FAKE, qo=FAKE, ki=FAKE, ko=FAKE, dt=0, B=1, S=4, Hq=8, Hkv=2, D=128, base=5e5,
+                pairing=0)
+    args.update(kw)
+    return lib.rope_qk_backward(args["qi"], args["qo"], S3, S3, args["ki"], args["ko"], S3, S3,
+                                args["dt"], args["B"], args["S"], args["Hq"], args["Hkv"], args["D"],
+                                None, args["base"], args["pairing"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qo=None), INVALID), (dict(ki=None, ko=FAKE), INVALID), (dict(base=0.0), INVALID),
+    (dict(pairing=2), INVALID), (dict(D=80), UNSUPPORTED), (dict(B=0), INVALID),
+])
+def test_rope_backward_rejects(lib, kw, status):
+    assert rope_back(lib, **kw) == status
+
+
+S3_HEAD_MAJOR = _lib.i64_array([1 << 20, 128, 4096])   # heads further apart than tokens
+
+
+def backward(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, g=FAKE, lse=FAKE, delta=FAKE, dq=FAKE, dk=FAKE,
+                dv=FAKE, dt=0, B=1, S=16, Hq=16, Hkv=4, D=128, qs=S3, gs=S3, cu=None, nd=1,
+                scale=0.0, ws=None)
+    args.update(kw)
+    return lib.gqa_attention_backward(
+        args["q"], args["k"], args["v"], args["o"], args["g"], args["lse"], args["delta"],
+        args["dq"], args["dk"], args["dv"], args["dt"], args["B"], args["S"], args["Hq"],
+        args["Hkv"], args["D"], args["qs"], S3, S3, S3, args["gs"], S3, S3, S3, args["cu"],
+        args["nd"], args["scale"], args["ws"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(g=None), INVALID), (dict(lse=None), INVALID),
+    (dict(delta=None), INVALID), (dict(dk=None), INVALID), (dict(dt=1), UNSUPPORTED),
+    (dict(D=80), UNSUPPORTED), (dict(Hq=48, Hkv=1), UNSUPPORTED), (dict(Hq=10, Hkv=4), INVALID),
+    (dict(S=0), INVALID), (dict(qs=S3_HEAD_MAJOR), INVALID), (dict(gs=S3_HEAD_MAJOR), INVALID),
+    (dict(dq=FAKE + 8), INVALID), (dict(ws=FAKE + 4), INVALID), (dict(cu=FAKE, nd=0), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(qs=S3_BAD), INVALID),
+])
+def test_backward_rejects(lib, kw, status):
+    assert backward(lib, **kw) == status
+
+
 def decode(lib, **kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, sl=FAKE, B=2, Hq=16, Hkv=1, D=128, Lmax=1000, chunk=256,
                 ms=4, op=FAKE, lp=FAKE)
