@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The loaded C-ABI library on a GPU machine (tests marked gpu only)."""
+    """The loaded C-ABI library (tests marked gpu only, on a machine with the GPU)."""
     import torch
     if not torch.cuda.is_available():
         pytest.fail("GPU test run without a visible GPU")
