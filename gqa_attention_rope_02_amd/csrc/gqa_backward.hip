@@ -66,28 +66,39 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int off) {
   return r;
 }
 
+// Physical 16-byte chunk of logical chunk c in row r of a tile read both as
+// rows (ds_read_b128: 16 consecutive rows of one chunk per 16 lanes) and
+// transposed (ds_read_b64_tr_b16: 4 consecutive rows x 4 consecutive chunks
+// per 32 lanes). For D = 128 the row term is the 4-bit transpose of r & 15:
+// any 16 consecutive rows get 16 distinct chunks and the 4 rows of an aligned
+// group land 64 bytes apart, so neither read conflicts (the transposing
+// reads' swizzle 4 (r & 3) alone gives the row reads a 4-way conflict). An
+// XOR with a row-only term is its own inverse, which the loaders rely on.
+template <int CH>
+__device__ __forceinline__ int t_chunk(int c, int r) {
+  return CH == 16 ? c ^ ((4 * (r & 3)) | ((r >> 2) & 3)) : v_chunk<CH>(c, r);
+}
+
 // A operand of a product whose M is head_dim and K 16 rows of a row-major
-// tile: rows 4hi + 0..3 and 8 + 4hi + 0..3 past p's row for lane half hi, two
-// transposing reads at the lane's offset (v_lane_off) within the 16 rows.
-template <int D>
-__device__ __forceinline__ bf16x8 read_tr_rows(const char* p) {
-  constexpr int ROW = 2 * D;
-  const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * ROW));
+// tile: rows 4hi + 0..3 (first read) and 8 + 4hi + 0..3 (second) of the 16
+// rows at p, for lane half hi; o1, o2 are the lane's offsets (tr_lane_off).
+__device__ __forceinline__ bf16x8 read_tr_rows(const char* p, int o1, int o2) {
+  const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + o1));
+  const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + o2));
   return __builtin_shufflevector(__builtin_bit_cast(bf16x4, r0), __builtin_bit_cast(bf16x4, r1),
                                  0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Per-lane byte offsets of the transposing reads within a 16-row group of a
-// row-major tile stored with the v_chunk swizzle: the 16-lane group
-// g = lane / 16 covers d = 32db + 16(g & 1) + (lane & 15); its input lane
-// L = lane & 15 addresses row 4hi + L/4 at d0 = 32db + 16(g & 1) + 4(L % 4).
+// Per-lane byte offset of a transposing read within a 16-row group of a
+// row-major tile stored with t_chunk: the 16-lane group g = lane / 16 covers
+// d = 32db + 16(g & 1) + (lane & 15); its input lane L = lane & 15 addresses
+// row r8 + 4hi + L/4 (r8 = 0 or 8) at d0 = 32db + 16(g & 1) + 4(L % 4).
 template <int D>
-__device__ __forceinline__ int v_lane_off(int lane, int db) {
+__device__ __forceinline__ int tr_lane_off(int lane, int db, int r8) {
   constexpr int CH = D / 8, ROW = 2 * D;
   const int L16 = lane & 15, hi = lane >> 5;
-  const int vrow = 4 * hi + (L16 >> 2);
-  return vrow * ROW + 16 * v_chunk<CH>(4 * db + 2 * ((lane >> 4) & 1) + ((L16 >> 1) & 1), vrow) + 8 * (L16 & 1);
+  const int row = r8 + 4 * hi + (L16 >> 2);
+  return row * ROW + 16 * t_chunk<CH>(4 * db + 2 * ((lane >> 4) & 1) + ((L16 >> 1) & 1), row) + 8 * (L16 & 1);
 }
 
 // ---------------------------------------------------------------- delta
@@ -195,7 +206,7 @@ void dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int p = 0; p < NLW; ++p) {
     const int row = (wave * NLW + p) * RPI + lane / CH;
-    const int lch = v_chunk<CH>(lane % CH, row);
+    const int lch = t_chunk<CH>(lane % CH, row);
     qoff[p] = (int)(((row / G) * a.qs_s + (row % G) * a.qs_h) * 2 + 16 * lch);
     goff[p] = (int)(((row / G) * a.gs_s + (row % G) * a.gs_h) * 2 + 16 * lch);
   }
@@ -219,9 +230,12 @@ void dkdv_kernel(BwdArgs a) {
     if (wave == 1) load_lds4(eb + tb0, lbytes, loff, dst + 2 * QT + kNC * 4);
   };
 
-  int v_lane[DB];
+  int tr1[DB], tr2[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) v_lane[db] = v_lane_off<D>(lane, db);
+  for (int db = 0; db < DB; ++db) {
+    tr1[db] = tr_lane_off<D>(lane, db, 0);
+    tr2[db] = tr_lane_off<D>(lane, db, 8);
+  }
   char* pbuf = lds + 2 * STAGE + grp * PB;    // the group's P, role 0 -> role 1
 
   f32x16 acc[DB];                             // dV^T (role 0) or dK^T (role 1)
@@ -256,7 +270,7 @@ void dkdv_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) sd[cb][i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int ch = 16 * v_chunk<CH>(2 * ks + hi, lc);
+        const int ch = 16 * t_chunk<CH>(2 * ks + hi, lc);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
           sd[cb] = mfma32(*reinterpret_cast<const bf16x8*>(src + (32 * cb + lc) * ROW + ch), kv[ks], sd[cb]);
@@ -306,7 +320,7 @@ void dkdv_kernel(BwdArgs a) {
           const bf16x8 x = pack8(sd[cb], 8 * h2);
           const int roff = 16 * (2 * cb + h2) * ROW;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] = mfma32(read_tr_rows<D>(tsrc + roff + v_lane[db]), x, acc[db]);
+          for (int db = 0; db < DB; ++db) acc[db] = mfma32(read_tr_rows(tsrc + roff, tr1[db], tr2[db]), x, acc[db]);
         }
     }
   }
@@ -406,7 +420,7 @@ void dq_kernel(BwdArgs a, int n_qtiles) {
 #pragma unroll
   for (int p = 0; p < NLW; ++p) {
     const int row = (wave * NLW + p) * RPI + lane / CH;
-    koff[p] = (int)(row * a.ks_s * 2 + 16 * v_chunk<CH>(lane % CH, row));
+    koff[p] = (int)(row * a.ks_s * 2 + 16 * t_chunk<CH>(lane % CH, row));
     voff[p] = (int)(row * a.vs_s * 2 + 16 * k_chunk<CH>(lane % CH, row));
   }
   auto issue = [&](int n) __attribute__((always_inline)) {
@@ -422,9 +436,12 @@ void dq_kernel(BwdArgs a, int n_qtiles) {
     }
   };
 
-  int v_lane[DB];
+  int tr1[DB], tr2[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) v_lane[db] = v_lane_off<D>(lane, db);
+  for (int db = 0; db < DB; ++db) {
+    tr1[db] = tr_lane_off<D>(lane, db, 0);
+    tr2[db] = tr_lane_off<D>(lane, db, 8);
+  }
 
   f32x16 dq[DB];
 #pragma unroll
@@ -456,7 +473,7 @@ void dq_kernel(BwdArgs a, int n_qtiles) {
       const int arow = (32 * kb + lc) * ROW;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lk + arow + 16 * v_chunk<CH>(2 * ks + hi, lc));
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lk + arow + 16 * t_chunk<CH>(2 * ks + hi, lc));
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(lv + arow + 16 * k_chunk<CH>(2 * ks + hi, lc));
         s[kb] = mfma32(ka, qreg[ks], s[kb]);
         dp[kb] = mfma32(va, greg[ks], dp[kb]);
@@ -481,7 +498,7 @@ void dq_kernel(BwdArgs a, int n_qtiles) {
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        dq[db] = mfma32(read_tr_rows<D>(lk + 16 * ks * ROW + v_lane[db]), sb[ks >> 1][ks & 1], dq[db]);
+        dq[db] = mfma32(read_tr_rows(lk + 16 * ks * ROW, tr1[db], tr2[db]), sb[ks >> 1][ks & 1], dq[db]);
   }
 
   // lane = column, element i of block db is d = 32db + 8(i/4) + 4hi + i%4
