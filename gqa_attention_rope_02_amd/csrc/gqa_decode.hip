@@ -47,6 +47,14 @@ constexpr int kWaves = 4;     // waves per workgroup
 constexpr float kLazy = 8.f;  // log2 headroom of the lazily moved softmax reference
 constexpr int kMaxB = kDecodeMaxBatch;   // sequences per call (tables in LDS)
 
+// Physical 16-byte chunk of logical chunk c in row r of a V tile. The
+// transposing reads of the 16x16x16 products take, per 32 lanes, 8
+// consecutive rows x 32 bytes: the row term spreads those 8 rows over the
+// 256-byte bank row (D = 128: 32-byte steps over 8 rows; D = 64, two rows per
+// bank row: 32-byte steps over row pairs), so no two lanes share a bank.
+template <int CH>
+__device__ __forceinline__ int dv_chunk(int c, int r) { return c ^ (CH == 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3)); }
+
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Lane exchanges on the VALU (v_permlane16/32_swap), not through the LDS
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     const int p = n * 64 + lane;   // LDS chunk written by this lane
     const int row = p / CH, ph = p % CH;
     koffv[n] = (int)(row * a.cs_l * 2 + 16 * k_chunk<CH>(ph, row));
-    voffv[n] = (int)(row * a.cs_l * 2 + 16 * v_chunk<CH>(ph, row));
+    voffv[n] = (int)(row * a.cs_l * 2 + 16 * dv_chunk<CH>(ph, row));
   }
   // K operand (A of S^T = K Q^T): row lc, logical chunk 4ks + lg
   const int k_lane = lc * ROW;
@@ -199,7 +207,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   int v_lane[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
-    v_lane[db] = vrow * ROW + 16 * v_chunk<CH>(2 * db + ((lc >> 1) & 1), vrow) + 8 * (lc & 1);
+    v_lane[db] = vrow * ROW + 16 * dv_chunk<CH>(2 * db + ((lc >> 1) & 1), vrow) + 8 * (lc & 1);
 
   char* my = &ring[wave][0][0][0];
 
