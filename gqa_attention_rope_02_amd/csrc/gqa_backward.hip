@@ -255,10 +255,8 @@ void dkdv_kernel(BwdArgs a) {
     // work (never the barriers)
     const bool skip = kw0 > tb0 + TB - 1 || tb0 >= w_dend_last;
     // every pair visible: all keys at or before every token, all tokens
-    // before the first key's document end; t - j is then in [0, S) for every
-    // pair and the mask test passes with the limit at its maximum
+    // before the first key's document end (no mask needed)
     const bool full = kw0 + 31 <= tb0 && tb0 + TB <= w_dend_first;
-    const unsigned lim_b = full ? ~0u : lim;
     // S = Q K^T (role 0) or dP = dO V^T (role 1), lane = key j; element i of
     // column block cb is column 32cb + 8(i/4) + 4hi + i%4
     f32x16 sd[NCB];
@@ -283,14 +281,24 @@ void dkdv_kernel(BwdArgs a) {
           for (int q4 = 0; q4 < 4; ++q4) {
             const int c0 = 32 * cb + 8 * q4 + 4 * hi;
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(st + 2 * QT + 4 * c0);
-            f32x4 pv;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int t = tb0 + (c0 + u) / G;
-              const float e = fast_exp2(fmaf(sd[cb][4 * q4 + u], a.scale_log2, -l4[u] * kLog2e));
-              pv[u] = (unsigned)(t - j) < lim_b ? e : 0.f;
-              sd[cb][4 * q4 + u] = pv[u];
+            for (int u = 0; u < 4; ++u)
+              sd[cb][4 * q4 + u] = fast_exp2(fmaf(sd[cb][4 * q4 + u], a.scale_log2, -l4[u] * kLog2e));
+          }
+        if (!full) {   // only blocks on a causal or document edge
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int t = tb0 + (32 * cb + 8 * (i >> 2) + 4 * hi + (i & 3)) / G;
+              sd[cb][i] = (unsigned)(t - j) < lim ? sd[cb][i] : 0.f;
             }
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 pv = {sd[cb][4 * q4], sd[cb][4 * q4 + 1], sd[cb][4 * q4 + 2], sd[cb][4 * q4 + 3]};
             *reinterpret_cast<f32x4*>(pbuf + ((cb * 4 + q4) * 64 + lane) * 16) = pv;
           }
       }
@@ -459,9 +467,7 @@ void dq_kernel(BwdArgs a, int n_qtiles) {
     const int kt = kv_lo + n * kKT;
     if (kt > w_tmax || kt + kKT - 1 < w_smin) continue;   // no key of the tile visible to the wave
     const bool full = wave_all_valid && kt + kKT - 1 <= w_tmin && kt >= w_smax;
-    // on such tiles key - dstart is in [0, S) for every pair: the mask test
-    // passes everywhere with the limit at its maximum (no branch)
-    const unsigned lim_b = full ? ~0u : lim;
+
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -483,14 +489,23 @@ void dq_kernel(BwdArgs a, int n_qtiles) {
     bf16x8 sb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], a.scale_log2, -lse2));
+    }
+    if (!full) {   // only tiles on a causal or document edge
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
+          s[kb][i] = (unsigned)(key - dstart) < lim ? s[kb][i] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
       f32x16 ds;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(fmaf(s[kb][i], a.scale_log2, -lse2));
-        const int key = kt + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
-        pv = (unsigned)(key - dstart) < lim_b ? pv : 0.f;
-        ds[i] = pv * (dp[kb][i] - dlt);
-      }
+      for (int i = 0; i < 16; ++i) ds[i] = s[kb][i] * (dp[kb][i] - dlt);
       sb[kb][0] = pack8(ds, 0);
       sb[kb][1] = pack8(ds, 8);
     }
