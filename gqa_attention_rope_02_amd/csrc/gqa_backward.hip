@@ -14,7 +14,7 @@
 // where the sums over i for a key also run over the g query heads that share
 // its KV head.
 //
-// How (gfx950), three launches on the caller's stream:
+// How (gfx950), launches in order on the caller's stream:
 // * delta: one row per 16 lanes (D = 128), fp32 dot products of the bf16 rows.
 // * dk/dv, key-stationary: one workgroup = (sequence, KV head, 128 keys),
 //   eight waves, two per SIMD sharing a group of 32 keys. The (token, query
@@ -26,7 +26,9 @@
 //   dK^T += Q^T dS (32x32x16 bf16 MFMA; dO^T and Q^T read from the same LDS
 //   rows with the transposing ds_read_b64_tr_b16). Each wave thus holds one
 //   operand row (K or V) and one accumulator (dV or dK), which fits two waves
-//   per SIMD, so one wave's waits are filled by the other's work.
+//   per SIMD, so one wave's waits are filled by the other's work. With a
+//   workspace, a long query range is cut into pieces (one workgroup each)
+//   whose fp32 partials a merge launch sums in a fixed order.
 // * dq, query-stationary (the forward's shape): one workgroup = (sequence,
 //   KV head, 256 / g tokens x g heads), eight waves of 32 columns; Q and dO
 //   rows in registers, key tiles of 64 K and V rows staged in LDS (two
