@@ -14,8 +14,9 @@
 // where the sums over i for a key also run over the g query heads that share
 // its KV head.
 //
-// How (gfx950), launches in order on the caller's stream:
-// * delta: one row per 16 lanes (D = 128), fp32 dot products of the bf16 rows.
+// How (gfx950), on the caller's stream: the dq kernel (which also writes
+// delta), then the dk/dv kernel, then, with a workspace, the merge of cut
+// query ranges:
 // * dk/dv, key-stationary: one workgroup = (sequence, KV head, 128 keys),
 //   eight waves, two per SIMD sharing a group of 32 keys. The (token, query
 //   head) columns that can see the keys go by in blocks of 64 staged in LDS
@@ -29,11 +30,13 @@
 //   per SIMD, so one wave's waits are filled by the other's work. With a
 //   workspace, a long query range is cut into pieces (one workgroup each)
 //   whose fp32 partials a merge launch sums in a fixed order.
-// * dq, query-stationary (the forward's shape): one workgroup = (sequence,
+// * dq (first), query-stationary (the forward's shape): one workgroup = (sequence,
 //   KV head, 256 / g tokens x g heads), eight waves of 32 columns; Q and dO
 //   rows in registers, key tiles of 64 K and V rows staged in LDS (two
 //   stages); S^T = K Q^T and dP^T = V dO^T (lane = column), then
-//   dQ^T += K^T dS^T with K^T read transposed from the K tile.
+//   dQ^T += K^T dS^T with K^T read transposed from the K tile. Each column's
+//   delta = dO . O is formed here from the dO rows in registers and written
+//   for the dk/dv kernel.
 // dq is therefore formed without atomics and every gradient is written once;
 // the cost is recomputing S and dP in the dq kernel (7 products per visible
 // pair instead of 5).
@@ -101,32 +104,6 @@ __device__ __forceinline__ int tr_lane_off(int lane, int db, int r8) {
   const int L16 = lane & 15, hi = lane >> 5;
   const int row = r8 + 4 * hi + (L16 >> 2);
   return row * ROW + 16 * t_chunk<CH>(4 * db + 2 * ((lane >> 4) & 1) + ((L16 >> 1) & 1), row) + 8 * (L16 & 1);
-}
-
-// ---------------------------------------------------------------- delta
-
-template <int D>
-__global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
-  constexpr int CH = D / 8;
-  constexpr int RPB = 256 / CH;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CH;
-  const int c = threadIdx.x % CH;
-  const int64_t nrows = (int64_t)a.B * a.S * a.Hq;
-  const bool ok = row < nrows;
-  const int64_t rr = ok ? row : 0;
-  const int h = (int)(rr % a.Hq);
-  const int64_t bt = rr / a.Hq;
-  const int t = (int)(bt % a.S);
-  const int b = (int)(bt / a.S);
-  float x[8], y[8];
-  load8_f32(static_cast<const __bf16*>(a.o) + b * a.os_b + t * a.os_s + h * a.os_h + 8 * c, x);
-  load8_f32(static_cast<const __bf16*>(a.dout) + b * a.gs_b + t * a.gs_s + h * a.gs_h + 8 * c, y);
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc = fmaf(x[i], y[i], acc);
-#pragma unroll
-  for (int m = CH / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, CH);
-  if (ok && c == 0) a.delta[((int64_t)b * a.Hq + h) * a.S + t] = acc;
 }
 
 // ---------------------------------------------------------------- dk, dv
@@ -402,7 +379,23 @@ void dq_kernel(BwdArgs a, int n_qtiles) {
   }
   const int64_t li = ((int64_t)b * a.Hq + head) * S + tc;
   const float lse2 = a.lse[li] * kLog2e;
-  const float dlt = a.delta[li];
+  // delta of the column, dO . O: this lane's half of the row (the d of its
+  // operand registers) plus the other half from lane l ^ 32; written for the
+  // dk/dv kernel, which runs after this one
+  float dlt = 0.f;
+  {
+    const __bf16* op = static_cast<const __bf16*>(a.o) + b * a.os_b + tc * a.os_s + head * a.os_h + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float x[8];
+      load8_f32(op + 16 * ks, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dlt = fmaf(x[i], (float)greg[ks][i], dlt);
+    }
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(dlt), __float_as_uint(dlt), false, false);
+    dlt = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    if (valid && hi == 0) a.delta[li] = dlt;
+  }
   const int dstart = cu ? doc_start(cu, a.n_docs, tc) : 0;
   // keys dstart .. t are visible: 0 <= key - dstart < lim
   const unsigned lim = valid ? (unsigned)(t - dstart + 1) : 0u;
@@ -567,10 +560,11 @@ __global__ __launch_bounds__(256) void dkdv_merge_kernel(BwdArgs a) {
 
 template <int D, int G>
 hipError_t launch_dg(const BwdArgs& a, hipStream_t st) {
+  // dq first: it also writes delta, which the dk/dv kernel reads
   {
-    const int64_t rows = (int64_t)a.B * a.S * a.Hq;
-    const int rpb = 256 / (D / 8);
-    hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st, a);
+    const int tq = kQCols / G;
+    const int nqt = (a.S + tq - 1) / tq;
+    hipLaunchKernelGGL((dq_kernel<D, G>), dim3(a.B * a.Hkv * nqt), dim3(64 * kQWaves), 0, st, a, nqt);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -587,10 +581,7 @@ hipError_t launch_dg(const BwdArgs& a, hipStream_t st) {
       if (e != hipSuccess) return e;
     }
   }
-  const int tq = kQCols / G;
-  const int nqt = (a.S + tq - 1) / tq;
-  hipLaunchKernelGGL((dq_kernel<D, G>), dim3(a.B * a.Hkv * nqt), dim3(64 * kQWaves), 0, st, a, nqt);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 template <int D>
