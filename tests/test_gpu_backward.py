@@ -82,6 +82,8 @@ def _check_case(B, S, Hq, Hkv, D, seed, cus, softmax_scale=0.0, workspace="nan")
     (1, 450, 128, 8, 128, 205, 4),    # 405B heads (g = 16)
     (1, 390, 16, 4, 128, 206, 6),     # many short documents
     (1, 1500, 32, 8, 128, 210, 1),    # long query ranges cut into pieces (g = 4)
+    (1, 600, 16, 2, 64, 213, 2),      # g = 8, D = 64, cut into pieces
+    (1, 400, 4, 2, 128, 214, 3),      # g = 2
 ])
 def test_backward_matches_oracle(B, S, Hq, Hkv, D, seed, nd):
     H.say("backward", dict(B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, seed=seed, nd=nd))
