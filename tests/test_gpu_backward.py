@@ -206,3 +206,32 @@ def test_backward_is_deterministic_and_writes_in_bounds():
         outs.append((gq.cpu(), gk.cpu(), gv.cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a[:, 1:S + 1], b[:, 1:S + 1])
+
+
+def test_backward_on_views_of_a_packed_projection():
+    """q, k, v as head slices of one [B, S, Hq + 2 Hkv, D] tensor (the output of
+    a fused projection; token stride (Hq + 2 Hkv) D), dq written into a view
+    of a wider buffer: strides are honoured and the result equals the
+    contiguous call's bit for bit."""
+    import gqa_attention_rope_02_amd as la
+    B, S, Hq, Hkv, D = 1, 700, 16, 4, 128
+    H.say("backward on packed views")
+    q, k, v = draw_prefill_inputs(B, S, Hq, Hkv, D, "bf16", 215)
+    dout = _dev(draw_grad_output(B, S, Hq, D, "bf16", 215))
+    cu = _dev(torch.as_tensor(draw_cu_docs(S, 215, 3, 6), dtype=torch.int32).reshape(1, -1))
+    qkv = torch.cat([q, k, v], dim=2).to(torch.device("cuda"))
+    qv, kv_, vv = qkv[:, :, :Hq], qkv[:, :, Hq:Hq + Hkv], qkv[:, :, Hq + Hkv:]
+    qd, kd, vd = qv.contiguous(), kv_.contiguous(), vv.contiguous()
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=qd.device)
+    la.gqa_prefill(qd, kd, vd, o, lse, cu)
+    ref = [torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)]
+    la.gqa_attention_backward(qd, kd, vd, o, dout, lse, *ref, None, cu)
+    wide = torch.full((B, S, 2 * Hq, D), float("nan"), dtype=torch.bfloat16, device=qd.device)
+    gq = wide[:, :, Hq:]
+    gk, gv = torch.empty_like(kd), torch.empty_like(vd)
+    la.gqa_attention_backward(qv, kv_, vv, o, dout, lse, gq, gk, gv, None, cu)
+    torch.cuda.synchronize()
+    assert torch.equal(gq.cpu(), ref[0].cpu()) and torch.equal(gk.cpu(), ref[1].cpu())
+    assert torch.equal(gv.cpu(), ref[2].cpu())
+    assert torch.isnan(wide[:, :, :Hq]).all()
