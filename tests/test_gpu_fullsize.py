@@ -168,3 +168,79 @@ def test_full_size_prefill_is_deterministic(name):
             first = (o, lse)
         else:
             assert torch.equal(first[0], o) and torch.equal(first[1], lse)
+
+
+def test_full_size_chunked_prefill_sampled_rows():
+    """bench.py's chunked prefill: the last 2048 of the llama8b workload's 8192
+    tokens over the cached prefix, gqa_prefill_split with its piece size
+    (queries rotated in the kernel at their positions), sampled block rows
+    against the fp64 row oracle."""
+    import bench
+    import gqa_attention_rope_02_amd as la
+    w = CONFIGS["llama8b"]
+    S, Sq = w.S, 2048
+    H.say("full-size chunked prefill", S, Sq, bench.CHUNK_SPLIT_TILES)
+    q, k, v = draw_prefill_inputs(w.B, w.S, w.Hq, w.Hkv, w.D, w.dtype, w.seed)
+    cu = draw_cu_docs(w.S, w.seed, w.n_docs, w.n_docs_max)
+    dev = torch.device("cuda")
+    kd, vd = k.to(dev), v.to(dev)
+    kr = torch.empty_like(kd)
+    la.rope_qk(None, None, kd, kr)
+    qb = q[:, S - Sq:].contiguous().to(dev)
+    o = torch.full_like(qb, float("nan"))
+    lse = torch.full((w.B, w.Hq, Sq), float("nan"), device=dev)
+    op, lp = la.prefill_split_workspace(w.B, Sq, S, w.Hq, w.D, bench.CHUNK_SPLIT_TILES, dev)
+    cu_d = torch.as_tensor(cu, dtype=torch.int32).reshape(1, -1).to(dev)
+    la.gqa_prefill_split(qb, kr, vd, o, bench.CHUNK_SPLIT_TILES, op, lp, lse, cu_d, rope_base=w.rope_base)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rows = sample_rows(S, cu, w.seed + 1, n_random=512)
+    rows = rows[rows >= S - Sq]
+    idx = torch.as_tensor(rows - (S - Sq), device=dev)
+    Ow, Lw = orc.rope_attention_rows(q[0], k[0], v[0], rows, cu, w.rope_base)
+    H.say("  rows", rows.size)
+    H.assert_close(o[0].index_select(0, idx).cpu(), Ow)
+    H.assert_close(lse[0].index_select(1, idx).cpu(), Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+
+
+def test_full_size_paged_decode_equals_contiguous():
+    """bench.py's paged decode shape (405B decode, 64-slot head-major pages in a
+    seeded random order, its kv_chunk) on pages copied from the contiguous
+    cache: partials and merged output equal gqa_decode's bit for bit (the
+    contiguous decode is checked against the oracle above)."""
+    import bench
+    import gqa_attention_rope_02_amd as la
+    H.say("full-size paged decode405b")
+    st = bench.setup_decode()
+    w, lens, chunk, P = st["w"], st["lens"], bench.KV_CHUNK, bench.PAGE_SIZE
+    st["op"].fill_(float("nan"))
+    st["lp"].fill_(float("nan"))
+    la.gqa_decode(st["q"], st["kc"], st["vc"], st["sl"], chunk, st["op"], st["lp"])
+    la.gqa_decode_combine(st["op"], st["lp"], st["sl"], chunk, st["o"])
+    torch.cuda.synchronize()
+    ref = (st["op"].cpu(), st["lp"].cpu(), st["o"].cpu())
+    need = [-(-int(L) // P) for L in lens]
+    order = np.random.default_rng(w.seed).permutation(int(sum(need)))
+    table = np.zeros((w.B, -(-st["Lmax"] // P)), dtype=np.int32)
+    dev = st["q"].device
+    kp = torch.empty(int(sum(need)), w.Hkv, P, w.D, dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    n = 0
+    for b in range(w.B):
+        ids = order[n:n + need[b]]
+        n += need[b]
+        table[b, :need[b]] = ids
+        idt = torch.as_tensor(ids, device=dev)
+        span = need[b] * P
+        kp.index_copy_(0, idt, st["kc"][b, :, :span].reshape(w.Hkv, need[b], P, w.D).permute(1, 0, 2, 3))
+        vp.index_copy_(0, idt, st["vc"][b, :, :span].reshape(w.Hkv, need[b], P, w.D).permute(1, 0, 2, 3))
+    tb = torch.as_tensor(table).to(dev)
+    op = torch.full_like(st["op"], float("nan"))
+    lp = torch.full_like(st["lp"], float("nan"))
+    o = torch.full_like(st["o"], float("nan"))
+    la.gqa_decode_paged(st["q"], kp.permute(0, 2, 1, 3), vp.permute(0, 2, 1, 3), tb, st["sl"], chunk, op, lp,
+                        st["Lmax"])
+    la.gqa_decode_combine(op, lp, st["sl"], chunk, o)
+    torch.cuda.synchronize()
+    for got, want in zip((op.cpu(), lp.cpu(), o.cpu()), ref):
+        assert torch.equal(torch.nan_to_num(got, nan=7.0), torch.nan_to_num(want, nan=7.0))
