@@ -244,3 +244,48 @@ def test_full_size_paged_decode_equals_contiguous():
     torch.cuda.synchronize()
     for got, want in zip((op.cpu(), lp.cpu(), o.cpu()), ref):
         assert torch.equal(torch.nan_to_num(got, nan=7.0), torch.nan_to_num(want, nan=7.0))
+
+
+def test_full_size_ring_sampled_rows():
+    """bench.py's ring: the llama405b workload as 8 devices of a context-
+    parallel ring would run it (8 shards of 4096 tokens, every query shard
+    against every key shard in ring order, fp32 partials merged, then
+    finalized), all on this GPU; sampled rows (and their LSE) against the fp64
+    row oracle."""
+    import gqa_attention_rope_02_amd as la
+    w = CONFIGS["llama405b"]
+    P = 8
+    S, L = w.S, w.S // P
+    H.say("full-size ring", S, P)
+    q, k, v = draw_prefill_inputs(w.B, w.S, w.Hq, w.Hkv, w.D, w.dtype, w.seed)
+    cu = draw_cu_docs(w.S, w.seed, w.n_docs, w.n_docs_max)
+    dev = torch.device("cuda")
+    qd, vd = q.to(dev), v.to(dev)
+    kr = torch.empty_like(k.to(dev))
+    la.rope_qk(None, None, k.to(dev), kr)
+    cu_d = torch.as_tensor(cu, dtype=torch.int32).reshape(1, -1).to(dev)
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((w.B, w.Hq, S), float("nan"), device=dev)
+    oa = torch.empty(w.B, L, w.Hq, w.D, dtype=torch.float32, device=dev)
+    lsa = torch.empty(w.B, w.Hq, L, dtype=torch.float32, device=dev)
+    lb = torch.empty(w.B, w.Hq, L, dtype=torch.float32, device=dev)
+    for i in range(P):
+        q0 = i * L
+        for step in range(P):
+            j = (i - step) % P
+            la.gqa_prefill_ring_step(qd[:, q0:q0 + L], kr[:, j * L:(j + 1) * L], vd[:, j * L:(j + 1) * L],
+                                     q0, j * L, oa, lsa, first=(step == 0), cu_docs=cu_d,
+                                     rope_base=w.rope_base)
+        la.gqa_prefill_ring_finalize(oa, lsa, o[:, q0:q0 + L], lb)
+        lse[:, :, q0:q0 + L] = lb
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rows = sample_rows(S, cu, w.seed + 2, n_random=256, n_edges=32)
+    idx = torch.as_tensor(rows, device=dev)
+    got_o = o[0].index_select(0, idx).cpu()
+    got_l = lse[0].index_select(1, idx).cpu()
+    del o, lse, oa
+    Ow, Lw = orc.rope_attention_rows(q[0], k[0], v[0], rows, cu, w.rope_base)
+    H.say("  rows", rows.size)
+    H.assert_close(got_o, Ow)
+    H.assert_close(got_l, Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
