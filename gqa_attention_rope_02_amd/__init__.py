@@ -115,6 +115,14 @@ def _dtype(t) -> int:
     return _DT[t.dtype]
 
 
+def _same_dtype(call, dt, **tensors):
+    """Every given tensor must have dtype dt (the kernels index all of a call's
+    tensors with one element size)."""
+    for name, t in tensors.items():
+        if t is not None and t.dtype != dt:
+            raise ValueError(f"{call}: {name} is {t.dtype}, the call's tensors are {dt}")
+
+
 def _strides(t, n):
     if t is None:
         return None
@@ -150,6 +158,7 @@ def rope_qk(q_in, q_out, k_in=None, k_out=None, positions=None, rope_base: float
         raise ValueError("rope_qk: q and k must share B, S and D")
     if positions is not None and tuple(positions.shape) != (B, S):
         raise ValueError("rope_qk: positions must be [B, S]")
+    _same_dtype("rope_qk", ref.dtype, q_in=q_in, q_out=q_out, k_in=k_in, k_out=k_out)
     st = _lib.load().rope_qk(
         _dev(q_in), _dev(q_out), _strides(q_in, 3), _strides(q_out, 3),
         _dev(k_in), _dev(k_out), _strides(k_in, 3), _strides(k_out, 3),
@@ -169,6 +178,7 @@ def rope_qk_backward(dq_in, dq_out, dk_in=None, dk_out=None, positions=None,
         raise ValueError("rope_qk_backward: dq and dk must share B, S and D")
     if positions is not None and tuple(positions.shape) != (B, S):
         raise ValueError("rope_qk_backward: positions must be [B, S]")
+    _same_dtype("rope_qk_backward", ref.dtype, dq_in=dq_in, dq_out=dq_out, dk_in=dk_in, dk_out=dk_out)
     st = _lib.load().rope_qk_backward(
         _dev(dq_in), _dev(dq_out), _strides(dq_in, 3), _strides(dq_out, 3),
         _dev(dk_in), _dev(dk_out), _strides(dk_in, 3), _strides(dk_out, 3),
@@ -201,6 +211,7 @@ def gqa_attention_backward(q, k, v, o, dout, lse, dq, dk, dv, delta=None, cu_doc
         raise ValueError("gqa_attention_backward: delta must be [B, Hq, S]")
     if cu_docs is not None and (cu_docs.dim() != 2 or cu_docs.shape[0] != B):
         raise ValueError("gqa_attention_backward: cu_docs must be [B, n_docs + 1]")
+    _same_dtype("gqa_attention_backward", torch.bfloat16, q=q, k=k, v=v, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("gqa_attention_backward: workspace must be a tensor, None or 'auto'")
@@ -229,6 +240,7 @@ def gqa_prefill(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float = 0.0):
         raise ValueError("gqa_prefill: lse must be [B, Hq, S]")
     if cu_docs is not None and (cu_docs.dim() != 2 or cu_docs.shape[0] != B):
         raise ValueError("gqa_prefill: cu_docs must be [B, n_docs + 1]")
+    _same_dtype("gqa_prefill", q.dtype, k=k, v=v, o=o)
     st = _lib.load().gqa_prefill(
         _dev(q), _dev(k), _dev(v), _dev(o), _f32c(lse), _dtype(q), B, S, Hq, Hkv, D,
         _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
@@ -250,6 +262,7 @@ def gqa_prefill_rope(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float = 
         raise ValueError("gqa_prefill_rope: cu_docs must be [B, n_docs + 1]")
     if positions is not None and tuple(positions.shape) != (B, S):
         raise ValueError("gqa_prefill_rope: positions must be [B, S]")
+    _same_dtype("gqa_prefill_rope", q.dtype, k=k, v=v, o=o)
     st = _lib.load().gqa_prefill_rope(
         _dev(q), _dev(k), _dev(v), _dev(o), _f32c(lse), _dtype(q), B, S, Hq, Hkv, D,
         _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
@@ -272,6 +285,7 @@ def gqa_prefill_chunk(q, k, v, o, lse=None, cu_docs=None, softmax_scale: float =
         raise ValueError("gqa_prefill_chunk: cu_docs must be [B, n_docs + 1]")
     if positions is not None and tuple(positions.shape) != (B, Sq):
         raise ValueError("gqa_prefill_chunk: positions must be [B, Sq]")
+    _same_dtype("gqa_prefill_chunk", q.dtype, k=k, v=v, o=o)
     st = _lib.load().gqa_prefill_chunk(
         _dev(q), _dev(k), _dev(v), _dev(o), _f32c(lse), _dtype(q), B, Sq, S, Hq, Hkv, D,
         _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(o, 3),
@@ -304,6 +318,7 @@ def gqa_prefill_split(q, k, v, o, split_tiles: int, o_part, lse_part, lse=None, 
         raise ValueError("gqa_prefill_split: cu_docs must be [B, n_docs + 1]")
     if positions is not None and tuple(positions.shape) != (B, Sq):
         raise ValueError("gqa_prefill_split: positions must be [B, Sq]")
+    _same_dtype("gqa_prefill_split", q.dtype, k=k, v=v, o=o)
     if tuple(o_part.shape) != (max_splits, B, Sq, Hq, D) or tuple(lse_part.shape) != (max_splits, B, Hq, Sq) \
             or o_part.dtype != torch.float32 or lse_part.dtype != torch.float32 \
             or not o_part.is_contiguous() or not lse_part.is_contiguous():
@@ -336,6 +351,7 @@ def gqa_prefill_ring_step(q, k, v, q_off: int, k_off: int, o_acc, lse_acc, first
         raise ValueError("gqa_prefill_ring_step: cu_docs must be [B, n_docs + 1]")
     if positions is not None and tuple(positions.shape) != (B, Sq):
         raise ValueError("gqa_prefill_ring_step: positions must be [B, Sq]")
+    _same_dtype("gqa_prefill_ring_step", q.dtype, k=k, v=v)
     st = _lib.load().gqa_prefill_ring_step(
         _dev(q), _dev(k), _dev(v), _dev(o_acc), _dev(lse_acc), _dtype(q), B, Sq, int(q_off), Skv,
         int(k_off), Hq, Hkv, D, _strides(q, 3), _strides(k, 3), _strides(v, 3), _i32(cu_docs),
@@ -351,7 +367,7 @@ def gqa_prefill_ring_finalize(o_acc, lse_acc, o, lse=None):
     if lse is not None and tuple(lse.shape) != (B, Hq, Sq):
         raise ValueError("gqa_prefill_ring_finalize: lse must be [B, Hq, Sq]")
     st = _lib.load().gqa_prefill_ring_finalize(
-        _dev(o_acc), _dev(lse_acc), _dev(o), _strides(o, 3), _f32c(lse), _dtype(o), B, Sq, Hq, D,
+        _f32c(o_acc), _f32c(lse_acc), _dev(o), _strides(o, 3), _f32c(lse), _dtype(o), B, Sq, Hq, D,
         _stream())
     _check(st, "gqa_prefill_ring_finalize")
 
@@ -367,6 +383,7 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk: int, o_part, lse_part,
     if k_cache.shape[0] != B or k_cache.shape[3] != D or tuple(o_part.shape) != (B, Hq, max_splits, D) \
             or tuple(lse_part.shape) != (B, Hq, max_splits) or tuple(seq_lens.shape) != (B,):
         raise ValueError("gqa_decode: inconsistent shapes")
+    _same_dtype("gqa_decode", torch.bfloat16, q=q, k_cache=k_cache, v_cache=v_cache)
     st = _lib.load().gqa_decode(
         _dev(q), _strides(q, 2), _dev(k_cache), _dev(v_cache), _strides(k_cache, 3),
         _i32(seq_lens), B, Hq, Hkv, D, Lmax, int(kv_chunk), max_splits, float(softmax_scale),
@@ -385,6 +402,7 @@ def gqa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, kv_chunk: int, 
             or tuple(lse_part.shape) != (B, Hq, max_splits) or tuple(seq_lens.shape) != (B,) \
             or block_table.dim() != 2 or block_table.shape[0] != B or block_table.stride(1) != 1:
         raise ValueError("gqa_decode_paged: inconsistent shapes")
+    _same_dtype("gqa_decode_paged", torch.bfloat16, q=q, k_pages=k_pages, v_pages=v_pages)
     ps = k_pages.stride()
     if ps[-1] != 1:
         raise ValueError("the last (head_dim) dimension must be contiguous")
@@ -392,7 +410,7 @@ def gqa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, kv_chunk: int, 
     st = _lib.load().gqa_decode_paged(
         _dev(q), _strides(q, 2), _dev(k_pages), _dev(v_pages), page_strides, page_size,
         _i32(block_table), block_table.stride(0), _i32(seq_lens), B, Hq, Hkv, D, int(Lmax),
-        int(kv_chunk), max_splits, float(softmax_scale), _dev(o_part), _dev(lse_part), _stream())
+        int(kv_chunk), max_splits, float(softmax_scale), _f32c(o_part), _f32c(lse_part), _stream())
     _check(st, "gqa_decode_paged")
 
 

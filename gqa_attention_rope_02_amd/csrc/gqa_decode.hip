@@ -399,18 +399,11 @@ __global__ __launch_bounds__(256) void combine_kernel_f(CombineArgs a, int dt) {
   if (a.lse && lane == 0) a.lse[pair] = M + logf(W);
 }
 
-int g_num_cu = 0;   // the grid size only shapes the work split, never the result
-
 template <int D, int G>
 hipError_t launch_dt(const DecodeArgs& a, hipStream_t st) {
-  if (g_num_cu == 0) {
-    int dev = 0;
-    hipGetDevice(&dev);
-    hipDeviceGetAttribute(&g_num_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (g_num_cu <= 0) g_num_cu = 256;
-  }
-  // persistent grid: one workgroup per CU (the LDS ring takes most of a CU's LDS)
-  const unsigned grid = (unsigned)g_num_cu;
+  // persistent grid: one workgroup per CU (the LDS ring takes most of a CU's
+  // LDS); the grid size only shapes the work split, never the result
+  const unsigned grid = (unsigned)(a.grid > 0 ? a.grid : 256);
   if (a.block_table)
     hipLaunchKernelGGL((decode_kernel<D, G, true>), dim3(grid), dim3(64 * kWaves), 0, st, a);
   else

@@ -77,6 +77,7 @@ struct DecodeArgs {
   // cs_b is then the page stride
   const int32_t* block_table;
   int bt_stride, page_shift;
+  int grid;                   // workgroups of the persistent grid (compute units)
 };
 
 struct CombineArgs {

@@ -1,11 +1,15 @@
 // Host side of the C ABI declared in include/llama_attn.h: argument checks
 // (all made before anything is enqueued), variant selection, and launches on
-// the caller's stream. The library allocates nothing and keeps no state.
+// the caller's stream. The library allocates no device memory; its only
+// state is a per-device compute-unit count read once.
 #include "llama_attn.h"
 
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <mutex>
+#include <vector>
 
 #include "kernels.hpp"
 
@@ -31,6 +35,99 @@ bool strides_ok(const int64_t* s, int n, int esize) {
 
 la_status launched(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH; }
 
+// ---- compute units per device, read once per process --------------------
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];
+std::once_flag g_cu_once;
+
+// The current device's compute-unit count (the persistent decode grid);
+// 256 if the runtime cannot tell. The table is filled once, under
+// std::call_once, so concurrent first calls from several threads are safe.
+int current_cu_count() {
+  std::call_once(g_cu_once, [] {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess) n = 0;
+    for (int d = 0; d < kMaxDevices; ++d) {
+      int c = 0;
+      if (d >= n || hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) c = 0;
+      g_cu_count[d] = c > 0 ? c : 256;
+    }
+  });
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  return g_cu_count[dev];
+}
+
+// ---- LLAMA_ATTN_DEBUG=1: contents of the device index arrays -------------
+// The environment variable is read at every call. When it is "1", a call
+// first copies the device-resident index arrays it was given (document
+// offsets, sequence lengths, positions, block tables) to the host on the
+// caller's stream, waits for that stream, and returns LA_ERR_INVALID_ARG
+// without launching anything if a value breaks the call's contract. This
+// synchronises the stream, so it is a debugging aid, not for graph capture.
+bool debug_mode() {
+  const char* e = std::getenv("LLAMA_ATTN_DEBUG");
+  return e != nullptr && e[0] == '1' && e[1] == '\0';
+}
+
+bool fetch_i32(const int32_t* d, int64_t n, hipStream_t st, std::vector<int32_t>& h) {
+  h.assign((size_t)std::max<int64_t>(n, 0), 0);
+  if (n <= 0) return true;
+  if (hipMemcpyAsync(h.data(), d, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return false;
+  return hipStreamSynchronize(st) == hipSuccess;
+}
+
+// Document offsets [B, n_docs + 1]: each row starts at 0, never decreases and
+// ends at `end` (at or past `end` when exact is false).
+bool docs_ok(const int32_t* cu, int B, int n_docs, int64_t end, bool exact, hipStream_t st) {
+  if (!cu) return true;
+  std::vector<int32_t> h;
+  if (!fetch_i32(cu, (int64_t)B * (n_docs + 1), st, h)) return false;
+  for (int b = 0; b < B; ++b) {
+    const int32_t* r = h.data() + (size_t)b * (n_docs + 1);
+    if (r[0] != 0) return false;
+    for (int d = 0; d < n_docs; ++d)
+      if (r[d + 1] < r[d]) return false;
+    if (exact ? r[n_docs] != end : r[n_docs] < end) return false;
+  }
+  return true;
+}
+
+// Positions [n]: non-negative token positions.
+bool positions_ok(const int32_t* pos, int64_t n, hipStream_t st) {
+  if (!pos) return true;
+  std::vector<int32_t> h;
+  if (!fetch_i32(pos, n, st, h)) return false;
+  for (int32_t x : h)
+    if (x < 0) return false;
+  return true;
+}
+
+// Sequence lengths [B]: lo <= L <= hi.
+bool lens_ok(const int32_t* lens, int B, int64_t lo, int64_t hi, hipStream_t st) {
+  std::vector<int32_t> h;
+  if (!fetch_i32(lens, B, st, h)) return false;
+  for (int32_t x : h)
+    if (x < lo || x > hi) return false;
+  return true;
+}
+
+// Block table rows [B] of bt_stride entries: the pages that hold slots
+// 0 .. seq_lens[b] - 1 are named by non-negative ids.
+bool block_table_ok(const int32_t* table, int bt_stride, const int32_t* lens, int B, int page_size,
+                    hipStream_t st) {
+  std::vector<int32_t> t, l;
+  if (!fetch_i32(lens, B, st, l) || !fetch_i32(table, (int64_t)B * bt_stride, st, t)) return false;
+  for (int b = 0; b < B; ++b) {
+    const int64_t pages = ((int64_t)l[b] + page_size - 1) / page_size;
+    if (pages > bt_stride) return false;
+    for (int64_t j = 0; j < pages; ++j)
+      if (t[(size_t)b * bt_stride + j] < 0) return false;
+  }
+  return true;
+}
+
 // theta_k = base^(-2k/D) (the RoPE frequencies), divided by 2 pi: the kernels
 // form the angles in revolutions
 void theta_revolutions(double base, int D, double* out) {
@@ -53,6 +150,8 @@ const char* la_status_str(la_status s) {
 }
 
 int la_version(void) { return kVersion; }
+
+}  // extern "C"
 
 namespace {
 
@@ -82,6 +181,8 @@ la_status rope_impl(const void* q_in, void* q_out, const int64_t q_in_strides[3]
                 !strides_ok(k_out_strides, 3, es)))
     return LA_ERR_INVALID_ARG;
 
+  if (debug_mode() && !positions_ok(positions, (int64_t)B * S, stream)) return LA_ERR_INVALID_ARG;
+
   la::RopeArgs qa{}, ka{};
   if (has_q) {
     qa = la::RopeArgs{q_in, q_out, q_in_strides[0], q_in_strides[1], q_in_strides[2],
@@ -100,6 +201,8 @@ la_status rope_impl(const void* q_in, void* q_out, const int64_t q_in_strides[3]
 }
 
 }  // namespace
+
+extern "C" {
 
 la_status rope_qk(const void* q_in, void* q_out, const int64_t q_in_strides[3],
                   const int64_t q_out_strides[3], const void* k_in, void* k_out,
@@ -121,6 +224,8 @@ la_status rope_qk_backward(const void* dq_in, void* dq_out, const int64_t dq_in_
                    dk_out_strides, dt, B, S, Hq, Hkv, D, positions, rope_base, rope_pairing, -1,
                    stream);
 }
+
+}  // extern "C"
 
 namespace {
 
@@ -158,6 +263,10 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
   // key/value rows of consecutive tokens may not overlap (tiles are fetched
   // with a byte range that ends at the last token's row)
   if (k_strides[1] < D || v_strides[1] < D) return LA_ERR_INVALID_ARG;
+  // a 64-key tile is fetched through one buffer descriptor whose per-lane byte
+  // offsets are 32-bit: its rows must span less than 2 GiB
+  if (64 * k_strides[1] * es > 0x7fffffffLL || 64 * v_strides[1] * es > 0x7fffffffLL)
+    return LA_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return LA_ERR_INVALID_ARG;
   const int G = Hq / Hkv;
   const int tq = la::prefill_tokens_per_block(G);
@@ -170,6 +279,13 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
     const long long need = ((S + 63) / 64 + split_tiles - 1) / split_tiles;
     if (max_splits < need || max_splits > 65535) return LA_ERR_INVALID_ARG;
     if ((long long)max_splits * B * Sq * Hq * D > (1LL << 46)) return LA_ERR_INVALID_ARG;
+  }
+
+  if (debug_mode()) {
+    // key positions end at S (or, for a ring step, the offsets cover both shards)
+    const int64_t end = ring ? std::max<int64_t>((int64_t)q_off + Sq, (int64_t)k_off + S) : S;
+    if (!docs_ok(cu_docs, B, n_docs, end, !ring, stream)) return LA_ERR_INVALID_ARG;
+    if (rope_base > 0.0 && !positions_ok(positions, (int64_t)B * Sq, stream)) return LA_ERR_INVALID_ARG;
   }
 
   la::PrefillArgs a{};
@@ -207,6 +323,8 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
 }
 
 }  // namespace
+
+extern "C" {
 
 la_status gqa_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                       la_dtype dt, int B, int S, int Hq, int Hkv, int D,
@@ -293,6 +411,8 @@ la_status gqa_prefill_ring_finalize(const float* o_acc, const float* lse_acc, vo
   return launched(la::launch_prefill_merge(a, D, dt == LA_BF16 ? 0 : 1, stream));
 }
 
+}  // extern "C"
+
 namespace {
 
 la_status decode_check(const void* q, const int64_t q_strides[2], const void* k_cache,
@@ -336,10 +456,13 @@ la::DecodeArgs decode_args(const void* q, const int64_t q_strides[2], const void
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.o_part = o_part; a.lse_part = lse_part;
+  a.grid = current_cu_count();
   return a;
 }
 
 }  // namespace
+
+extern "C" {
 
 la_status gqa_decode(const void* q, const int64_t q_strides[2], const void* k_cache,
                      const void* v_cache, const int64_t cache_strides[3],
@@ -350,6 +473,7 @@ la_status gqa_decode(const void* q, const int64_t q_strides[2], const void* k_ca
                                     Hkv, D, Lmax, kv_chunk, max_splits, softmax_scale, o_part,
                                     lse_part);
   if (st != LA_OK) return st;
+  if (debug_mode() && !lens_ok(seq_lens, B, 1, Lmax, stream)) return LA_ERR_INVALID_ARG;
   const la::DecodeArgs a = decode_args(q, q_strides, k_cache, v_cache, cache_strides, seq_lens, B,
                                        Hq, Hkv, D, Lmax, kv_chunk, max_splits, softmax_scale,
                                        o_part, lse_part);
@@ -373,6 +497,9 @@ la_status gqa_decode_paged(const void* q, const int64_t q_strides[2], const void
   la_status st = decode_check(q, q_strides, k_pages, v_pages, cache_strides, seq_lens, B, Hq, Hkv,
                               D, Lmax, kv_chunk, max_splits, softmax_scale, o_part, lse_part);
   if (st != LA_OK) return st;
+  if (debug_mode() && (!lens_ok(seq_lens, B, 1, Lmax, stream) ||
+                       !block_table_ok(block_table, bt_stride, seq_lens, B, page_size, stream)))
+    return LA_ERR_INVALID_ARG;
   la::DecodeArgs a = decode_args(q, q_strides, k_pages, v_pages, cache_strides, seq_lens, B, Hq,
                                  Hkv, D, Lmax, kv_chunk, max_splits, softmax_scale, o_part,
                                  lse_part);
@@ -395,6 +522,10 @@ la_status gqa_decode_combine(const float* o_part, const float* lse_part, const i
   if (!supported_d(D)) return LA_ERR_UNSUPPORTED;
   if (!o_strides || o_strides[0] < 0 || o_strides[1] < 0) return LA_ERR_INVALID_ARG;
   if ((long long)B * Hq > 0x7fffffffLL - 3) return LA_ERR_INVALID_ARG;
+  // the workspace gqa_decode writes (16-byte aligned rows)
+  if (!aligned16(o_part) || (reinterpret_cast<uintptr_t>(lse_part) & 3u) != 0) return LA_ERR_INVALID_ARG;
+  if (debug_mode() && !lens_ok(seq_lens, B, 1, (int64_t)max_splits * kv_chunk, stream))
+    return LA_ERR_INVALID_ARG;
 
   la::CombineArgs a{};
   a.o_part = o_part; a.lse_part = lse_part; a.seq_lens = seq_lens;
@@ -403,6 +534,8 @@ la_status gqa_decode_combine(const float* o_part, const float* lse_part, const i
   a.lse = lse;
   return launched(la::launch_combine(a, D, dt == LA_BF16 ? 0 : 1, stream));
 }
+
+}  // extern "C"
 
 namespace {
 
@@ -413,6 +546,8 @@ bool bwd_rows_ok(const int64_t* st, int H, int D) {
 }
 
 }  // namespace
+
+extern "C" {
 
 la_status gqa_attention_backward(const void* q, const void* k, const void* v, const void* o,
                                  const void* dout, const float* lse, float* delta, void* dq,
@@ -446,6 +581,7 @@ la_status gqa_attention_backward(const void* q, const void* k, const void* v, co
   if ((long long)B * Hkv * std::max(nkb, (S + tq - 1) / tq) > 0x7fffffffLL) return LA_ERR_INVALID_ARG;
   if ((long long)B * S * Hq > (1LL << 40)) return LA_ERR_INVALID_ARG;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+  if (debug_mode() && !docs_ok(cu_docs, B, n_docs, S, true, stream)) return LA_ERR_INVALID_ARG;
 
   la::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.delta = delta;
