@@ -21,23 +21,22 @@
 //   already has the layout of the P^T operand.
 // * Q stays in registers for the whole key loop. K and V tiles of 64 keys go
 //   from HBM straight into LDS (buffer_load_dwordx4 ... lds, no register
-//   staging), row-major with XOR swizzles, through four stages: a tile is
-//   issued three tiles before it is read. The buffer descriptor moves with the
-//   tile and its size ends at the sequence end, so rows past the end read as
-//   zero. K operands are read with ds_read_b128; the V^T operand with the
-//   transposing ds_read_b64_tr_b16 from the row-major V tile. The four K
-//   stages fill the first 64 KB of LDS and the four V stages the second; the
-//   tile loop is unrolled over the stages, so every operand read is one
-//   per-lane address register plus a constant offset (no address arithmetic
-//   in the loop).
-// * The two waves of a SIMD run one phase apart ("ping-pong"): each wave
-//   alternates an MFMA phase (PV of tile k and QK of tile k+1: 32 MFMAs and
-//   their 48 operand reads, kept eight reads ahead) with a softmax phase
-//   (mask, max, exp, bf16 rounding, row sums of tile k+1), every phase ends at
-//   a workgroup barrier, and the other wave of the SIMD is then in the other
-//   kind of phase. On gfx950 the VALU work of one wave and the MFMAs of the
-//   other do not run concurrently; what the offset buys is that each wave's
-//   waits (MFMA results, LDS reads, exp latency) are filled by the other.
+//   staging), row-major with XOR swizzles, through two rings of four stages
+//   (K in the first 64 KB of LDS, V in the second). The buffer descriptor
+//   moves with the tile and its size ends at the sequence end, so rows past
+//   the end read as zero. K operands are read with ds_read_b128; the V^T
+//   operand with the transposing ds_read_b64_tr_b16 from the row-major V tile.
+// * Software pipeline, one workgroup barrier per tile: between two barriers
+//   every wave runs the PV product of the previous tile with the score FMA of
+//   the current one interleaved, then the QK product of the next tile with the
+//   exponentials, bf16 rounding and row sums of the current one interleaved.
+//   Each piece (one MFMA, its operand read a few MFMAs ahead, two VALU or
+//   transcendental operations) is emitted in program order and fenced, so a
+//   wave keeps its matrix core and its VALU busy at the same time (on gfx950
+//   a wave's own independent VALU work issues while its MFMA runs); the two
+//   waves of a SIMD fill each other's waits. The loop is unrolled over the
+//   four stage indices, so every LDS operand address is a per-lane register
+//   plus a constant offset.
 // * Online softmax in the base-2 domain with fp32 statistics; probabilities
 //   are rounded to bf16 once and the row sums accumulate those rounded values
 //   (v_dot2_f32_bf16), so numerator and denominator use the same weights. The
@@ -71,6 +70,7 @@ namespace {
 constexpr int kCols = 256;    // columns per workgroup
 constexpr int kNW = 8;        // waves per workgroup
 constexpr int kCB = kCols / kNW / 32;   // 32-column blocks per wave
+static_assert(kCB == 1, "one 32-column block per wave");
 constexpr int kKT = 64;       // keys per tile
 constexpr float kLazyW = 256.f;   // bound on a weight under the lazily moved softmax reference
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
@@ -245,19 +245,16 @@ void prefill_kernel(PrefillArgs a) {
     n_tiles = min(a.split_tiles, n_tiles - sp * a.split_tiles);
   }
 
-  f32x16 acc[DB][kCB];
+  // ---- online-softmax state of this lane's column ------------------------------
+  // Mref: the reference the exponents are taken against, in log2 units
+  // (scale * log2(e) * score); -inf until the column has seen a visible key.
+  // negM: what the score FMA adds (-Mref, or 0 while Mref is -inf).
+  f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[db][cb][j] = 0.f;
-  float m[kCB], l[kCB];
-#pragma unroll
-  for (int cb = 0; cb < kCB; ++cb) {
-    m[cb] = -INFINITY;
-    l[cb] = 0.f;
-  }
+    for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
+  float Mref = -INFINITY, negM = 0.f, l = 0.f;
 
   // ---- tile staging: per-lane byte offsets of this wave's 1 KB loads --------
   int koff[NL], voff[NL];
@@ -268,37 +265,39 @@ void prefill_kernel(PrefillArgs a) {
     koff[n] = (int)(row * a.ks_s * (int64_t)sizeof(T) + 8 * k_chunk<CH>(ph, row) * (int)sizeof(T));
     voff[n] = (int)(row * a.vs_s * (int64_t)sizeof(T) + 8 * v_chunk<CH>(ph, row) * (int)sizeof(T));
   }
-  auto stage = [&](int kt, char* dst) __attribute__((always_inline)) {
+  // The K (V) rows of the tile at key position kt into the stage at dst: rows
+  // at or past kend read as zero. bf16: this wave's NL direct-to-LDS loads,
+  // tracked by vmcnt; fp32: converted to bf16 through registers and written
+  // with ds_write (complete once lgkmcnt drains).
+  auto stage_kv = [&](int kt, char* dst, bool is_v) __attribute__((always_inline)) {
+    const T* base = is_v ? vbase : kbase;
+    const int64_t ss = is_v ? a.vs_s : a.ks_s;
     if constexpr (std::is_same<T, __bf16>::value) {
-      const int64_t rows = max(kend - kt, 0);   // rows past the last key read as zero
-      const int kb_ = (int)min(rows * a.ks_s * 2, (int64_t)0x7fffffff);
-      const int vb_ = (int)min(rows * a.vs_s * 2, (int64_t)0x7fffffff);
-      const void* kp = kbase + (int64_t)(kt - k_off) * a.ks_s;
-      const void* vp = vbase + (int64_t)(kt - k_off) * a.vs_s;
+      const int64_t rows = max(kend - kt, 0);
+      const int nb = (int)min(rows * ss * 2, (int64_t)0x7fffffff);
+      const void* p = base + (int64_t)(kt - k_off) * ss;
 #pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        load_lds16(kp, kb_, koff[n], dst + (n * kNW + wave) * 1024);
-        load_lds16(vp, vb_, voff[n], dst + 4 * TILE + (n * kNW + wave) * 1024);
-      }
-    } else {   // fp32 inputs: convert to bf16 on the way into LDS
+      for (int n = 0; n < NL; ++n)
+        load_lds16(p, nb, is_v ? voff[n] : koff[n], dst + (n * kNW + wave) * 1024);
+    } else {
       for (int p = tid; p < kKT * CH; p += 64 * kNW) {
         const int row = p / CH, ph = p % CH;
         const int j = kt + row;
-        bf16x8 kv = zero_bf16x8(), vv = zero_bf16x8();
-        if (j < kend) {
-          kv = load8(kbase + (int64_t)(j - k_off) * a.ks_s + 8 * k_chunk<CH>(ph, row));
-          vv = load8(vbase + (int64_t)(j - k_off) * a.vs_s + 8 * v_chunk<CH>(ph, row));
-        }
-        *reinterpret_cast<bf16x8*>(dst + p * 16) = kv;
-        *reinterpret_cast<bf16x8*>(dst + 4 * TILE + p * 16) = vv;
+        bf16x8 x = zero_bf16x8();
+        if (j < kend) x = load8(base + (int64_t)(j - k_off) * ss + 8 * (is_v ? v_chunk<CH>(ph, row) : k_chunk<CH>(ph, row)));
+        *reinterpret_cast<bf16x8*>(dst + p * 16) = x;
       }
     }
   };
+  // tile k's key position; tiles past the last one load nothing (zero rows),
+  // so every wave has the same loads in flight at every wait
+  auto tile_kt = [&](int k) __attribute__((always_inline)) { return k < n_tiles ? kv_lo + k * kKT : kend; };
 
   // ---- per-lane LDS operand offsets ------------------------------------------
   // K operand: row 32kb + lc, logical chunk 2ks + hi.
   const int k_lane = lc * ROW;
   const int k_x = hi ^ (lc & (CH - 1));              // physical chunk = (2ks) ^ k_x
+  const int k_row_x = k_lane + 16 * k_x;
   // V^T operand (transposing read): the 16-lane group g = lane/16 covers
   // d = 32db + 16(g&1) + (lane&15) and keys 16ks + 4hi (+8) + 0..3; its input
   // lane L = lane&15 addresses row 16ks + 4hi + L/4 at d0 = 32db + 16(g&1) + 4(L%4).
@@ -316,160 +315,231 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) v_lane[db] += v_region;
 
-  // ---- ping-pong schedule ------------------------------------------------------
-  // Waves w and w + 4 share a SIMD; they form groups A (waves 0-3) and B (4-7).
-  // Work of a wave per tile k: QK(k) (MFMA), SM(k) (mask + softmax, VALU),
-  // PV(k) (MFMA). Every wave runs QK(0) | SM(0) | X(0) | SM(1) | X(1) | ... |
-  // X(n-1), X(k) = PV(k) + QK(k+1); group B runs it one phase behind group A
-  // and every phase ends with a workgroup barrier, so in every phase one wave
-  // of each SIMD feeds the matrix core while the other runs its softmax on the
-  // VALU. K/V: four LDS stages; tile k+3 is issued at the start of iteration k
-  // (phase 2k+2, when the stage of tile k-1 is free in both groups) and must
-  // have landed at the end of phase 2k+5, before its first read in phase 2k+6.
-  const int group = wave >> 2;
-  auto stage_ptr = [&](int k) __attribute__((always_inline)) -> char* { return lds + (k & 3) * TILE; };
-  // tiles past the last one are issued as loads that read nothing, so every
-  // wave has the same number of loads in flight at every wait
-  auto issue = [&](int k) __attribute__((always_inline)) { stage(k < n_tiles ? kv_lo + k * kKT : kend, stage_ptr(k)); };
-  auto barrier = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(kLgkm0);   // this wave's LDS reads are done
+  // ---- the tile pipeline -----------------------------------------------------
+  // K and V tiles go through separate four-stage rings: K of tile j in
+  // K stage j % 4 (lds + (j % 4) TILE), V of tile j in V stage j % 4 (V region,
+  // lds + (4 + j % 4) TILE). Barrier B(k) ends iteration k. Between B(k-1) and
+  // B(k) every wave runs, for its 32 columns:
+  //   PV(k-1): 4 DB MFMAs O^T += V^T P^T of tile k-1, with the scale FMA
+  //            t = s * scale * log2(e) - Mref of tile k interleaved;
+  //   the causal/document mask of tile k (edge tiles only);
+  //   QK(k+1): 2 KS MFMAs S^T = K Q^T of tile k+1, with the exponentials,
+  //            bf16 rounding and row sums of tile k interleaved;
+  //   the lazy reference check of tile k.
+  // Operand reads run PF MFMAs ahead of their use, across the phase boundary
+  // and across the barrier. Each piece of work is emitted in program order and
+  // fenced (sched_barrier), so every wave keeps its own matrix core and VALU
+  // busy at once; the two waves of a SIMD fill each other's waits.
+  // Loads: in iteration k a wave issues K of tile k+3 (into the stage of
+  // K(k-1), last read before B(k-2)) and V of tile k+2 (the stage of V(k-2),
+  // last read before B(k-1)); before B(k) it waits until only the loads it
+  // issued in iteration k may be pending, so K(k+2) and V(k+1), the first
+  // tiles read after B(k), have landed for every wave once B(k) passes.
+  constexpr int NQ = 2 * KS;      // QK MFMAs per tile
+  constexpr int NP = 4 * DB;      // PV MFMAs per tile
+  constexpr int PF = 3;           // operand reads ahead
+  constexpr int EQ = 32 / NQ;     // scores per lane exponentiated per QK MFMA
+  constexpr int EP = 32 / NP;     // scores per lane scaled per PV MFMA
+  static_assert(PF <= NQ && PF <= NP && EQ % 2 == 0, "pipeline shape");
+  char* const kst[4] = {lds, lds + TILE, lds + 2 * TILE, lds + 3 * TILE};
+  char* const vst[4] = {lds + 4 * TILE, lds + 5 * TILE, lds + 6 * TILE, lds + 7 * TILE};
+
+  // t of the tile being exponentiated and its weights, one register per value
+  // (flat index e = 16 kb + j of the S^T accumulator element j of key block
+  // kb), so each frees as soon as it is used; S^T of the next tile is the pair
+  // of MFMA accumulators sn
+  float sc[32];
+  uint32_t pw[16];                // weights e, e+1 as a bf16 pair in pw[e / 2]
+  f32x16 sn[2];
+  bf16x8 kbuf[NQ], vbuf[NP];      // operands read ahead
+  float rs = 0.f;                 // this lane's sum of the tile's rounded weights
+
+  // operand of QK MFMA i (key block i / KS, k-step i % KS) from the K stage
+  // lk: row 32 kb + lc, physical chunk (2 ks) ^ k_x; k_lane is a multiple of
+  // the row size, so the in-row byte offset 16 ((2 ks) ^ k_x) is the XOR of
+  // k_row_x = k_lane + 16 k_x with 32 ks (one VALU op per k-step instead of a
+  // register per k-step)
+  auto rd_k = [&](const char* lk, int i) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(lk + (i / KS) * 32 * ROW + (k_row_x ^ (32 * (i % KS))));
+  };
+  // operand of PV MFMA i (16-key step i / DB, 32-row block i % DB); lv is the
+  // stage's offset from the V region (v_lane holds the region start)
+  auto rd_v = [&](const char* lv, int i) __attribute__((always_inline)) {
+    const char* vp = lv + 16 * (i / DB) * ROW + v_lane[i % DB];
+    const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
+    const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * ROW));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4, r0), __builtin_bit_cast(bf16x4, r1),
+                                   0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+  // weights of scores e, e+1 into P^T and the row sum
+  auto exp_pair = [&](int e) __attribute__((always_inline)) {
+    bf16x2 pr;
+    pr[0] = to_bf16(fast_exp2(sc[e]));
+    pr[1] = to_bf16(fast_exp2(sc[e + 1]));
+    pw[e >> 1] = __builtin_bit_cast(uint32_t, pr);
+    rs = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rs, false);
+  };
+  // P^T operand of 16-key step ks (key block ks / 2, half ks % 2): weights
+  // 8 ks .. 8 ks + 7
+  auto p_op = [&](int ks) __attribute__((always_inline)) {
+    const u32x4 w = {pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]};
+    return __builtin_bit_cast(bf16x8, w);
+  };
+  // QK of the next tile (K stage lk) with the weights of the current one; the
+  // reads past the QK operands fetch the first PF V operands of the current
+  // tile (V stage lv)
+  auto phase_qk = [&](const char* __restrict__ lk, const char* __restrict__ lv) __attribute__((always_inline)) {
+    rs = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int kb = i / KS, ks = i % KS;
+      sn[kb] = mfma32(kbuf[i], qreg[0][ks], ks == 0 ? f32x16{} : sn[kb]);
+      const int j = i + PF;
+      if (j < NQ) kbuf[j] = rd_k(lk, j);
+      else vbuf[j - NQ] = rd_v(lv, j - NQ);
+#pragma unroll
+      for (int e = EQ * i; e < EQ * (i + 1); e += 2) exp_pair(e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // tile k crosses a causal or document edge of the wave's columns, or the end
+  // of the keys held
+  // (bitwise, so that no branch is formed: a branch right after an MFMA can
+  // leave the MFMA result read in its target without enough wait states)
+  auto needs_mask = [&](int k) __attribute__((always_inline)) {
+    const int kt = kv_lo + k * kKT;
+    return (!wave_all_valid) | (kt + kKT - 1 > w_tmin + qo) | (kt < w_smax) | (kt + kKT > kend);
+  };
+  // PV of the previous tile (V stage lv) with the scale FMA of tile k's
+  // scores; the reads past the PV operands fetch the first PF K operands of
+  // tile k+1 (K stage lk2). Each FMA result is pinned where it is formed (an
+  // empty asm that takes it in a register), or the compiler would move all 32
+  // FMAs out of the MFMA stream to where the scores are first used.
+  auto phase_pv = [&](const char* __restrict__ lv, const char* __restrict__ lk2) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int ks = i / DB, db = i % DB;
+      acc[db] = mfma32(vbuf[i], p_op(ks), acc[db]);
+      const int j = i + PF;
+      if (j < NP) vbuf[j] = rd_v(lv, j);
+      else kbuf[j - NP] = rd_k(lk2, j - NP);
+#pragma unroll
+      for (int e = EP * i; e < EP * (i + 1); ++e) {
+        sc[e] = fmaf(sn[e >> 4][e & 15], a.scale_log2, negM);
+        asm volatile("" : "+v"(sc[e]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // the causal/document mask of tile k's scores (applied to tiles that cross
+  // an edge of the wave's columns): key rows of this lane's scores are
+  // 32 kb + 8 (j / 4) + 4 hi + j % 4, visible when in [st, min(tok + qo,
+  // kend - 1)]; keys at or past kend (a ring step's key shard can end before
+  // the rows' positions) are masked too
+  auto mask_tile = [&](int k) __attribute__((always_inline)) {
+    const int kt = kv_lo + k * kKT;
+    const int lo4 = (valid[0] ? st[0] - kt : kKT) - 4 * hi;
+    const int hi4 = (valid[0] ? min(tok[0] + qo, kend - 1) - kt : -1) - 4 * hi;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int r = 32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3);
+      sc[e] = (r >= lo4 && r <= hi4) ? sc[e] : -INFINITY;
+    }
+  };
+  // the last PV (tile n_tiles - 1, V stage lv): its first PF operands were
+  // read by the last QK phase
+  auto phase_pv_last = [&](const char* lv) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int ks = i / DB, db = i % DB;
+      if (i + PF < NP) vbuf[i + PF] = rd_v(lv, i + PF);
+      acc[db] = mfma32(vbuf[i], p_op(ks), acc[db]);
+    }
+  };
+  // After the weights of a tile: the reference must move only if a weight may
+  // exceed kLazyW (some lane's sum of them does) or the column has no
+  // reference yet. It then moves up to the tile's column max (d = how far, in
+  // log2 units), the accumulator and row sum are scaled by 2^-d and the
+  // weights are formed again; a column still without a visible key keeps
+  // Mref = -inf. Softmax does not depend on the reference, so this is exact.
+  auto settle = [&]() __attribute__((always_inline)) {
+    if (__any(Mref == -INFINITY || !(rs <= kLazyW))) {
+      float mx = sc[0];
+#pragma unroll
+      for (int e = 1; e < 32; ++e) mx = fmaxf(mx, sc[e]);
+      mx = max_xor32(mx);
+      const bool none = Mref == -INFINITY;
+      const float d = none ? (mx > -INFINITY ? mx : 0.f) : fmaxf(mx, 0.f);
+      const float al = none ? 1.f : fast_exp2(-d);
+      Mref = none ? (mx > -INFINITY ? mx : -INFINITY) : Mref + d;
+      negM = Mref == -INFINITY ? 0.f : -Mref;
+      l *= al;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= al;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) sc[e] -= d;
+      rs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; e += 2) exp_pair(e);
+    }
+    l += rs;
+  };
+  // only the loads issued after the previous barrier (2 NL per wave) may be
+  // pending, then the barrier (the fp32 path writes its stages with ds_write:
+  // drain those first)
+  auto sync_tiles = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL));
+    if constexpr (!std::is_same<T, __bf16>::value) __builtin_amdgcn_s_waitcnt(kLgkm0);
     __builtin_amdgcn_s_barrier();
   };
+  // Iteration k (1 <= k < n_tiles) of the loop below, stage indices as
+  // constants: PV(k-1) with the scale FMA (and mask) of tile k, the loads of
+  // K(k+3) and V(k+2), then QK(k+1) with the weights of tile k. Its LDS
+  // pointers are restrict parameters of one call, so the compiler does not
+  // take the direct-to-LDS loads it issues as writers of what its reads fetch;
+  // the waits and barriers order the stages.
+  auto iter = [&](char* __restrict__ kdst, char* __restrict__ vdst, const char* __restrict__ vprev,
+                  const char* __restrict__ knext, const char* __restrict__ vcur, int k)
+      __attribute__((always_inline)) {
+    const bool masked = needs_mask(k);
+    phase_pv(vprev - 4 * TILE, knext);
+    if (masked) mask_tile(k);
+    // (issued here rather than before the PV: the register allocator then
+    // keeps every operand in registers; issued earlier they measured no faster)
+    stage_kv(tile_kt(k + 3), kdst, false);
+    stage_kv(tile_kt(k + 2), vdst, true);
+    phase_qk(knext, vcur - 4 * TILE);
+  };
+  // Iteration 0: the loads of K3 and V2, QK of tile 0 (its operands read
+  // here), the scale FMA and mask of tile 0, the first K1 operands, then QK(1)
+  // with the weights of tile 0.
+  auto iter0 = [&](char* __restrict__ kdst, char* __restrict__ vdst, const char* __restrict__ k0,
+                   const char* __restrict__ k1, const char* __restrict__ v0) __attribute__((always_inline)) {
+    const bool masked = needs_mask(0);
+    stage_kv(tile_kt(3), kdst, false);
+    stage_kv(tile_kt(2), vdst, true);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) kbuf[i] = rd_k(k0, i);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) sn[i / KS] = mfma32(kbuf[i], qreg[0][i % KS], i % KS == 0 ? f32x16{} : sn[i / KS]);
+    // (no PV precedes tile 0: its scale FMA and mask run on their own)
+#pragma unroll
+    for (int e = 0; e < 32; ++e) sc[e] = fmaf(sn[e >> 4][e & 15], a.scale_log2, negM);
+    if (masked) mask_tile(0);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) kbuf[i] = rd_k(k1, i);
+    phase_qk(k1, v0 - 4 * TILE);
+  };
 
-  f32x16 sc[2];           // S^T of one tile: [32-key block]
-  bf16x8 pc[2][2];        // P^T of one tile: [32-key block][16-key half]
-
-  auto qk_tile = [&](const char* lk) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sc[kb][j] = 0.f;
-#pragma unroll
-      for (int k4 = 0; k4 < KS; k4 += 4) {
-        bf16x8 ka[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          ka[u] = *reinterpret_cast<const bf16x8*>(lk + kb * 32 * ROW + k_lane + 16 * ((2 * (k4 + u)) ^ k_x));
-#pragma unroll
-        for (int u = 0; u < 4; ++u) sc[kb] = mfma32(ka[u], qreg[0][k4 + u], sc[kb]);
-      }
-    }
-  };
-  auto pv_tile = [&](const char* lv) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 va[DB];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const char* vp = lv + 16 * ks * ROW + v_lane[db];
-        const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
-        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 8 * ROW));
-        va[db] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, r0), __builtin_bit_cast(bf16x4, r1),
-                                         0, 1, 2, 3, 4, 5, 6, 7);
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db][0] = mfma32(va[db], pc[ks >> 1][ks & 1], acc[db][0]);
-    }
-  };
-  auto sm_tile = [&](int k) __attribute__((always_inline)) {
-    const int kt = kv_lo + k * kKT;
-    // (keys at or past kend, the end of the keys held, are masked too: a
-    // ring step's key shard can end before the rows' positions)
-    if (!wave_all_valid || kt + kKT - 1 > w_tmin + qo || kt < w_smax || kt + kKT > kend) {
-      const int lo = valid[0] ? st[0] - kt : kKT;
-      const int hi_ = valid[0] ? min(tok[0] + qo, kend - 1) - kt : -1;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int kr = kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-          sc[kb][j] = (kr >= lo && kr <= hi_) ? sc[kb][j] : -INFINITY;
-        }
-    }
-    // P^T of the tile against the reference mc (log2 units); returns this
-    // lane's sum of the rounded weights
-    auto weights = [&](float mc) __attribute__((always_inline)) -> float {
-      float rs = 0.f;
-      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            bf16x2 pr;
-            pr[0] = to_bf16(fast_exp2(fmaf(sc[kb][8 * h2 + i], a.scale_log2, -mc)));
-            pr[1] = to_bf16(fast_exp2(fmaf(sc[kb][8 * h2 + i + 1], a.scale_log2, -mc)));
-            pc[kb][h2][i] = pr[0];
-            pc[kb][h2][i + 1] = pr[1];
-            rs = __builtin_amdgcn_fdot2_f32_bf16(pr, one, rs, false);
-          }
-      return rs;
-    };
-    // The reference must move only when a weight would exceed kLazyW. The
-    // weights are non-negative, so a lane whose sum is at most kLazyW holds
-    // none larger, and the tile max is needed only when some lane's sum is
-    // larger (or a column has no reference yet); the reference then moves to
-    // the tile max whenever that is higher.
-    bool slow = __any(m[0] == -INFINITY);
-    float rs = 0.f;
-    if (!slow) {
-      rs = weights(m[0] * a.scale_log2);
-      slow = __any(!(rs <= kLazyW));
-    }
-    if (slow) {
-      float mx = sc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
-      mx = max_xor32(mx);
-      const bool mv = mx > m[0];
-      const float al = mv ? fast_exp2((m[0] - mx) * a.scale_log2) : 1.f;   // 0 when m = -inf
-      m[0] = mv ? mx : m[0];
-      l[0] *= al;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db][0] *= al;
-      rs = weights(m[0] == -INFINITY ? 0.f : m[0] * a.scale_log2);
-    }
-    l[0] += rs;
-  };
-  // the MFMA phase runs at raised priority, so the SIMD's arbiter keeps the
-  // matrix core fed from it first
-  // The refill of tile k+3 and the operand reads of the MFMA phase go through
-  // one call whose stage pointers are restrict, so the compiler does not take
-  // the refill's LDS-direct loads as writers of what the phase reads (it would
-  // otherwise wait for every load in flight before the first read); the
-  // vmcnt waits before the barriers order each stage's loads before its reads.
-  auto x_phase = [&](char* __restrict__ dst, int kd, const char* __restrict__ lv,
-                     const char* __restrict__ lk, int k) __attribute__((always_inline)) {
-    if (dst) stage(kd < n_tiles ? kv_lo + kd * kKT : kend, dst);
-    __builtin_amdgcn_s_setprio(1);
-    // one block of 32 MFMAs and their 48 operand reads (after the last tile
-    // the QK of the stage beyond it is computed and dropped): keep eight reads
-    // ahead of the MFMAs instead of the one or two the default schedule keeps
-    pv_tile(lv);
-    qk_tile(lk);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_s_setprio(0);
-  };
-  // tile k+2 landed: only the loads issued after it (tile k+3) may be pending
-  auto landed = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL)); };
-
-  issue(0);
-  issue(1);
-  issue(2);
+  // ---- prologue loads: K0, K1, V0, K2, V1 (K and V stage 3 hold the RoPE table) --
+  stage_kv(tile_kt(0), kst[0], false);
+  stage_kv(tile_kt(1), kst[1], false);
+  stage_kv(tile_kt(0), vst[0], true);
+  stage_kv(tile_kt(2), kst[2], false);
+  stage_kv(tile_kt(1), vst[1], true);
   if (rope_q) {
     // RoPE of this lane's query channels 16ks + 8hi + 0..7, i.e. the pairs
     // k = 8ks + 4hi + p (adjacent pairs (2k, 2k+1)) or, for half-split pairs
@@ -578,61 +648,34 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * NL));   // tile 0 landed
-  __builtin_amdgcn_s_barrier();
-  if (group == 0) {
-    __builtin_amdgcn_s_setprio(1);
-    qk_tile(stage_ptr(0));
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL));   // tile 1 landed
-    barrier();                                       // end of phase 0
-    sm_tile(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));        // tile 2 landed
-    barrier();                                       // end of phase 1
-    // unrolled over the four stages so every stage offset is a constant
-    auto step = [&](auto U, int k) __attribute__((always_inline)) {
-      constexpr int u = decltype(U)::value;
-      x_phase(lds + ((u + 3) & 3) * TILE, k + 3, lds + u * TILE, lds + ((u + 1) & 3) * TILE, k);
-      barrier();                                     // end of phase 2k+2
-      if (k + 1 < n_tiles) sm_tile(k + 1);
-      landed();
-      barrier();                                     // end of phase 2k+3
-    };
-    for (int k = 0; k < n_tiles; k += 4) {
-      step(std::integral_constant<int, 0>{}, k);
-      if (k + 1 >= n_tiles) break;
-      step(std::integral_constant<int, 1>{}, k + 1);
-      if (k + 2 >= n_tiles) break;
-      step(std::integral_constant<int, 2>{}, k + 2);
-      if (k + 3 >= n_tiles) break;
-      step(std::integral_constant<int, 3>{}, k + 3);
+  sync_tiles();   // K0, K1, V0 landed; every wave is done with the RoPE table
+  iter0(kst[3], vst[2], kst[0], kst[1], vst[0]);
+  settle();
+  sync_tiles();   // B(0)
+  // Unrolled over the four stage indices so every stage offset is a constant.
+  // The loop has one exit: steps at or past the last tile are skipped by a
+  // uniform branch that rejoins (an exit after every unrolled step keeps the
+  // register allocator from merging the accumulators' copies).
+  auto step = [&](auto U, int k) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;   // k % 4
+    if (k < n_tiles) {
+      iter(kst[(u + 3) & 3], vst[(u + 2) & 3], vst[(u + 3) & 3], kst[(u + 1) & 3], vst[u], k);
+      settle();
+      sync_tiles();   // B(k)
     }
-  } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL));
-    barrier();                                       // end of phase 0
-    __builtin_amdgcn_s_setprio(1);
-    qk_tile(stage_ptr(0));
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    barrier();                                       // end of phase 1
-    auto step = [&](auto U, int k) __attribute__((always_inline)) {
-      constexpr int u = decltype(U)::value;
-      stage(k + 3 < n_tiles ? kv_lo + (k + 3) * kKT : kend, lds + ((u + 3) & 3) * TILE);
-      sm_tile(k);
-      barrier();                                     // end of phase 2k+2
-      x_phase(nullptr, 0, lds + u * TILE, lds + ((u + 1) & 3) * TILE, k);
-      landed();
-      barrier();                                     // end of phase 2k+3
-    };
-    for (int k = 0; k < n_tiles; k += 4) {
-      step(std::integral_constant<int, 0>{}, k);
-      if (k + 1 >= n_tiles) break;
-      step(std::integral_constant<int, 1>{}, k + 1);
-      if (k + 2 >= n_tiles) break;
-      step(std::integral_constant<int, 2>{}, k + 2);
-      if (k + 3 >= n_tiles) break;
-      step(std::integral_constant<int, 3>{}, k + 3);
-    }
+  };
+  for (int k = 1; k < n_tiles; k += 4) {
+    step(std::integral_constant<int, 1>{}, k);
+    step(std::integral_constant<int, 2>{}, k + 1);
+    step(std::integral_constant<int, 3>{}, k + 2);
+    step(std::integral_constant<int, 0>{}, k + 3);
+  }
+  // PV of the last tile, from V stage (n_tiles - 1) % 4
+  switch ((n_tiles - 1) & 3) {
+    case 0: phase_pv_last(vst[0] - 4 * TILE); break;
+    case 1: phase_pv_last(vst[1] - 4 * TILE); break;
+    case 2: phase_pv_last(vst[2] - 4 * TILE); break;
+    default: phase_pv_last(vst[3] - 4 * TILE); break;
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));          // loads past the last tile
 
@@ -646,7 +689,7 @@ void prefill_kernel(PrefillArgs a) {
   float lt[kCB], rl[kCB];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
-    lt[cb] = l[cb] + __shfl_xor(l[cb], 32);
+    lt[cb] = l + __shfl_xor(l, 32);
     rl[cb] = lt[cb] > 0.f ? __builtin_amdgcn_rcpf(lt[cb]) : 0.f;
   }
   auto quot = [&](float x, int cb) __attribute__((always_inline)) {
@@ -654,7 +697,7 @@ void prefill_kernel(PrefillArgs a) {
     return fmaf(fmaf(-q, lt[cb], x), rl[cb], q);
   };
   auto row_lse = [&](int cb) __attribute__((always_inline)) {
-    return lt[cb] > 0.f ? m[cb] * a.scale + fast_log2(lt[cb]) * kLn2 : -INFINITY;
+    return lt[cb] > 0.f ? (Mref + fast_log2(lt[cb])) * kLn2 : -INFINITY;
   };
   if (a.acc_mode) {
     // ring step: this shard's (o, lse) of every row, written (first step) or
@@ -686,8 +729,8 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
           f32x4* dst = reinterpret_cast<f32x4*>(op + db * 32 + 8 * jq + 4 * hi);
-          f32x4 v = {quot(acc[db][cb][4 * jq], cb), quot(acc[db][cb][4 * jq + 1], cb),
-                     quot(acc[db][cb][4 * jq + 2], cb), quot(acc[db][cb][4 * jq + 3], cb)};
+          f32x4 v = {quot(acc[db][4 * jq], cb), quot(acc[db][4 * jq + 1], cb),
+                     quot(acc[db][4 * jq + 2], cb), quot(acc[db][4 * jq + 3], cb)};
           if (a.acc_mode == 2) v = (wo * (*dst) + wn * v) * rw;
           *dst = v;
         }
@@ -708,8 +751,8 @@ void prefill_kernel(PrefillArgs a) {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
-          const f32x4 v = {quot(acc[db][cb][4 * jq], cb), quot(acc[db][cb][4 * jq + 1], cb),
-                           quot(acc[db][cb][4 * jq + 2], cb), quot(acc[db][cb][4 * jq + 3], cb)};
+          const f32x4 v = {quot(acc[db][4 * jq], cb), quot(acc[db][4 * jq + 1], cb),
+                           quot(acc[db][4 * jq + 2], cb), quot(acc[db][4 * jq + 3], cb)};
           *reinterpret_cast<f32x4*>(op + db * 32 + 8 * jq + 4 * hi) = v;
         }
       if (hi == 0) a.lse_part[(((int64_t)sp * a.B + b) * a.Hq + head[cb]) * Sq + tok[cb]] = row_lse(cb);
@@ -724,7 +767,6 @@ void prefill_kernel(PrefillArgs a) {
     // back 16 contiguous bytes per lane, D/8 lanes per row. The barrier
     // orders every wave's last operand reads and LDS-direct loads before the
     // stage memory is reused; each wave then only touches its own rows.
-    static_assert(kCB == 1, "one 32-column block per wave");
     __syncthreads();
     char* ow = lds + wave * 32 * ROW;
 #pragma unroll
@@ -733,7 +775,7 @@ void prefill_kernel(PrefillArgs a) {
       for (int jq = 0; jq < 4; ++jq) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = to_bf16(quot(acc[db][0][4 * jq + e], 0));
+        for (int e = 0; e < 4; ++e) v[e] = to_bf16(quot(acc[db][4 * jq + e], 0));
         *reinterpret_cast<bf16x4*>(ow + lc * ROW + 16 * ((4 * db + jq) ^ (lc & (CH - 1))) + 8 * hi) = v;
       }
     constexpr int RPI = 64 / CH;   // rows per wave-wide 16-byte access
@@ -758,8 +800,8 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
           const int d = db * 32 + 8 * jq + 4 * hi;
-          store4(op + d, quot(acc[db][cb][4 * jq], cb), quot(acc[db][cb][4 * jq + 1], cb),
-                 quot(acc[db][cb][4 * jq + 2], cb), quot(acc[db][cb][4 * jq + 3], cb));
+          store4(op + d, quot(acc[db][4 * jq], cb), quot(acc[db][4 * jq + 1], cb),
+                 quot(acc[db][4 * jq + 2], cb), quot(acc[db][4 * jq + 3], cb));
         }
     }
   }
