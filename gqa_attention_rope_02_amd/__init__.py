@@ -384,10 +384,11 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk: int, o_part, lse_part,
             or tuple(lse_part.shape) != (B, Hq, max_splits) or tuple(seq_lens.shape) != (B,):
         raise ValueError("gqa_decode: inconsistent shapes")
     _same_dtype("gqa_decode", torch.bfloat16, q=q, k_cache=k_cache, v_cache=v_cache)
+    op, lp = _f32c(o_part), _f32c(lse_part)
     st = _lib.load().gqa_decode(
         _dev(q), _strides(q, 2), _dev(k_cache), _dev(v_cache), _strides(k_cache, 3),
         _i32(seq_lens), B, Hq, Hkv, D, Lmax, int(kv_chunk), max_splits, float(softmax_scale),
-        _f32c(o_part), _f32c(lse_part), _stream())
+        op, lp, _stream())
     _check(st, "gqa_decode")
 
 
@@ -403,6 +404,7 @@ def gqa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, kv_chunk: int, 
             or block_table.dim() != 2 or block_table.shape[0] != B or block_table.stride(1) != 1:
         raise ValueError("gqa_decode_paged: inconsistent shapes")
     _same_dtype("gqa_decode_paged", torch.bfloat16, q=q, k_pages=k_pages, v_pages=v_pages)
+    op, lp = _f32c(o_part), _f32c(lse_part)
     ps = k_pages.stride()
     if ps[-1] != 1:
         raise ValueError("the last (head_dim) dimension must be contiguous")
@@ -410,7 +412,7 @@ def gqa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, kv_chunk: int, 
     st = _lib.load().gqa_decode_paged(
         _dev(q), _strides(q, 2), _dev(k_pages), _dev(v_pages), page_strides, page_size,
         _i32(block_table), block_table.stride(0), _i32(seq_lens), B, Hq, Hkv, D, int(Lmax),
-        int(kv_chunk), max_splits, float(softmax_scale), _f32c(o_part), _f32c(lse_part), _stream())
+        int(kv_chunk), max_splits, float(softmax_scale), op, lp, _stream())
     _check(st, "gqa_decode_paged")
 
 
@@ -423,3 +425,4 @@ def gqa_decode_combine(o_part, lse_part, seq_lens, kv_chunk: int, o, lse=None):
         _f32c(o_part), _f32c(lse_part), _i32(seq_lens), B, Hq, D, int(kv_chunk), max_splits,
         _dev(o), _strides(o, 2), _f32c(lse), _dtype(o), _stream())
     _check(st, "gqa_decode_combine")
+
