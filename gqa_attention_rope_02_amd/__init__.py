@@ -48,6 +48,9 @@ contiguous):
   Hkv, D] (any page/slot/head strides), block_table int32 [B, pages per sequence].
 * ``gqa_decode_combine(o_part, lse_part, seq_lens, kv_chunk, o, lse=None)``:
   o [B,Hq,D] (bf16 or fp32), lse fp32 [B,Hq].
+* ``gqa_decode_noalloc(q, k_cache, v_cache, seq_lens, kv_chunk, o, lse=None,
+  softmax_scale=0.0)``: gqa_decode + gqa_decode_combine with the partials in the
+  library's own device scratch (no workspace, no allocation).
 """
 
 from __future__ import annotations
@@ -59,7 +62,7 @@ from . import _lib
 __all__ = ["LlamaAttnError", "rope_qk", "rope_qk_backward", "gqa_attention_backward", "backward_workspace", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk",
            "gqa_prefill_split", "prefill_split_workspace", "gqa_prefill_ring_step",
            "gqa_prefill_ring_finalize", "gqa_decode", "gqa_decode_paged",
-           "gqa_decode_combine", "version", "LA_BF16", "LA_FP32"]
+           "gqa_decode_combine", "gqa_decode_noalloc", "version", "LA_BF16", "LA_FP32"]
 
 LA_BF16, LA_FP32 = 0, 1
 _DT = {torch.bfloat16: LA_BF16, torch.float32: LA_FP32}
@@ -426,3 +429,21 @@ def gqa_decode_combine(o_part, lse_part, seq_lens, kv_chunk: int, o, lse=None):
         _dev(o), _strides(o, 2), _f32c(lse), _dtype(o), _stream())
     _check(st, "gqa_decode_combine")
 
+
+def gqa_decode_noalloc(q, k_cache, v_cache, seq_lens, kv_chunk: int, o, lse=None,
+                       softmax_scale: float = 0.0):
+    B, Hq, D = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must share strides")
+    _same_shape("gqa_decode_noalloc", (k_cache, v_cache))
+    if k_cache.shape[0] != B or k_cache.shape[3] != D or tuple(seq_lens.shape) != (B,) \
+            or tuple(o.shape) != (B, Hq, D) or (lse is not None and tuple(lse.shape) != (B, Hq)):
+        raise ValueError("gqa_decode_noalloc: inconsistent shapes")
+    _same_dtype("gqa_decode_noalloc", torch.bfloat16, q=q, k_cache=k_cache, v_cache=v_cache)
+    lp = _f32c(lse)
+    st = _lib.load().gqa_decode_noalloc(
+        _dev(q), _strides(q, 2), _dev(k_cache), _dev(v_cache), _strides(k_cache, 3), _i32(seq_lens),
+        B, Hq, Hkv, D, Lmax, int(kv_chunk), float(softmax_scale), _dev(o), _strides(o, 2), lp,
+        _dtype(o), _stream())
+    _check(st, "gqa_decode_noalloc")

@@ -46,6 +46,8 @@ SIGNATURES = {
     "gqa_decode_paged": ([_vp, _c_i64_p, _vp, _vp, _c_i64_p, _i, _vp, _i, _vp, _i, _i, _i, _i,
                           _i, _i, _i, ctypes.c_float, _vp, _vp, _vp], _i),
     "gqa_decode_combine": ([_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _c_i64_p, _vp, _i, _vp], _i),
+    "gqa_decode_noalloc": ([_vp, _c_i64_p, _vp, _vp, _c_i64_p, _vp, _i, _i, _i, _i, _i, _i,
+                            ctypes.c_float, _vp, _c_i64_p, _vp, _i, _vp], _i),
 }
 
 _lib = None

@@ -35,6 +35,8 @@
 //   issue order, so "tile p has landed" is "at most the loads of the tiles
 //   issued after it are pending", whatever other memory operations (query
 //   loads, partial stores) are outstanding.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -43,7 +45,7 @@ namespace {
 
 constexpr int kKT = 16;       // keys per wave tile
 constexpr int kNS = 4;        // LDS ring stages per wave
-constexpr int kWaves = 4;     // waves per workgroup
+constexpr int kWaves = kDecodeWaves;   // waves per workgroup
 constexpr float kLazy = 8.f;  // log2 headroom of the lazily moved softmax reference
 constexpr int kMaxB = kDecodeMaxBatch;   // sequences per call (tables in LDS)
 
@@ -188,6 +190,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const int gw = blockIdx.x * kWaves + wave;
   const int i0 = first_item_from((int64_t)gw * T / W);
   const int i1 = first_item_from((int64_t)(gw + 1) * T / W);
+  if (a.hdr) {   // compact partials: which (sequence, KV head) pairs this wave holds runs of
+    int first = 0x7fffffff, last = -1;
+    if (i0 < i1) {
+      const Item f = item_at(i0), t = item_at(i1 - 1);
+      first = f.b * a.Hkv + f.kvh;
+      last = t.b * a.Hkv + t.kvh;
+    }
+    if (lane == 0) {
+      a.hdr[2 * gw] = first;
+      a.hdr[2 * gw + 1] = last;
+    }
+  }
   if (i0 >= i1) return;
 
   // ---- per-lane constant offsets ---------------------------------------------
@@ -337,7 +351,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         if (++ct == cit.nt) {   // item done
           if (ci + 1 == i1 || cit.s + 1 == cit.ns) {   // run done: its partial goes to slot run_s0
             const float lt2 = add_xor32(add_xor16(l));
-            if (lc < G) {
+            if (lc < G && a.hdr) {   // compact: slot gw + bh, head lc of the group
+              const int64_t slot = ((int64_t)gw + cit.b * a.Hkv + cit.kvh) * G + lc;
+              float* op = a.o_part + slot * D;
+    #pragma unroll
+              for (int db = 0; db < DB; ++db)
+                *reinterpret_cast<f32x4*>(op + 16 * db + 4 * lg) = acc[db] / lt2;
+              if (lg == 0) a.lse_part[slot] = m * a.scale + fast_log2(lt2) * kLn2;
+            } else if (lc < G) {
               const int64_t row = ((int64_t)cit.b * a.Hq + cit.kvh * G + lc) * a.max_splits;
               float* op = a.o_part + (row + run_s0) * D;
     #pragma unroll
@@ -363,28 +384,56 @@ __global__ __launch_bounds__(256) void combine_kernel_f(CombineArgs a, int dt) {
   const int pair = blockIdx.x * 4 + wave;
   if (pair >= a.B * a.Hq) return;
   const int b = pair / a.Hq, h = pair % a.Hq;
-  const int L = max(1, a.seq_lens[b]);
-  const int n = min((L + a.kv_chunk - 1) / a.kv_chunk, a.max_splits);
-  const float* lp = a.lse_part + (int64_t)pair * a.max_splits;
-  const float* op = a.o_part + (int64_t)pair * a.max_splits * D;
-  float M = -INFINITY;
-  for (int s = lane; s < n; s += 64) M = fmaxf(M, lp[s]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float W = 0.f;
   float o[D / 64];
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) o[i] = 0.f;
-  for (int s0 = 0; s0 < n; s0 += 64) {   // slots with lse = -inf carry nothing and are skipped
-    const float ls = s0 + lane < n ? lp[s0 + lane] : -INFINITY;
-    uint64_t live = __ballot(ls != -INFINITY);
-    while (live) {
-      const int j = __builtin_ctzll(live);
-      live &= live - 1;
-      const float w = expf(__shfl(ls, j) - M);
-      W += w;
+  float M = -INFINITY;
+  if (a.hdr) {
+    // compact partials: the runs of pair bh are held by the waves whose
+    // header range contains bh, in slot w + bh; merged in wave order, which is
+    // the split order of the slot layout below
+    const int G = a.Hq / a.Hkv;
+    const int bh = b * a.Hkv + h / G, gh = h % G;
+    auto run_lse = [&](int w) -> float {
+      const bool in = w < a.W && a.hdr[2 * w] <= bh && bh <= a.hdr[2 * w + 1];
+      return in ? a.lse_part[((int64_t)w + bh) * G + gh] : -INFINITY;
+    };
+    for (int w = lane; w < a.W; w += 64) M = fmaxf(M, run_lse(w));
 #pragma unroll
-      for (int i = 0; i < D / 64; ++i) o[i] += w * op[(int64_t)(s0 + j) * D + lane + 64 * i];
+    for (int x = 32; x > 0; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+    for (int w0 = 0; w0 < a.W; w0 += 64) {
+      const float ls = run_lse(w0 + lane);
+      uint64_t live = __ballot(ls != -INFINITY);
+      while (live) {
+        const int j = __builtin_ctzll(live);
+        live &= live - 1;
+        const float w = expf(__shfl(ls, j) - M);
+        W += w;
+        const float* op = a.o_part + (((int64_t)w0 + j + bh) * G + gh) * D;
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) o[i] += w * op[lane + 64 * i];
+      }
+    }
+  } else {
+    const int L = max(1, a.seq_lens[b]);
+    const int n = min((L + a.kv_chunk - 1) / a.kv_chunk, a.max_splits);
+    const float* lp = a.lse_part + (int64_t)pair * a.max_splits;
+    const float* op = a.o_part + (int64_t)pair * a.max_splits * D;
+    for (int s = lane; s < n; s += 64) M = fmaxf(M, lp[s]);
+#pragma unroll
+    for (int x = 32; x > 0; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+    for (int s0 = 0; s0 < n; s0 += 64) {   // slots with lse = -inf carry nothing and are skipped
+      const float ls = s0 + lane < n ? lp[s0 + lane] : -INFINITY;
+      uint64_t live = __ballot(ls != -INFINITY);
+      while (live) {
+        const int j = __builtin_ctzll(live);
+        live &= live - 1;
+        const float w = expf(__shfl(ls, j) - M);
+        W += w;
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) o[i] += w * op[(int64_t)(s0 + j) * D + lane + 64 * i];
+      }
     }
   }
   if (dt == 0) {
@@ -427,6 +476,38 @@ hipError_t launch_d(const DecodeArgs& a, int G, hipStream_t st) {
 
 hipError_t launch_decode(const DecodeArgs& a, int D, int G, hipStream_t st) {
   return D == 64 ? launch_d<64>(a, G, st) : launch_d<128>(a, G, st);
+}
+
+// ---- scratch of the allocation-free decode ----------------------------------
+// A file-scope device array: each device the library runs on holds its own
+// copy from module load until the process ends. Host code takes its device
+// address from hipGetSymbolAddress, once per device with that device current;
+// the array's name itself is only a host-side stand-in.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** ptr, size_t* bytes) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = kScratchBytes;
+  return hipSuccess;
 }
 
 hipError_t launch_combine(const CombineArgs& a, int D, int dt, hipStream_t st) {

@@ -78,6 +78,11 @@ struct DecodeArgs {
   const int32_t* block_table;
   int bt_stride, page_shift;
   int grid;                   // workgroups of the persistent grid (compute units)
+  // compact partials (hdr non-null): wave w writes hdr[2w], hdr[2w+1] = the
+  // first and last (sequence, KV head) index b * Hkv + kvh it holds a run of
+  // (INT_MAX, -1 when it holds none), and the run of pair bh goes to slot
+  // w + bh: o_part [slot][G][D], lse_part [slot][G]
+  int* hdr;
 };
 
 struct CombineArgs {
@@ -88,6 +93,9 @@ struct CombineArgs {
   void* o;
   int64_t os_b, os_h;
   float* lse;                 // [B, Hq] or null
+  // compact partials (hdr non-null): see DecodeArgs; W waves wrote headers
+  const int* hdr;
+  int Hkv, W;
 };
 
 // Gradient pass (bf16 tensors): q, k rotated; o, lse from the forward; dout
@@ -128,6 +136,11 @@ hipError_t launch_prefill(const PrefillArgs& a, int D, int G, int dt, hipStream_
 hipError_t launch_prefill_merge(const PrefillArgs& a, int D, int dt, hipStream_t st);
 // Sequences per gqa_decode call (the kernel keeps per-sequence tables in LDS).
 constexpr int kDecodeMaxBatch = 1024;
+// Waves per workgroup of the persistent decode grid (one workgroup per CU).
+constexpr int kDecodeWaves = 4;
+// The allocation-free decode's scratch: its device address on the current
+// device (looked up once per device) and its size in bytes.
+hipError_t decode_scratch(void** ptr, size_t* bytes);
 
 hipError_t launch_decode(const DecodeArgs& a, int D, int G, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& a, int D, int dt, hipStream_t st);

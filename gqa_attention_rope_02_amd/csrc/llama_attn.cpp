@@ -145,6 +145,7 @@ const char* la_status_str(la_status s) {
     case LA_ERR_INVALID_ARG: return "invalid argument";
     case LA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case LA_ERR_LAUNCH: return "kernel launch failed";
+    case LA_ERR_SCRATCH: return "working set exceeds the allocation-free scratch buffer";
   }
   return "unknown status";
 }
@@ -533,6 +534,57 @@ la_status gqa_decode_combine(const float* o_part, const float* lse_part, const i
   a.o = o; a.os_b = o_strides[0]; a.os_h = o_strides[1];
   a.lse = lse;
   return launched(la::launch_combine(a, D, dt == LA_BF16 ? 0 : 1, stream));
+}
+
+la_status gqa_decode_noalloc(const void* q, const int64_t q_strides[2], const void* k_cache,
+                             const void* v_cache, const int64_t cache_strides[3],
+                             const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int Lmax,
+                             int kv_chunk, float softmax_scale, void* o, const int64_t o_strides[2],
+                             float* lse, la_dtype dt, hipStream_t stream) {
+  // every check that does not need the scratch comes first (placeholder,
+  // aligned workspace pointers for the decode's own checks)
+  if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
+  if (!o || !o_strides || o_strides[0] < 0 || o_strides[1] < 0) return LA_ERR_INVALID_ARG;
+  if (kv_chunk < 64 || kv_chunk % 64 != 0 || Lmax < 1) return LA_ERR_INVALID_ARG;
+  const int max_splits = (int)(((long long)Lmax + kv_chunk - 1) / kv_chunk);
+  float* placeholder = reinterpret_cast<float*>(uintptr_t(256));
+  la_status st = decode_check(q, q_strides, k_cache, v_cache, cache_strides, seq_lens, B, Hq, Hkv, D,
+                              Lmax, kv_chunk, max_splits, softmax_scale, placeholder, placeholder);
+  if (st != LA_OK) return st;
+  if (debug_mode() && !lens_ok(seq_lens, B, 1, Lmax, stream)) return LA_ERR_INVALID_ARG;
+
+  void* base = nullptr;
+  size_t cap = 0;
+  if (la::decode_scratch(&base, &cap) != hipSuccess) return LA_ERR_LAUNCH;
+  // scratch: wave headers, then the run slots' o and lse (one run per wave
+  // and (sequence, KV head) pair it touches: at most waves + B * Hkv slots)
+  const int grid = current_cu_count();
+  const long long W = (long long)grid * la::kDecodeWaves;
+  const long long G = Hq / Hkv;
+  const long long slots = W + (long long)B * Hkv;
+  auto up256 = [](long long x) { return (x + 255) / 256 * 256; };
+  const long long hdr_bytes = up256(8 * W);
+  const long long o_bytes = up256(slots * G * D * 4);
+  const long long need = hdr_bytes + o_bytes + slots * G * 4;
+  if (need > (long long)cap) return LA_ERR_SCRATCH;
+  char* sp = static_cast<char*>(base);
+  int* hdr = reinterpret_cast<int*>(sp);
+  float* o_c = reinterpret_cast<float*>(sp + hdr_bytes);
+  float* l_c = reinterpret_cast<float*>(sp + hdr_bytes + o_bytes);
+
+  la::DecodeArgs a = decode_args(q, q_strides, k_cache, v_cache, cache_strides, seq_lens, B, Hq, Hkv,
+                                 D, Lmax, kv_chunk, max_splits, softmax_scale, o_c, l_c);
+  a.grid = grid;
+  a.hdr = hdr;
+  st = launched(la::launch_decode(a, D, Hq / Hkv, stream));
+  if (st != LA_OK) return st;
+  la::CombineArgs c{};
+  c.o_part = o_c; c.lse_part = l_c; c.seq_lens = seq_lens;
+  c.B = B; c.Hq = Hq; c.kv_chunk = kv_chunk; c.max_splits = max_splits;
+  c.o = o; c.os_b = o_strides[0]; c.os_h = o_strides[1];
+  c.lse = lse;
+  c.hdr = hdr; c.Hkv = Hkv; c.W = (int)W;
+  return launched(la::launch_combine(c, D, dt == LA_BF16 ? 0 : 1, stream));
 }
 
 }  // extern "C"

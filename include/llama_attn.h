@@ -54,7 +54,8 @@ typedef enum {
   LA_OK = 0,
   LA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, stride or alignment */
   LA_ERR_UNSUPPORTED = 2,   /* a shape or dtype this library has no kernel for */
-  LA_ERR_LAUNCH = 3         /* the HIP runtime refused the launch */
+  LA_ERR_LAUNCH = 3,        /* the HIP runtime refused the launch */
+  LA_ERR_SCRATCH = 4        /* gqa_decode_noalloc: the working set exceeds its scratch */
 } la_status;
 
 typedef enum { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
@@ -380,6 +381,36 @@ la_status gqa_attention_backward(const void* q, const void* k, const void* v, co
                                  const int64_t dk_strides[3], const int64_t dv_strides[3],
                                  const int32_t* cu_docs, int n_docs, float softmax_scale,
                                  float* dkv_workspace, hipStream_t stream);
+
+/*
+ * gqa_decode_noalloc — gqa_decode followed by gqa_decode_combine, for callers
+ * that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the split partials live in a scratch
+ * array the library holds in device memory (32 MiB per device, from the
+ * library's load until the process ends), so the caller passes only inputs
+ * and outputs and the call performs no allocation.
+ *
+ * Arguments as gqa_decode (q, caches, strides, seq_lens, sizes, kv_chunk,
+ * softmax_scale) and gqa_decode_combine (o [B, Hq, D] of type dt with strides
+ * o_strides (b, h); lse fp32 [B, Hq] or NULL). The partials are kept one per
+ * run of consecutive splits that one wave of the persistent decode grid
+ * takes: (waves + B * Hkv) slots of (Hq / Hkv) * (D + 1) fp32 values, plus
+ * 8 bytes per wave (waves = 4 per compute unit). Results equal those of
+ * gqa_decode + gqa_decode_combine with the same kv_chunk.
+ * Every call on a device shares that device's scratch: calls that overlap on
+ * one device (different streams, or host threads without ordering) race and
+ * must not be issued; calls in one stream are ordered and safe. Nothing in the
+ * scratch needs clearing between calls (every value a call reads is written
+ * earlier in the same call).
+ * Errors: as gqa_decode and gqa_decode_combine; LA_ERR_SCRATCH (nothing
+ * launched) when the slots above exceed the scratch; LA_ERR_LAUNCH if the
+ * scratch's device address cannot be obtained.
+ */
+la_status gqa_decode_noalloc(const void* q, const int64_t q_strides[2], const void* k_cache,
+                             const void* v_cache, const int64_t cache_strides[3],
+                             const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int Lmax,
+                             int kv_chunk, float softmax_scale, void* o, const int64_t o_strides[2],
+                             float* lse, la_dtype dt, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <string>
 
 #include "llama_attn.h"
 #include "stub_launchers.hpp"
@@ -100,6 +101,20 @@ int main() {
                            nullptr) == LA_ERR_INVALID_ARG);
   CHECK(gqa_decode_combine((float*)fake(), (float*)fake(2), sl, B, Hq, D, 256, 16, fake(), q2, nullptr, LA_BF16,
                            nullptr) == LA_ERR_INVALID_ARG);
+
+  // allocation-free decode: argument checks, then (no device here) the
+  // scratch lookup fails before anything is launched
+  const int dec_before = g_stub.decode;
+  CHECK(gqa_decode_noalloc(fake(), q2, fake(), fake(), cs, sl, B, Hq, Hkv, D, 4096, 100, 0.f, fake(), q2, nullptr,
+                           LA_BF16, nullptr) == LA_ERR_INVALID_ARG);
+  CHECK(gqa_decode_noalloc(fake(), q2, fake(), fake(), cs, sl, B, Hq, Hkv, 96, 4096, 256, 0.f, fake(), q2, nullptr,
+                           LA_BF16, nullptr) == LA_ERR_UNSUPPORTED);
+  CHECK(gqa_decode_noalloc(fake(), q2, fake(), fake(), cs, sl, B, Hq, Hkv, D, 4096, 256, 0.f, nullptr, q2, nullptr,
+                           LA_BF16, nullptr) == LA_ERR_INVALID_ARG);
+  CHECK(gqa_decode_noalloc(fake(), q2, fake(), fake(), cs, sl, B, Hq, Hkv, D, 4096, 256, 0.f, fake(), q2, nullptr,
+                           LA_BF16, nullptr) == LA_ERR_LAUNCH);
+  CHECK(g_stub.decode == dec_before);
+  CHECK(std::string(la_status_str(LA_ERR_SCRATCH)).find("scratch") != std::string::npos);
 
   // backward
   CHECK(gqa_attention_backward(fake(), fake(), fake(), fake(), fake(), (float*)fake(), (float*)fake(), fake(),

@@ -45,7 +45,10 @@ def unpadded_reads_across_branches(asm: str):
     VALU read of an MFMA destination reached through a branch taken within
     four instructions of the MFMA with fewer wait states than it needs."""
     found = []
+    functions = set(re.findall(r"\.type\s+(_Z[^,\s]+),@function", asm))
     for name in re.findall(r"^(_Z[^:\s]+):", asm, re.M):
+        if functions and name not in functions:   # data objects (the decode scratch) have no code
+            continue
         i = asm.index(name + ":")
         j = asm.index(".Lfunc_end", i)
         lines = []

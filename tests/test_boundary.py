@@ -48,6 +48,7 @@ def test_status_strings(lib):
     assert lib.la_status_str(1) == b"invalid argument"
     assert lib.la_status_str(2) == b"unsupported shape or dtype"
     assert lib.la_status_str(3) == b"kernel launch failed"
+    assert b"scratch" in lib.la_status_str(4)
     assert lib.la_status_str(99) == b"unknown status"
     assert lib.la_version() >= 100
 
