@@ -77,7 +77,7 @@ def test_decode_matches_oracle(B, Hq, Hkv, D, lens, Lmax, chunks):
         n_runs = H.check_partials(op, lp, q_rot, k_rot, vs, lens, chunk)
         H.say("  runs", n_runs, "of splits", Hq * int(sum(-(-int(L) // chunk) for L in lens)))
         H.assert_close(o, Ow)
-        H.assert_close(lse, Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+        H.assert_lse_close(lse, Lw, "LSE")
 
 
 
@@ -95,7 +95,7 @@ def test_decode_equals_last_row_of_gpu_prefill():
     vp = vs[0].transpose(0, 1)[None].contiguous()
     Op, Lp, _, _ = H.run_prefill(qp, kp, vp, None)
     H.assert_close(o[0], Op[0, -1].double().numpy(), what="decode vs prefill O")
-    H.assert_close(lse[0], Lp[0, :, -1].double().numpy(), H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+    H.assert_lse_close(lse[0], Lp[0, :, -1].double().numpy(), "LSE")
 
 
 def test_combine_invariant_over_chunk_sizes():

@@ -84,4 +84,4 @@ def test_paged_decode_equals_contiguous_and_oracle(B, Hq, Hkv, D, lens, Lmax, ch
     q_rot, k_rot = oracle_inputs(q, ks, lens)
     Ow, Lw = orc.decode(q_rot, k_rot, vs, lens)
     H.assert_close(got[2], Ow)
-    H.assert_close(got[3], Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+    H.assert_lse_close(got[3], Lw, "LSE")

@@ -32,7 +32,7 @@ def _check_case(B, S, Hq, Hkv, D, dtype, seed, n_docs=None, n_docs_max=1, positi
         Ow[b:b + 1], Lw[b:b + 1] = orc.rope_attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], cu[b],
                                                       500000.0, pb)
     H.assert_close(O, Ow)
-    H.assert_close(L, Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+    H.assert_lse_close(L, Lw, "LSE")
     return O, L
 
 
@@ -154,4 +154,4 @@ def test_softmax_scale_argument():
     O, L, _, _ = H.run_prefill(q, k, v, None, softmax_scale=0.05)
     Ow, Lw = orc.rope_attention(q, k, v, None, 500000.0, scale=0.05)
     H.assert_close(O, Ow)
-    H.assert_close(L, Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+    H.assert_lse_close(L, Lw, "LSE")

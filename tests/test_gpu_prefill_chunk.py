@@ -66,7 +66,7 @@ def test_prefill_chunk_matches_oracle(B, S, Sq, Hq, Hkv, D, dtype, seed, nd):
     for b in range(B):
         Ow, Lw = orc.rope_attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], cu[b], BASE, rows=rows)
         H.assert_close(O[b:b + 1], Ow)
-        H.assert_close(L[b:b + 1], Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+        H.assert_lse_close(L[b:b + 1], Lw, "LSE")
 
 
 def test_prefill_chunk_with_positions_matches_oracle():
@@ -81,7 +81,7 @@ def test_prefill_chunk_with_positions_matches_oracle():
     O, L = _chunk(_dev(q[:, S - Sq:].contiguous()), kr, _dev(v), cu, positions=pos[:, S - Sq:])
     Ow, Lw = orc.rope_attention(q, k, v, cu, BASE, pos, rows=np.arange(S - Sq, S))
     H.assert_close(O, Ow)
-    H.assert_close(L, Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+    H.assert_lse_close(L, Lw, "LSE")
 
 
 @pytest.mark.parametrize("Hq,Hkv,S,Sq", [(32, 8, 640, 192), (16, 1, 500, 52), (8, 8, 800, 544)])

@@ -83,7 +83,7 @@ def test_ring_matches_oracle(S, bounds, Hq, Hkv, D, dtype, seed, nd, fused):
     O, L = _ring(qd, kr, _dev(v), cu, bounds, rb)
     Ow, Lw = orc.rope_attention(q, k, v, cu, BASE)
     H.assert_close(O, Ow)
-    H.assert_close(L, Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+    H.assert_lse_close(L, Lw, "LSE")
 
 
 def test_ring_single_shard_equals_gqa_prefill():

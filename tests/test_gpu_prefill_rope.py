@@ -53,7 +53,7 @@ def test_prefill_rope_matches_oracle(B, S, Hq, Hkv, D, dtype, seed, nd, position
         Ow[b:b + 1], Lw[b:b + 1] = orc.rope_attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], cu[b],
                                                       500000.0, pb)
     H.assert_close(O, Ow)
-    H.assert_close(L, Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+    H.assert_lse_close(L, Lw, "LSE")
 
 
 def test_prefill_rope_agrees_with_the_two_call_path():
@@ -104,4 +104,4 @@ def test_prefill_rope_half_pairing_matches_oracle(B, S, Hq, Hkv, D, seed, positi
     O, L = _fused(q, k, v, cu, pos, pairing="half")
     Ow, Lw = orc.rope_attention(q, k, v, cu, 500000.0, pos, pairing="half")
     H.assert_close(O, Ow)
-    H.assert_close(L, Lw, H.LSE_MAX_ABS, H.LSE_MAX_ABS, "LSE")
+    H.assert_lse_close(L, Lw, "LSE")

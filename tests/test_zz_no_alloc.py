@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import LSE_MAX_ABS, MEAN_ABS, assert_close, say
+from gpu_helpers import assert_close, assert_lse_close, say
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def test_noalloc_equals_workspace_decode_on_two_calls(gpu_lib):
         # and the oracle (keys in the cache are used as stored)
         ow, lw = orc.decode(q.double().numpy(), kc.double().numpy(), vc.double().numpy(), lens)
         assert_close(o.cpu(), ow, what="o")
-        assert_close(lse.cpu().double(), lw, LSE_MAX_ABS, MEAN_ABS, "lse")
+        assert_lse_close(lse.cpu().double(), lw, "lse")
 
 
 def test_noalloc_full_size_405b_decode_equals_workspace_decode(gpu_lib):
