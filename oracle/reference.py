@@ -267,6 +267,94 @@ def attention_backward(qr, kr, v, dO, cu_docs=None, scale: Optional[float] = Non
     return dq, dk, dv
 
 
+def attention_backward_rows(qr, kr, v, dO, rows, keys, cu_docs=None, scale: Optional[float] = None,
+                            block: int = 64, magnitudes: bool = False):
+    """``attention_backward`` of one sequence, restricted to the query rows
+    whose dq and the keys whose dk, dv are asked for, at sizes where the whole
+    gradient in fp64 is out of reach.
+
+    qr, dO [S,Hq,D]; kr, v [S,Hkv,D] (rotated; any array type). dq_i needs only
+    row i's own softmax; dk_j and dv_j sum over every query row i >= j of
+    j's document, so those rows' softmaxes are formed as well (each over its
+    whole visible window, in blocks of ``block`` rows). The terms are those of
+    ``attention_backward``, summed over rows (and the g heads of a KV head)
+    for dk, dv and over keys for dq:
+      dv_j = sum P_ij dO_i,  dk_j = scale sum dS_ij qr_i,  dq_i = scale sum_j dS_ij kr_j.
+    Returns dq [R,Hq,D], dk [K,Hkv,D], dv [K,Hkv,D] in the order asked. With
+    ``magnitudes``, also (l1, l2): for each of the three, per element, the sum
+    of the absolute values and the root of the sum of squares of its terms.
+    """
+    S, Hq, D = qr.shape
+    Hkv = kr.shape[1]
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    cu = np.asarray([0, S] if cu_docs is None else cu_docs, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    if np.unique(rows).size != rows.size:
+        raise ValueError("rows must be distinct")
+    doc = document_of(cu, S)
+    dq = np.zeros((rows.size, Hq, D))
+    dk = np.zeros((keys.size, Hkv, D))
+    dv = np.zeros((keys.size, Hkv, D))
+    l1 = [np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)]
+    sq = [np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)]
+    # rows whose softmax is needed: those asked for, and every row at or after
+    # an asked-for key within its document
+    need = np.zeros(S, dtype=bool)
+    need[rows] = True
+    for d in np.unique(doc[keys]):
+        need[int(keys[doc[keys] == d].min()):int(cu[d + 1])] = True
+    want_row = {int(r): n for n, r in enumerate(rows)}
+    for d in np.unique(doc[np.flatnonzero(need)]):
+        lo = int(cu[d])
+        rows_d = np.flatnonzero(need & (doc == d))
+        hi_d = int(rows_d.max()) + 1
+        kw, vw = _f64(kr[lo:hi_d]), _f64(v[lo:hi_d])          # [W, Hkv, D]
+        kd = np.flatnonzero(doc[keys] == d)                     # output slots of d's keys
+        kcol = keys[kd] - lo
+        for b0 in range(0, rows_d.size, block):
+            ri = rows_d[b0:b0 + block]
+            n, W = ri.size, int(ri.max()) + 1 - lo
+            qi, gi = _f64(qr[ri]), _f64(dO[ri])                # [n, Hq, D]
+            visible = np.arange(lo, lo + W)[None, :] <= ri[:, None]
+            asked = [(m, want_row[int(r)]) for m, r in enumerate(ri) if int(r) in want_row]
+            am = np.array([m for m, _ in asked], dtype=np.int64)
+            ao = np.array([o for _, o in asked], dtype=np.int64)
+            kin = kcol < W
+            cols, slots = kcol[kin], kd[kin]
+            for kv in range(Hkv):
+                heads = slice(kv * g, (kv + 1) * g)
+                qh = qi[:, heads, :].reshape(n * g, D)
+                gh = gi[:, heads, :].reshape(n * g, D)
+                s = (qh @ kw[:W, kv, :].T).reshape(n, g, W) * scale
+                s = np.where(visible[:, None, :], s, -np.inf)
+                e = np.exp(s - s.max(axis=2, keepdims=True))
+                P = e / e.sum(axis=2, keepdims=True)
+                dP = (gh @ vw[:W, kv, :].T).reshape(n, g, W)
+                dS = P * (dP - (P * dP).sum(axis=2, keepdims=True))
+                if am.size:
+                    t = scale * dS[am].reshape(am.size * g, W)
+                    kk = kw[:W, kv, :]
+                    dq[ao, heads, :] = (t @ kk).reshape(am.size, g, D)
+                    if magnitudes:
+                        l1[0][ao, heads, :] = (np.abs(t) @ np.abs(kk)).reshape(am.size, g, D)
+                        sq[0][ao, heads, :] = ((t * t) @ (kk * kk)).reshape(am.size, g, D)
+                if cols.size:
+                    Pc = P[:, :, cols].reshape(n * g, cols.size).T          # [C, n*g]
+                    Sc = scale * dS[:, :, cols].reshape(n * g, cols.size).T
+                    np.add.at(dv, (slots, kv), Pc @ gh)
+                    np.add.at(dk, (slots, kv), Sc @ qh)
+                    if magnitudes:
+                        np.add.at(l1[2], (slots, kv), np.abs(Pc) @ np.abs(gh))
+                        np.add.at(l1[1], (slots, kv), np.abs(Sc) @ np.abs(qh))
+                        np.add.at(sq[2], (slots, kv), (Pc * Pc) @ (gh * gh))
+                        np.add.at(sq[1], (slots, kv), (Sc * Sc) @ (qh * qh))
+    if magnitudes:
+        return dq, dk, dv, (l1, [np.sqrt(x) for x in sq])
+    return dq, dk, dv
+
+
 def decode_partials(q_rot, k_cache, v_cache, seq_lens, kv_chunk: int, max_splits: int,
                     scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Attention of each new token restricted to each chunk of its cache.

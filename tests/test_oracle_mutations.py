@@ -100,7 +100,38 @@ def _backward_variant(no_row_term=False, overwrite_heads=False, dq_unscaled=Fals
     return attention_backward
 
 
+_real_bwd_rows = orc.attention_backward_rows
+
+
+def _bwd_rows_keys_from_asked_rows(qr, kr, v, dO, rows, keys, cu_docs=None, scale=None, block=64,
+                                   magnitudes=False):
+    """Slip: dk and dv summed over the asked-for query rows only, not over
+    every row that sees the key (the other rows' output gradients dropped)."""
+    keep = np.zeros(qr.shape[0], dtype=bool)
+    keep[np.asarray(rows)] = True
+    dO = np.where(keep[:, None, None], orc._f64(dO), 0.0)
+    return _real_bwd_rows(qr, kr, v, dO, rows, keys, cu_docs, scale, block, magnitudes)
+
+
+def _bwd_rows_no_documents(qr, kr, v, dO, rows, keys, cu_docs=None, scale=None, block=64, magnitudes=False):
+    """Slip: the rows' softmax windows start at the sequence start."""
+    return _real_bwd_rows(qr, kr, v, dO, rows, keys, None, scale, block, magnitudes)
+
+
+def _bwd_rows_magnitude_of_sum(qr, kr, v, dO, rows, keys, cu_docs=None, scale=None, block=64,
+                               magnitudes=False):
+    """Slip: the l1 magnitude taken as |sum of terms| instead of the sum of |terms|."""
+    out = _real_bwd_rows(qr, kr, v, dO, rows, keys, cu_docs, scale, block, magnitudes)
+    if not magnitudes:
+        return out
+    return out[:3] + (([np.abs(x) for x in out[:3]], out[3][1]),)
+
+
 MUTATIONS = {
+    "restricted backward: keys fed by the asked rows only": ("attention_backward_rows",
+                                                            _bwd_rows_keys_from_asked_rows),
+    "restricted backward: no document starts": ("attention_backward_rows", _bwd_rows_no_documents),
+    "restricted backward: l1 of the sum": ("attention_backward_rows", _bwd_rows_magnitude_of_sum),
     "backward drops the softmax row term": ("attention_backward", _backward_variant(no_row_term=True)),
     "backward keeps one head per KV head": ("attention_backward", _backward_variant(overwrite_heads=True)),
     "backward dq without the scale": ("attention_backward", _backward_variant(dq_unscaled=True)),
@@ -135,6 +166,9 @@ PIN_CALLS = [
     pins.test_attention_with_half_pairing_equals_permuted_adjacent,
     pins.test_backward_matches_finite_differences,
     pins.test_backward_matches_autograd_of_sdpa,
+    lambda: pins.test_restricted_backward_equals_full_backward(11, 29, 4, 2, 8, [0, 9, 9, 21, 29]),
+    pins.test_restricted_backward_matches_autograd_of_sdpa,
+    pins.test_restricted_backward_magnitudes,
 ]
 
 

@@ -170,6 +170,90 @@ def test_backward_matches_autograd_of_sdpa():
     np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("seed,S,Hq,Hkv,D,cu", [
+    (11, 29, 4, 2, 8, [0, 9, 9, 21, 29]),    # an empty document
+    (12, 40, 6, 3, 4, [0, 40]),
+    (13, 33, 8, 1, 8, [0, 1, 2, 17, 33]),   # one-token documents, g = 8
+])
+def test_restricted_backward_equals_full_backward(seed, S, Hq, Hkv, D, cu):
+    """The row/key-restricted backward returns exactly the full backward's
+    dq at the asked rows and dk, dv at the asked keys, for any subsets (rows in
+    any order, keys repeated), with blocks smaller than a document."""
+    rng = np.random.default_rng(seed)
+    qr, kr, v = (rng.standard_normal((1, S, H, D)) for H in (Hq, Hkv, Hkv))
+    dO = rng.standard_normal((1, S, Hq, D))
+    cu = np.array(cu)
+    Wq, Wk, Wv = orc.attention_backward(qr, kr, v, dO, cu)
+    for trial in range(3):
+        rows = rng.permutation(S)[:rng.integers(1, S)]
+        keys = rng.integers(0, S, size=rng.integers(1, S))
+        dq, dk, dv = orc.attention_backward_rows(qr[0], kr[0], v[0], dO[0], rows, keys, cu, block=5)
+        np.testing.assert_allclose(dq, Wq[0, rows], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dk, Wk[0, keys], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dv, Wv[0, keys], rtol=0, atol=1e-12)
+
+
+def test_restricted_backward_matches_autograd_of_sdpa():
+    """The restricted backward against the library route directly (torch
+    autograd of fp64 scaled_dot_product_attention, KV heads repeated), with an
+    explicit softmax scale."""
+    rng = np.random.default_rng(14)
+    S, Hq, Hkv, D = 24, 8, 2, 16
+    g = Hq // Hkv
+    qr, kr, v = (rng.standard_normal((S, H, D)) for H in (Hq, Hkv, Hkv))
+    dO = rng.standard_normal((S, Hq, D))
+    cu = np.array([0, 10, 24])
+    tq, tk, tv = (torch.tensor(x[None], requires_grad=True) for x in (qr, kr, v))
+    doc = torch.bucketize(torch.arange(S), torch.as_tensor(cu[1:-1]), right=True)
+    i = torch.arange(S)
+    mask = (i[None, :] <= i[:, None]) & (doc[None, :] == doc[:, None])
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq.transpose(1, 2), tk.repeat_interleave(g, dim=2).transpose(1, 2),
+        tv.repeat_interleave(g, dim=2).transpose(1, 2), attn_mask=mask, scale=0.3)
+    (out.transpose(1, 2) * torch.tensor(dO[None])).sum().backward()
+    rows, keys = np.array([23, 0, 10, 9, 15]), np.array([0, 9, 10, 23, 4])
+    dq, dk, dv = orc.attention_backward_rows(qr, kr, v, dO, rows, keys, cu, scale=0.3)
+    np.testing.assert_allclose(dq, tq.grad[0].numpy()[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad[0].numpy()[keys], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad[0].numpy()[keys], rtol=0, atol=1e-12)
+
+
+def test_restricted_backward_magnitudes():
+    """The per-element term magnitudes: with zero queries every visible weight
+    of row i is 1 / (i - start + 1), so dv_j's terms are dO_i / (i - start + 1)
+    over the rows i >= j of j's document (closed forms for the sum of absolute
+    values and the root of the sum of squares), and dk's terms are all zero;
+    a document of one token has P = 1 and dS = 0 (dq and its magnitudes
+    vanish). For random inputs, |gradient| <= l1 and l2 <= l1 <= sqrt(terms) l2."""
+    rng = np.random.default_rng(15)
+    S, Hq, Hkv, D = 20, 4, 2, 8
+    g = Hq // Hkv
+    cu = np.array([0, 1, 12, 20])
+    kr, v = (rng.standard_normal((S, Hkv, D)) for _ in range(2))
+    dO = rng.standard_normal((S, Hq, D))
+    rows, keys = np.arange(S), np.arange(S)
+    dq, dk, dv, (l1, l2) = orc.attention_backward_rows(np.zeros((S, Hq, D)), kr, v, dO, rows, keys, cu,
+                                                       magnitudes=True)
+    doc = orc.document_of(cu, S)
+    for j in range(S):
+        a, e = cu[doc[j]], cu[doc[j] + 1]
+        w = 1.0 / (np.arange(j, e) - a + 1)                                  # P_ij for i >= j
+        t = w[:, None, None, None] * dO[j:e].reshape(e - j, Hkv, g, D)     # terms over (i, head)
+        t = t.transpose(0, 2, 1, 3).reshape(-1, Hkv, D)
+        np.testing.assert_allclose(dv[j], t.sum(axis=0), rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(l1[2][j], np.abs(t).sum(axis=0), rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(l2[2][j], np.sqrt((t * t).sum(axis=0)), rtol=1e-13, atol=1e-13)
+    assert np.all(dk == 0) and np.all(l1[1] == 0) and np.all(l2[1] == 0)
+    assert np.all(dq[0] == 0) and np.all(l1[0][0] == 0)
+    qr = rng.standard_normal((S, Hq, D))
+    dq, dk, dv, (l1, l2) = orc.attention_backward_rows(qr, kr, v, dO, rows, keys, cu, magnitudes=True)
+    n_terms = [S * np.ones(1), S * g * np.ones(1), S * g * np.ones(1)]
+    for x, a1, a2, n in zip((dq, dk, dv), l1, l2, n_terms):
+        assert np.all(np.abs(x) <= a1 * (1 + 1e-12) + 1e-15)
+        assert np.all(a2 <= a1 * (1 + 1e-12) + 1e-15)
+        assert np.all(a1 <= np.sqrt(n) * a2 * (1 + 1e-12) + 1e-15)
+
+
 # ---------------------------------------------------------------- invariants
 
 def test_gqa_equals_mha_with_repeated_kv():
