@@ -11,7 +11,11 @@ import torch
 
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
+# LSE: max-abs 2e-2 as for O; mean-abs the same 2e-3 bar (the bf16 rounding of
+# the weights inside the row sum bounds |dLSE| by ln(1 + 2^-9) ~ 2e-3 per row in
+# the worst case and averages far below it)
 LSE_MAX_ABS = 2e-2
+LSE_MEAN_ABS = 2e-3
 
 
 def say(*args):
@@ -50,8 +54,97 @@ def assert_close(got, want, max_abs=MAX_ABS, mean_abs=MEAN_ABS, what="O"):
     got = got.double().numpy() if isinstance(got, torch.Tensor) else np.asarray(got)
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     mx, mn = errors(got, want)
+    print(f"[err] {what}: max-abs {mx:.3e} mean-abs {mn:.3e}", flush=True)
     assert mx <= max_abs and mn <= mean_abs, f"{what}: max-abs {mx:.3e} mean-abs {mn:.3e}"
     return mx, mn
+
+
+def assert_lse_close(got, want, what="LSE"):
+    """LSE against the oracle at the LSE bar (max-abs 2e-2, mean-abs 2e-3)."""
+    return assert_close(got, want, LSE_MAX_ABS, LSE_MEAN_ABS, what)
+
+
+def oracle_rows_threaded(q, k, v, rows, cu, base, n_threads=16, chunk=64):
+    """The fp64 row oracle (oracle.reference.rope_attention_rows) evaluated on
+    chunks of the asked-for rows by a pool of threads, each with a
+    single-threaded BLAS: NumPy releases the interpreter lock in its matrix
+    products and large element-wise passes, so the chunks run in parallel.
+    Every row's value is computed by the oracle itself; only the work is
+    divided. Returns O [R,Hq,D] and LSE [Hq,R] in the order of rows."""
+    import concurrent.futures as cf
+    from threadpoolctl import threadpool_limits
+    from oracle import reference as orc
+    rows = np.asarray(rows, dtype=np.int64)
+    parts = [rows[i:i + chunk] for i in range(0, rows.size, chunk)]
+    with threadpool_limits(limits=1, user_api="blas"):
+        with cf.ThreadPoolExecutor(max_workers=n_threads) as ex:
+            res = list(ex.map(lambda r: orc.rope_attention_rows(q, k, v, r, cu, base), parts))
+    O = np.concatenate([r[0] for r in res], axis=0)
+    L = np.concatenate([r[1] for r in res], axis=1)
+    return O, L
+
+
+# Gradient bar. Each term of a gradient sum (P_ij dO_i for dv, scale dS_ij q_i
+# for dk, scale dS_ij k_j for dq) is formed from bf16 inputs and goes through
+# at most two bf16 roundings (P or dS rounded for the matrix product, dS
+# carrying P's error), each at most 2^-9 relative; the sums run in fp32 and the
+# result is rounded once more to bf16 (at most 2^-9 |ref|). Worst case, per
+# element: |err| <= 2^-8 l1 + 2^-9 |ref| with l1 the sum of the terms' absolute
+# values; the bar allows 2^-7 l1 + 2^-8 |ref| (twice that) plus 1e-6 for fp32
+# rounding of sums that cancel to nearly zero. On average the roundings are
+# independent and uniform, so an element's error has standard deviation at
+# most 2^-9 sqrt(2/3) l2 (l2 the root of the sum of the squared terms) and
+# mean absolute value at most sqrt(2/pi) times that, 0.66 2^-9 l2, plus 2^-10
+# |ref| on average for the final rounding: the mean bar is 2^-8 mean(l2 + |ref|).
+GRAD_MAX_L1 = 2.0 ** -7
+GRAD_MAX_REF = 2.0 ** -8
+GRAD_MAX_FLOOR = 1e-6
+GRAD_MEAN = 2.0 ** -8
+
+
+def assert_grad_bar(got, want, l1, l2, what):
+    """A gradient against the oracle's fp64 values at the bar above: every
+    element within 2^-7 l1 + 2^-8 |ref| + 1e-6 and mean |err| within
+    2^-8 mean(l2 + |ref|)."""
+    got = got.double().numpy() if isinstance(got, torch.Tensor) else np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    d = np.abs(got - want)
+    lim = GRAD_MAX_L1 * l1 + GRAD_MAX_REF * np.abs(want) + GRAD_MAX_FLOOR
+    worst = float((d / lim).max())
+    mean_lim = GRAD_MEAN * float(np.mean(l2 + np.abs(want)))
+    mn = float(d.mean())
+    print(f"[grad] {what}: n {d.size} max|ref| {np.abs(want).max():.3e} max-abs {d.max():.3e} "
+          f"worst err/bar {worst:.3e} mean-abs {mn:.3e} (bar {mean_lim:.3e}) "
+          f"mean-abs / mean|ref| {mn / max(float(np.abs(want).mean()), 1e-30):.3e}", flush=True)
+    assert worst <= 1.0, f"{what}: an element exceeds its bar by {worst:.3f}x"
+    assert mn <= mean_lim, f"{what}: mean-abs {mn:.3e} above {mean_lim:.3e}"
+
+
+def backward_oracle_threaded(q, k, v, dout, rows, keys, cu, n_threads=16, scale=None):
+    """oracle.reference.attention_backward_rows (with term magnitudes) for one
+    sequence, one KV head group per task: the groups' gradients are
+    independent, so each task runs the oracle on its heads' slices (the
+    oracle's own arithmetic, only the work divided). Returns dq [R,Hq,D],
+    dk [K,Hkv,D], dv [K,Hkv,D] and (l1, l2) as the oracle does."""
+    import concurrent.futures as cf
+    from threadpoolctl import threadpool_limits
+    from oracle import reference as orc
+    Hq, Hkv = q.shape[1], k.shape[1]
+    g = Hq // Hkv
+    blas = max(1, n_threads // Hkv)
+
+    def one(kv):
+        h = slice(kv * g, (kv + 1) * g)
+        return orc.attention_backward_rows(q[:, h], k[:, kv:kv + 1], v[:, kv:kv + 1], dout[:, h], rows, keys,
+                                           cu, scale, magnitudes=True)
+
+    with threadpool_limits(limits=blas, user_api="blas"):
+        with cf.ThreadPoolExecutor(max_workers=min(Hkv, n_threads)) as ex:
+            res = list(ex.map(one, range(Hkv)))
+    cat = lambda i, ax: np.concatenate([r[i] for r in res], axis=ax)            # noqa: E731
+    l1 = [np.concatenate([r[3][0][t] for r in res], axis=1) for t in range(3)]
+    l2 = [np.concatenate([r[3][1][t] for r in res], axis=1) for t in range(3)]
+    return cat(0, 1), cat(1, 1), cat(2, 1), (l1, l2)
 
 
 def bf16_ulp(x):
@@ -93,5 +186,5 @@ def check_partials(op, lp, q_rot, k_rot, vs, lens, chunk):
                 want_l.append(ml)
                 n_runs += 1
     assert_close(np.array(got_o), np.array(want_o), what="o_part runs")
-    assert_close(np.array(got_l), np.array(want_l), LSE_MAX_ABS, LSE_MAX_ABS, "lse_part runs")
+    assert_lse_close(np.array(got_l), np.array(want_l), "lse_part runs")
     return n_runs
