@@ -3,18 +3,22 @@
 One step = one pass of the prefill path (rope_qk on the keys, then
 gqa_prefill_rope, which rotates the queries in the kernel and applies the
 causal + cross-document mask, writing O and the log-sum-exp) over one batch of
-seeded synthetic input of the Llama-3.1-8B layer shape (S=8192, 32 query heads
-on 8 KV heads, head_dim 128, bf16, 1-8 documents). Inputs are resident in HBM
-before the timed region starts.
+seeded synthetic input of the largest single-GPU workload: the 405B layer
+shape at the 128K context (S=131072, 128 query heads on 8 KV heads,
+head_dim 128, bf16, 4 documents). Inputs are resident in HBM before the timed
+region starts.
 
-The JSON line also carries the 8B-shape chunked prefill (the last 2048 tokens
-over a cached prefix of 6144), the 405B-shape prefill (S=32768, 128/8 heads)
-and the 405B-shape split-KV decode (16 sequences, cache lengths
-U[4096, 131072], measured as cache-read GB/s), each against its own roofline,
-plus the fp64 oracle timed on a bounded row sample of the headline workload.
+The JSON line also carries the other workloads, each against its own
+roofline: the 8B-shape prefill (with its chunked prefill and backward pass),
+the 405B-shape prefill at S=32768 (with the 8-shard context-parallel ring),
+the 405B-shape split-KV decode (16 sequences, cache lengths U[4096, 131072],
+as cache-read GB/s; contiguous, paged and allocation-free) and the tiny
+workload's absolute time; the fp64 oracle timed on bounded row samples of the
+workloads on the host cores; and a plain device copy's bandwidth (the scale
+for the HBM counters).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--only prefill|decode] [--with-128k]
+                       [--only prefill|decode|llama8b|llama405b|long128k|decode405b|tiny|copy|backward]
 """
 
 from __future__ import annotations
@@ -91,6 +95,57 @@ def setup_prefill(name: str):
     return st, (q, k, v)
 
 
+class ClockSampler:
+    """Samples the GPU's current shader clock from the kernel driver's DPM
+    table (the line of pp_dpm_sclk marked '*') every few milliseconds on a
+    host thread while the timed steps run; summary() gives the median, range
+    and count of the samples in MHz, or None where the file is not readable."""
+
+    def __init__(self, period_s: float = 0.005):
+        import glob
+        import threading
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            x = self._read()
+            if x is not None:
+                self.samples.append(x)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.path:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        x = np.asarray(self.samples)
+        return {"median_mhz": float(np.median(x)), "min_mhz": float(x.min()), "max_mhz": float(x.max()),
+                "samples": int(x.size), "source": self.path}
+
+
 def settle(step, seconds: float):
     """Run whole steps, untimed, for `seconds` of wall time before the warmup
     steps: the GPU's clocks ramp up over the first tens of milliseconds of
@@ -126,17 +181,18 @@ def time_prefill(st, steps: int, warmup: int, settle_s: float = 0.0):
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     rope_ms = [e[0].elapsed_time(e[1]) for e in evs]
     attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
     gpu_ms = [e[0].elapsed_time(e[2]) for e in evs]
     return dict(wall_ms_per_step=1e3 * wall / steps, rope_ms=float(np.mean(rope_ms)),
                 prefill_ms=float(np.mean(attn_ms)), gpu_ms_per_step=float(np.mean(gpu_ms)),
-                prefill_ms_median=float(np.median(attn_ms)))
+                prefill_ms_median=float(np.median(attn_ms)), gpu_clock=clk.summary())
 
 
 def time_backward(st, steps: int, warmup: int, settle_s: float = 0.0):
@@ -347,14 +403,38 @@ def time_decode(st, steps: int, warmup: int, settle_s: float = 0.0, paged: bool 
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
+    with ClockSampler(0.001) as clk:
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
     dec = [e[0].elapsed_time(e[1]) for e in evs]
     comb = [e[1].elapsed_time(e[2]) for e in evs]
     tot = [e[0].elapsed_time(e[2]) for e in evs]
     return dict(decode_ms=float(np.mean(dec)), combine_ms=float(np.mean(comb)),
-                ms_per_step=float(np.mean(tot)), decode_ms_median=float(np.median(dec)))
+                ms_per_step=float(np.mean(tot)), decode_ms_median=float(np.median(dec)),
+                gpu_clock=clk.summary())
+
+
+def time_noalloc(st, steps: int, warmup: int, settle_s: float = 0.0) -> float:
+    """ms per gqa_decode_noalloc call (decode + combine, partials in the
+    library's scratch) on the contiguous cache."""
+    import torch
+    import gqa_attention_rope_02_amd as la
+
+    def step():
+        la.gqa_decode_noalloc(st["q"], st["kc"], st["vc"], st["sl"], KV_CHUNK, st["o"])
+
+    settle(step, settle_s)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def decode_bytes(st) -> float:
@@ -367,13 +447,14 @@ def decode_bytes(st) -> float:
 COPY_BYTES = 1 << 30
 
 
-def copy_calibration(reps: int = 3):
+def copy_calibration(reps: int = 10):
     """A plain elementwise device copy of COPY_BYTES (read once, written once):
     what FETCH_SIZE and WRITE_SIZE read for it is the scale that turns those
     counters into HBM bytes for the attention kernels of the same run."""
     import torch
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    settle(lambda: torch.mul(src, 1.0, out=dst), 0.3)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -389,51 +470,132 @@ def copy_calibration(reps: int = 3):
 
 # ----------------------------------------------------------------- cpu oracle
 
-def cpu_baseline(host_inputs, w, cu, budget_s: float = 20.0):
-    """The fp64 oracle on a row sample of the same workload, as TFLOP/s."""
-    from oracle import reference as orc
-    from workloads import sample_rows
-    q, k, v = host_inputs
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    rows_all = sample_rows(w.S, cu, w.seed, n_random=4096, tile=64, n_edges=0)
+        return os.cpu_count() or 1
+
+
+def cpu_prefill_rate(host_inputs, w, cu, budget_s: float):
+    """The fp64 row oracle (incl. RoPE), as it stands, on 64-row blocks of
+    consecutive query rows (all heads) drawn uniformly, one oracle call per
+    block, for about budget_s seconds: TFLOP/s counting 4 D per visible
+    (query head, key) pair of the rows done, and the whole workload's oracle
+    time extrapolated linearly in visible pairs."""
+    from oracle import reference as orc
+    q, k, v = host_inputs
     rng = np.random.default_rng(w.seed + 7)
-    rows_all = rng.permutation(rows_all)
     doc = orc.document_of(cu, w.S)
     start = np.asarray(cu)[doc]
-    done, flops, t_used = 0, 0.0, 0.0
+    blk = 64
+    order = rng.permutation(-(-w.S // blk))
+    done_rows, done_blocks, flops, t_used = 0, 0, 0.0, 0.0
     t0 = time.perf_counter()
-    chunk = 256
-    while done < rows_all.size and t_used < budget_s:
-        rows = np.sort(rows_all[done:done + chunk])
-        orc.rope_attention(q, k, v, cu, w.rope_base, None, None, rows)
-        done += rows.size
+    for b in order:
+        rows = np.arange(b * blk, min((b + 1) * blk, w.S))
+        orc.rope_attention_rows(q[0], k[0], v[0], rows, cu, w.rope_base, block=blk)
+        done_rows += rows.size
+        done_blocks += 1
         flops += 4.0 * w.D * w.Hq * float(np.sum(rows - start[rows] + 1))
         t_used = time.perf_counter() - t0
-    return dict(value=flops / t_used / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=f"{done} query rows x all {w.Hq} heads of the {w.name} prefill "
-                       f"(fp64 NumPy oracle incl. RoPE), {t_used:.1f}s")
+        if t_used >= budget_s:
+            break
+    rate = flops / t_used
+    whole = prefill_flops(w, cu)
+    full = done_rows >= w.S
+    return dict(value=rate / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+                cpu_model=cpu_model(),
+                sample=(f"all {w.S} query rows" if full else
+                        f"{done_blocks} uniformly drawn blocks of {blk} consecutive query rows "
+                        f"({done_rows} of {w.S} rows)") +
+                       f" x all {w.Hq} heads of the {w.name} prefill (fp64 NumPy row oracle incl. RoPE, "
+                       f"one call per block), {t_used:.1f}s",
+                oracle_s_whole_workload=round(whole / rate, 1),
+                extrapolated=not full)
+
+
+def cpu_decode_rate(st, budget_s: float):
+    """The fp64 decode oracle on whole (sequence, KV head) caches of the decode
+    workload, sequences in a drawn order, for about budget_s seconds: cache
+    bytes (K and V, bf16) processed per second, extrapolated to the whole
+    workload."""
+    from oracle import reference as orc
+    w, lens = st["w"], st["lens"]
+    g = w.Hq // w.Hkv
+    rng = np.random.default_rng(w.seed + 7)
+    pairs = [(int(b), int(h)) for b in rng.permutation(w.B) for h in rng.permutation(w.Hkv)]
+    done, nbytes, t_used = 0, 0.0, 0.0
+    t0 = time.perf_counter()
+    for b, h in pairs:
+        L = int(lens[b])
+        qb = st["q"][b:b + 1, h * g:(h + 1) * g].cpu()
+        kb = [st["kc"][b, h:h + 1, :L].cpu()]
+        vb = [st["vc"][b, h:h + 1, :L].cpu()]
+        orc.decode(qb, kb, vb, [L])
+        done += 1
+        nbytes += L * w.D * 2 * 2
+        t_used = time.perf_counter() - t0
+        if t_used >= budget_s:
+            break
+    rate = nbytes / t_used
+    return dict(value=rate / 1e9, unit="GB/s", cores=blas_threads(), kind="oracle", cpu_model=cpu_model(),
+                sample=f"{done} of {len(pairs)} (sequence, KV head) caches of the decode405b workload "
+                       f"(fp64 NumPy decode oracle), {t_used:.1f}s",
+                oracle_s_whole_workload=round(decode_bytes(st) / rate, 1), extrapolated=done < len(pairs))
+
+
+def cpu_tiny_rate(host_inputs, w, cu):
+    """The whole tiny workload through the fp64 oracle (incl. RoPE)."""
+    from oracle import reference as orc
+    q, k, v = host_inputs
+    t0 = time.perf_counter()
+    orc.rope_attention(q, k, v, cu, w.rope_base)
+    t = time.perf_counter() - t0
+    return dict(value=prefill_flops(w, cu) / t / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+                cpu_model=cpu_model(), sample=f"the whole tiny workload, {t * 1e3:.1f} ms", extrapolated=False)
 
 
 # ------------------------------------------------------------------------ main
 
+def prefill_record(st, t, label):
+    """Rates of one timed prefill workload: path (keys' RoPE + prefill) and
+    kernel, against the bf16 MFMA peak."""
+    w, cu = st["w"], st["cu"]
+    fl = prefill_flops(w, cu)
+    return {"workload": label, "documents": int(cu.size - 1), "allowed_pairs": allowed_pairs(cu), "flops": fl,
+            "tflops_path": round(fl / (t["gpu_ms_per_step"] * 1e-3) / 1e12, 2),
+            "tflops_kernel": round(fl / (t["prefill_ms"] * 1e-3) / 1e12, 2),
+            "frac_kernel": round(fl / (t["prefill_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "ms_per_step": round(t["gpu_ms_per_step"], 4), "prefill_ms": round(t["prefill_ms"], 4),
+            "rope_ms": round(t["rope_ms"], 4), "gpu_clock": t["gpu_clock"]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle", type=float, default=0.3,
                     help="seconds of untimed whole steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "llama8b", "llama405b", "decode405b", "copy", "backward"],
-                    default=None, help="run one part: both prefills, the decode, one workload, "
-                                       "or only the copy used to scale HBM counters")
-    ap.add_argument("--with-128k", action="store_true", help="also time the S=131072 prefill")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run a plain device copy of known size (scale for FETCH/WRITE_SIZE)")
+    ap.add_argument("--only", default=None,
+                    choices=["prefill", "decode", "llama8b", "llama405b", "long128k", "decode405b", "tiny",
+                             "copy", "backward"],
+                    help="run one part: the prefills, the decode, one workload, the backward pass, "
+                         "or only the copy used to scale HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -449,64 +611,73 @@ def main():
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "settle_s": args.settle,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-           "data": "synthetic (seeded N(0,1) Q/K/V, seeded document cuts)"}
+           "data": "synthetic (seeded N(0,1) Q/K/V, seeded document cuts and cache lengths)"}
     phash = kernel_hash("gqa_prefill.hip")
-    run_8b = args.only in (None, "prefill", "llama8b")
-    run_405 = args.only in (None, "prefill", "llama405b")
-    run_dec = args.only in (None, "decode", "decode405b")
+    only = args.only
+    run = lambda *names: only is None or only in names   # noqa: E731
+    cpu = not args.no_cpu_baseline
+    cpu_cfg = {}
+    extra_steps = max(3, args.steps // 2)
 
-    if args.calibrate_copy or args.only == "copy":
-        out["copy_calibration"] = copy_calibration()
-        if args.only == "copy":
-            out.update(value=out["copy_calibration"]["gbs"], unit="GB/s",
-                       config={"workload": "plain device copy of 1 GiB"})
+    out["copy_calibration"] = copy_calibration()
+    if only == "copy":
+        out.update(value=out["copy_calibration"]["gbs"], unit="GB/s",
+                   config={"workload": "plain device copy of 1 GiB"})
 
-    if args.only == "backward":
-        st, _ = setup_prefill("llama8b")
-        tb = time_backward(st, args.steps, args.warmup, args.settle)
-        flb = 10.0 * st["w"].D * st["w"].Hq * st["w"].B * allowed_pairs(st["cu"])
-        tf = flb / (tb["backward_ms"] * 1e-3) / 1e12
-        out.update(value=round(tf, 2), unit="TFLOP/s", ms_per_step=round(tb["backward_ms"], 4),
-                   config={"workload": "llama-3.1-8b attention layer backward (gqa_attention_backward)"},
-                   frac=round(tf / PEAK_BF16_TFLOPS, 4))
-
-    if run_8b:
-        st, host = setup_prefill("llama8b")
+    # ---- headline: the 128K prefill (largest single-GPU workload) -------------
+    if run("prefill", "long128k"):
+        st, host = setup_prefill("long128k")
         w, cu = st["w"], st["cu"]
         t = time_prefill(st, args.steps, args.warmup, args.settle)
         fl = prefill_flops(w, cu)
-        value = fl / (t["gpu_ms_per_step"] * 1e-3) / 1e12
         achieved = fl / (t["prefill_ms"] * 1e-3) / 1e12
-        out.update(value=round(value, 2), unit="TFLOP/s", ms_per_step=round(t["gpu_ms_per_step"], 4))
-        out["config"] = {"workload": "llama-3.1-8b attention layer prefill: rope_qk (keys) + "
-                                     "gqa_prefill_rope (queries rotated in the kernel), "
+        out.update(value=round(fl / (t["gpu_ms_per_step"] * 1e-3) / 1e12, 2), unit="TFLOP/s",
+                   ms_per_step=round(t["gpu_ms_per_step"], 4))
+        out["config"] = {"workload": "llama-3.1-405b attention layer prefill at the 128K context: "
+                                     "rope_qk (keys) + gqa_prefill_rope (queries rotated in the kernel), "
                                      "causal + cross-document mask",
-                         "batch": w.B, "seq_len": w.S, "q_heads": w.Hq, "kv_heads": w.Hkv,
-                         "head_dim": w.D, "rope_base": w.rope_base, "documents": int(cu.size - 1),
-                         "allowed_pairs": allowed_pairs(cu), "flops_per_step": fl,
-                         "parallelism": "none (1 GPU)"}
-        out["roofline"] = {"kernel": "gqa_prefill_rope", "bound": "mfma", "achieved": round(achieved, 2),
-                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "batch": w.B, "seq_len": w.S, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
+                         "rope_base": w.rope_base, "documents": int(cu.size - 1),
+                         "document_lengths": np.diff(cu).tolist(), "seed": w.seed,
+                         "allowed_pairs": allowed_pairs(cu), "flops_per_step": fl, "parallelism": "none (1 GPU)"}
+        out["roofline"] = {"kernel": "gqa_prefill_rope (prefill_kernel<bf16, D=128, g=16>)", "bound": "mfma",
+                           "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                           "traffic": measured_traffic("gqa_prefill", "llama8b", phash),
+                           "traffic": measured_traffic("gqa_prefill", "long128k", phash),
                            "launch_ms": round(t["prefill_ms"], 4)}
-        out["timing"] = {k: round(x, 4) for k, x in t.items()}
-        Sq = 2048
-        tc = time_chunk(st, Sq, args.steps, args.warmup, args.settle, CHUNK_SPLIT_TILES)
-        tu = time_chunk(st, Sq, args.steps, args.warmup, 0.0)
-        flc = 4.0 * w.D * w.Hq * w.B * chunk_pairs(cu, w.S, Sq)
-        out["prefill_chunk_8b"] = {
-            "workload": f"llama-3.1-8b chunked prefill: the last {Sq} of {w.S} tokens over the "
-                        f"cached prefix (rope_qk on the block's keys + gqa_prefill_split, key ranges "
-                        f"in pieces of {CHUNK_SPLIT_TILES} x 64 keys, partials merged)",
-            "flops": flc,
-            "tflops_path": round(flc / (tc["gpu_ms_per_step"] * 1e-3) / 1e12, 2),
-            "tflops_kernel": round(flc / (tc["chunk_ms"] * 1e-3) / 1e12, 2),
-            "frac_kernel": round(flc / (tc["chunk_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "chunk_ms": round(tc["chunk_ms"], 4), "rope_ms": round(tc["rope_ms"], 4),
-            "unsplit_chunk_ms": round(tu["chunk_ms"], 4),
-            "unsplit_tflops_kernel": round(flc / (tu["chunk_ms"] * 1e-3) / 1e12, 2)}
-        tb = time_backward(st, max(args.steps // 4, 5), max(args.warmup // 2, 2), args.settle)
+        out["timing"] = {k: (round(x, 4) if isinstance(x, float) else x) for k, x in t.items()}
+        if cpu:
+            log("timing the fp64 oracle on a row sample of the 128K prefill ...")
+            out["cpu_baseline"] = cpu_prefill_rate(host, w, cu, 15.0)
+        del st, host
+        torch.cuda.empty_cache()
+
+    # ---- 8B: prefill, chunked prefill, backward ---------------------------------
+    if run("prefill", "llama8b", "backward"):
+        st, host = setup_prefill("llama8b")
+        w, cu = st["w"], st["cu"]
+        if only != "backward":
+            t = time_prefill(st, args.steps, args.warmup, args.settle)
+            out["prefill_8b"] = prefill_record(
+                st, t, "llama-3.1-8b attention layer prefill S=8192, 32 q / 8 kv heads: rope_qk (keys) + "
+                       "gqa_prefill_rope")
+            out["prefill_8b"]["traffic"] = measured_traffic("gqa_prefill", "llama8b", phash)
+            Sq = 2048
+            tc = time_chunk(st, Sq, args.steps, args.warmup, args.settle, CHUNK_SPLIT_TILES)
+            tu = time_chunk(st, Sq, args.steps, args.warmup, 0.0)
+            flc = 4.0 * w.D * w.Hq * w.B * chunk_pairs(cu, w.S, Sq)
+            out["prefill_chunk_8b"] = {
+                "workload": f"llama-3.1-8b chunked prefill: the last {Sq} of {w.S} tokens over the "
+                            f"cached prefix (rope_qk on the block's keys + gqa_prefill_split, key ranges "
+                            f"in pieces of {CHUNK_SPLIT_TILES} x 64 keys, partials merged)",
+                "flops": flc,
+                "tflops_path": round(flc / (tc["gpu_ms_per_step"] * 1e-3) / 1e12, 2),
+                "tflops_kernel": round(flc / (tc["chunk_ms"] * 1e-3) / 1e12, 2),
+                "frac_kernel": round(flc / (tc["chunk_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "chunk_ms": round(tc["chunk_ms"], 4), "rope_ms": round(tc["rope_ms"], 4),
+                "unsplit_chunk_ms": round(tu["chunk_ms"], 4),
+                "unsplit_tflops_kernel": round(flc / (tu["chunk_ms"] * 1e-3) / 1e12, 2)}
+        tb = time_backward(st, extra_steps, max(args.warmup // 2, 2), args.settle)
         flb = 10.0 * w.D * w.Hq * w.B * allowed_pairs(cu)
         out["backward_8b"] = {
             "workload": "llama-3.1-8b attention layer backward: gqa_attention_backward (delta, "
@@ -516,24 +687,25 @@ def main():
             "tflops": round(flb / (tb["backward_ms"] * 1e-3) / 1e12, 2),
             "frac": round(flb / (tb["backward_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "backward_ms": round(tb["backward_ms"], 4)}
-        if not args.no_cpu_baseline:
-            log("timing the fp64 oracle on a row sample ...")
-            out["cpu_baseline"] = cpu_baseline(host, w, cu)
-        del st
+        if only == "backward":
+            out.update(value=out["backward_8b"]["tflops"], unit="TFLOP/s",
+                       ms_per_step=out["backward_8b"]["backward_ms"],
+                       config={"workload": out["backward_8b"]["workload"]})
+        elif cpu:
+            log("timing the fp64 oracle on a row sample of the 8B prefill ...")
+            cpu_cfg["llama8b"] = cpu_prefill_rate(host, w, cu, 8.0)
+        del st, host
 
-    if run_405:
-        st3, _ = setup_prefill("llama405b")
-        t3 = time_prefill(st3, max(3, args.steps // 2), args.warmup, args.settle)
-        fl3 = prefill_flops(st3["w"], st3["cu"])
-        out["prefill_405b"] = {
-            "workload": "llama-3.1-405b attention layer prefill S=32768, 128 q / 8 kv heads",
-            "documents": int(st3["cu"].size - 1),
-            "tflops_path": round(fl3 / (t3["gpu_ms_per_step"] * 1e-3) / 1e12, 2),
-            "tflops_kernel": round(fl3 / (t3["prefill_ms"] * 1e-3) / 1e12, 2),
-            "frac_kernel": round(fl3 / (t3["prefill_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "ms_per_step": round(t3["gpu_ms_per_step"], 4), "prefill_ms": round(t3["prefill_ms"], 4),
-            "rope_ms": round(t3["rope_ms"], 4), "traffic": measured_traffic("gqa_prefill", "llama405b", phash)}
+    # ---- 405B at S=32768: prefill, context-parallel ring ----------------------------
+    if run("prefill", "llama405b"):
+        st3, host3 = setup_prefill("llama405b")
+        t3 = time_prefill(st3, extra_steps, args.warmup, args.settle)
+        out["prefill_405b"] = prefill_record(
+            st3, t3, "llama-3.1-405b attention layer prefill S=32768, 128 q / 8 kv heads: rope_qk (keys) + "
+                     "gqa_prefill_rope")
+        out["prefill_405b"]["traffic"] = measured_traffic("gqa_prefill", "llama405b", phash)
         P = 8
+        fl3 = prefill_flops(st3["w"], st3["cu"])
         tr = time_ring(st3, P, 2)
         out["ring_405b"] = {
             "workload": f"405b-shape context-parallel attention, S=32768 in {P} shards of {32768 // P}: "
@@ -541,24 +713,24 @@ def main():
             "tflops": round(fl3 / (tr * 1e-3) / 1e12, 2),
             "frac": round(fl3 / (tr * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "ms_per_ring": round(tr, 3)}
-        if not run_8b:
-            out.update(value=out["prefill_405b"]["tflops_path"], unit="TFLOP/s",
-                       ms_per_step=out["prefill_405b"]["ms_per_step"],
-                       config={"workload": out["prefill_405b"]["workload"]})
-        del st3
-        if args.with_128k:
-            st5, _ = setup_prefill("long128k")
-            t5 = time_prefill(st5, 3, 1)
-            fl5 = prefill_flops(st5["w"], st5["cu"])
-            out["prefill_128k"] = {
-                "workload": "405b-shape long-context prefill S=131072, 4 documents",
-                "tflops_kernel": round(fl5 / (t5["prefill_ms"] * 1e-3) / 1e12, 2),
-                "frac_kernel": round(fl5 / (t5["prefill_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "prefill_ms": round(t5["prefill_ms"], 3), "rope_ms": round(t5["rope_ms"], 3)}
-            del st5
+        if cpu:
+            log("timing the fp64 oracle on a row sample of the 405B prefill ...")
+            cpu_cfg["llama405b"] = cpu_prefill_rate(host3, st3["w"], st3["cu"], 8.0)
+        del st3, host3
         torch.cuda.empty_cache()
 
-    if run_dec:
+    # ---- tiny: absolute time (launch-bound) ---------------------------------------
+    if run("prefill", "tiny"):
+        st1, host1 = setup_prefill("tiny")
+        t1 = time_prefill(st1, args.steps, args.warmup, 0.0)
+        out["tiny"] = prefill_record(st1, t1, "tiny prefill S=128, 8 q / 2 kv heads, head_dim 64, fp32 "
+                                              "(launch-bound: absolute time only)")
+        if cpu:
+            cpu_cfg["tiny"] = cpu_tiny_rate(host1, st1["w"], st1["cu"])
+        del st1, host1
+
+    # ---- 405B-shape decode ---------------------------------------------------------
+    if run("decode", "decode405b"):
         sd = setup_decode()
         td = time_decode(sd, args.steps, args.warmup, args.settle)
         nbytes = decode_bytes(sd)
@@ -567,13 +739,22 @@ def main():
         out["decode_405b"] = {
             "workload": "405b-shape decode: 16 sequences x 1 token, 128 q / 8 kv heads, "
                         "cache lengths U[4096,131072]", "kv_chunk": KV_CHUNK,
+            "seq_lens": sd["lens"].tolist(),
             "kv_bytes": nbytes, "gbs_path": round(nbytes / (td["ms_per_step"] * 1e-3) / 1e9, 1),
             "ms_per_step": round(td["ms_per_step"], 4),
             "roofline": {"kernel": "gqa_decode", "bound": "hbm", "achieved": round(gbs, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic("gqa_decode", "decode405b", dhash),
                          "launch_ms": round(td["decode_ms"], 4)},
-            "combine_ms": round(td["combine_ms"], 4)}
+            "combine_ms": round(td["combine_ms"], 4), "gpu_clock": td["gpu_clock"]}
+        tn = time_noalloc(sd, args.steps, args.warmup, args.settle)
+        out["decode_405b_noalloc"] = {
+            "workload": "the same decode through gqa_decode_noalloc (partials in the library's device "
+                        "scratch, decode + combine in one call)",
+            "gbs_path": round(nbytes / (tn * 1e-3) / 1e9, 1), "ms_per_step": round(tn, 4)}
+        if cpu:
+            log("timing the fp64 decode oracle on a sample of the caches ...")
+            cpu_cfg["decode405b"] = cpu_decode_rate(sd, 8.0)
         page_decode_cache(sd)
         tp = time_decode(sd, args.steps, args.warmup, args.settle, paged=True)
         gbp = nbytes / (tp["decode_ms"] * 1e-3) / 1e9
@@ -582,11 +763,22 @@ def main():
                         "in random order, one block table per sequence (gqa_decode_paged)",
             "gbs": round(gbp, 1), "frac": round(gbp / PEAK_HBM_GBS, 4),
             "decode_ms": round(tp["decode_ms"], 4), "ms_per_step": round(tp["ms_per_step"], 4)}
-        if not (run_8b or run_405):
+        if only in ("decode", "decode405b"):
             out.update(value=round(gbs, 1), unit="GB/s", ms_per_step=round(td["ms_per_step"], 4),
                        config={"workload": out["decode_405b"]["workload"]},
                        roofline=out["decode_405b"]["roofline"])
+        del sd
+        torch.cuda.empty_cache()
 
+    # secondary workloads given the headline's slot when run alone
+    if "value" not in out:
+        for key in ("prefill_8b", "prefill_405b", "tiny"):
+            if key in out:
+                out.update(value=out[key]["tflops_path"], unit="TFLOP/s", ms_per_step=out[key]["ms_per_step"],
+                           config={"workload": out[key]["workload"]})
+                break
+    if cpu_cfg:
+        out["cpu_baseline_configs"] = cpu_cfg
     print(json.dumps(out), flush=True)
 
 

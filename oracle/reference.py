@@ -280,9 +280,21 @@ def attention_backward_rows(qr, kr, v, dO, rows, keys, cu_docs=None, scale: Opti
     ``attention_backward``, summed over rows (and the g heads of a KV head)
     for dk, dv and over keys for dq:
       dv_j = sum P_ij dO_i,  dk_j = scale sum dS_ij qr_i,  dq_i = scale sum_j dS_ij kr_j.
-    Returns dq [R,Hq,D], dk [K,Hkv,D], dv [K,Hkv,D] in the order asked. With
-    ``magnitudes``, also (l1, l2): for each of the three, per element, the sum
-    of the absolute values and the root of the sum of squares of its terms.
+    Returns dq [R,Hq,D], dk [K,Hkv,D], dv [K,Hkv,D] in the order asked.
+
+    With ``magnitudes``, also (l1, l2), per element of each of the three: the
+    scale of what rounding can do to it. l1 is the sum of the absolute values
+    of its terms and l2 the root of the sum of their squares, where a dS term
+    also carries its row term: D_i = sum_j P_ij dP_ij equals dO_i . O_i, and
+    formed from a rounded O it is off by at most a small multiple of
+    A_i = sum_d |dO_id| sum_j P_ij |v_jd| (typically of R_i, the root of the
+    sum over d of (dO_id sum_j P_ij |v_jd|)^2). So for dq (and likewise dk,
+    summed over rows and heads)
+      l1 = scale sum_j P_ij (|dP_ij - D_i| + A_i) |kr_jd|,
+      l2 = scale sqrt(sum_j dS_ij^2 kr_jd^2) + scale R_i |sum_j P_ij kr_jd|
+    (for dk, l2 = scale sqrt(sum_i (dS_ij^2 + P_ij^2 R_i^2) qr_id^2), the
+    rows' D errors being independent), and for dv, l1 = sum_i P_ij |dO_id|,
+    l2 = sqrt(sum_i P_ij^2 dO_id^2).
     """
     S, Hq, D = qr.shape
     Hkv = kr.shape[1]
@@ -332,26 +344,38 @@ def attention_backward_rows(qr, kr, v, dO, rows, keys, cu_docs=None, scale: Opti
                 e = np.exp(s - s.max(axis=2, keepdims=True))
                 P = e / e.sum(axis=2, keepdims=True)
                 dP = (gh @ vw[:W, kv, :].T).reshape(n, g, W)
-                dS = P * (dP - (P * dP).sum(axis=2, keepdims=True))
+                Dr = (P * dP).sum(axis=2, keepdims=True)
+                dS = P * (dP - Dr)
+                if magnitudes:
+                    pva = (P.reshape(n * g, W) @ np.abs(vw[:W, kv, :]))          # sum_j P_ij |v_jd|
+                    A = (np.abs(gh) * pva).sum(axis=1).reshape(n, g, 1)
+                    R = np.sqrt(((gh * pva) ** 2).sum(axis=1)).reshape(n, g, 1)
+                    M = P * (np.abs(dP - Dr) + A)
                 if am.size:
                     t = scale * dS[am].reshape(am.size * g, W)
                     kk = kw[:W, kv, :]
                     dq[ao, heads, :] = (t @ kk).reshape(am.size, g, D)
                     if magnitudes:
-                        l1[0][ao, heads, :] = (np.abs(t) @ np.abs(kk)).reshape(am.size, g, D)
-                        sq[0][ao, heads, :] = ((t * t) @ (kk * kk)).reshape(am.size, g, D)
+                        Pa = P[am].reshape(am.size * g, W)
+                        l1[0][ao, heads, :] = (scale * M[am].reshape(am.size * g, W)
+                                               @ np.abs(kk)).reshape(am.size, g, D)
+                        sq[0][ao, heads, :] = (np.sqrt((t * t) @ (kk * kk)) + scale * R[am].reshape(-1, 1)
+                                               * np.abs(Pa @ kk)).reshape(am.size, g, D)
                 if cols.size:
                     Pc = P[:, :, cols].reshape(n * g, cols.size).T          # [C, n*g]
                     Sc = scale * dS[:, :, cols].reshape(n * g, cols.size).T
                     np.add.at(dv, (slots, kv), Pc @ gh)
                     np.add.at(dk, (slots, kv), Sc @ qh)
                     if magnitudes:
-                        np.add.at(l1[2], (slots, kv), np.abs(Pc) @ np.abs(gh))
-                        np.add.at(l1[1], (slots, kv), np.abs(Sc) @ np.abs(qh))
+                        Mc = scale * M[:, :, cols].reshape(n * g, cols.size).T
+                        PRc = scale * (P * R)[:, :, cols].reshape(n * g, cols.size).T
+                        np.add.at(l1[2], (slots, kv), Pc @ np.abs(gh))
+                        np.add.at(l1[1], (slots, kv), Mc @ np.abs(qh))
                         np.add.at(sq[2], (slots, kv), (Pc * Pc) @ (gh * gh))
-                        np.add.at(sq[1], (slots, kv), (Sc * Sc) @ (qh * qh))
+                        np.add.at(sq[1], (slots, kv), (Sc * Sc + PRc * PRc) @ (qh * qh))
     if magnitudes:
-        return dq, dk, dv, (l1, [np.sqrt(x) for x in sq])
+        # dq's l2 is formed whole per element above; dk's and dv's from sums of squares
+        return dq, dk, dv, (l1, [sq[0], np.sqrt(sq[1]), np.sqrt(sq[2])])
     return dq, dk, dv
 
 

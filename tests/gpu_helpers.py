@@ -88,14 +88,18 @@ def oracle_rows_threaded(q, k, v, rows, cu, base, n_threads=16, chunk=64):
 # for dk, scale dS_ij k_j for dq) is formed from bf16 inputs and goes through
 # at most two bf16 roundings (P or dS rounded for the matrix product, dS
 # carrying P's error), each at most 2^-9 relative; the sums run in fp32 and the
-# result is rounded once more to bf16 (at most 2^-9 |ref|). Worst case, per
-# element: |err| <= 2^-8 l1 + 2^-9 |ref| with l1 the sum of the terms' absolute
-# values; the bar allows 2^-7 l1 + 2^-8 |ref| (twice that) plus 1e-6 for fp32
-# rounding of sums that cancel to nearly zero. On average the roundings are
-# independent and uniform, so an element's error has standard deviation at
-# most 2^-9 sqrt(2/3) l2 (l2 the root of the sum of the squared terms) and
-# mean absolute value at most sqrt(2/pi) times that, 0.66 2^-9 l2, plus 2^-10
-# |ref| on average for the final rounding: the mean bar is 2^-8 mean(l2 + |ref|).
+# result is rounded once more to bf16 (at most 2^-9 |ref|). The row term of
+# dS_ij = P_ij (dP_ij - D_i), D_i = dO_i . O_i, is formed from the forward's
+# output, itself rounded: its error is at most about 2^-8 of A_i, the absolute
+# sum behind it, and the oracle's magnitudes count it (l1 with A_i, l2 with
+# its typical size R_i). Worst case, per element: |err| <= 2^-8 l1 + 2^-9 |ref|;
+# the bar allows 2^-7 l1 + 2^-8 |ref| (twice that) plus 1e-6 for fp32 rounding
+# of sums that cancel to nearly zero. On average the roundings are
+# independent and uniform, so the terms' share of an element's error has
+# standard deviation at most 2^-9 sqrt(2/3) of their root-sum-square, mean
+# absolute value at most sqrt(2/pi) times that (0.66 2^-9), the row term's
+# share is about 2^-9 of its l2 part, and the final rounding adds 2^-10 |ref|
+# on average: the mean bar is 2^-8 mean(l2 + |ref|).
 GRAD_MAX_L1 = 2.0 ** -7
 GRAD_MAX_REF = 2.0 ** -8
 GRAD_MAX_FLOOR = 1e-6

@@ -219,12 +219,14 @@ def test_restricted_backward_matches_autograd_of_sdpa():
 
 
 def test_restricted_backward_magnitudes():
-    """The per-element term magnitudes: with zero queries every visible weight
+    """The per-element magnitudes: with zero queries every visible weight
     of row i is 1 / (i - start + 1), so dv_j's terms are dO_i / (i - start + 1)
     over the rows i >= j of j's document (closed forms for the sum of absolute
     values and the root of the sum of squares), and dk's terms are all zero;
-    a document of one token has P = 1 and dS = 0 (dq and its magnitudes
-    vanish). For random inputs, |gradient| <= l1 and l2 <= l1 <= sqrt(terms) l2."""
+    a document of one token has P = 1 and dS = 0, so dq vanishes and only its
+    row term's share is left: l1 = scale (sum_d |dO_d| |v_d|) |k| and
+    l2 = scale sqrt(sum_d dO_d^2 v_d^2) |k|. For random inputs,
+    |gradient| <= l1, l2 <= l1, and for dk and dv l1 <= sqrt(terms * D) l2."""
     rng = np.random.default_rng(15)
     S, Hq, Hkv, D = 20, 4, 2, 8
     g = Hq // Hkv
@@ -244,14 +246,21 @@ def test_restricted_backward_magnitudes():
         np.testing.assert_allclose(l1[2][j], np.abs(t).sum(axis=0), rtol=1e-13, atol=1e-13)
         np.testing.assert_allclose(l2[2][j], np.sqrt((t * t).sum(axis=0)), rtol=1e-13, atol=1e-13)
     assert np.all(dk == 0) and np.all(l1[1] == 0) and np.all(l2[1] == 0)
-    assert np.all(dq[0] == 0) and np.all(l1[0][0] == 0)
+    assert np.all(dq[0] == 0)
+    sc = 1.0 / np.sqrt(D)
+    for h in range(Hq):
+        kv = h // g
+        A = np.sum(np.abs(dO[0, h]) * np.abs(v[0, kv]))
+        R = np.sqrt(np.sum((dO[0, h] * v[0, kv]) ** 2))
+        np.testing.assert_allclose(l1[0][0, h], sc * A * np.abs(kr[0, kv]), rtol=1e-13, atol=0)
+        np.testing.assert_allclose(l2[0][0, h], sc * R * np.abs(kr[0, kv]), rtol=1e-13, atol=0)
     qr = rng.standard_normal((S, Hq, D))
     dq, dk, dv, (l1, l2) = orc.attention_backward_rows(qr, kr, v, dO, rows, keys, cu, magnitudes=True)
-    n_terms = [S * np.ones(1), S * g * np.ones(1), S * g * np.ones(1)]
-    for x, a1, a2, n in zip((dq, dk, dv), l1, l2, n_terms):
+    for x, a1, a2 in zip((dq, dk, dv), l1, l2):
         assert np.all(np.abs(x) <= a1 * (1 + 1e-12) + 1e-15)
         assert np.all(a2 <= a1 * (1 + 1e-12) + 1e-15)
-        assert np.all(a1 <= np.sqrt(n) * a2 * (1 + 1e-12) + 1e-15)
+    for a1, a2 in zip(l1[1:], l2[1:]):          # dk, dv: at most S g terms of D-fold row terms
+        assert np.all(a1 <= np.sqrt(S * g * D) * a2 * (1 + 1e-12) + 1e-15)
 
 
 # ---------------------------------------------------------------- invariants
