@@ -321,19 +321,11 @@ void prefill_kernel(PrefillArgs a) {
   // lds + (4 + j % 4) TILE). Barrier B(k) ends iteration k. Between B(k-1) and
   // B(k) every wave runs, for its 32 columns:
   //   PV(k-1): 4 DB MFMAs O^T += V^T P^T of tile k-1, with the scale FMA
-  //            t = s * scale * log2(e) - Mref of tile k and the exponentials,
-  //            bf16 rounding and row sums of its first 16 scores per lane
-  //            interleaved;
-  //   the causal/document mask of tile k (edge tiles only; the first half's
-  //            weights are then formed again);
+  //            t = s * scale * log2(e) - Mref of tile k interleaved;
+  //   the causal/document mask of tile k (edge tiles only);
   //   QK(k+1): 2 KS MFMAs S^T = K Q^T of tile k+1, with the exponentials,
-  //            bf16 rounding and row sums of the other 16 scores of tile k
-  //            interleaved;
+  //            bf16 rounding and row sums of tile k interleaved;
   //   the lazy reference check of tile k.
-  // The exponentials (quarter-rate) are split between the two products so
-  // that neither phase has more VALU time per MFMA than the MFMA itself; the
-  // weights of consecutive tiles go to alternate register buffers, since
-  // tile k's are formed while PV(k-1) still reads tile k-1's.
   // Operand reads run PF MFMAs ahead of their use, across the phase boundary
   // and across the barrier. Each piece of work is emitted in program order and
   // fenced (sched_barrier), so every wave keeps its own matrix core and VALU
@@ -346,12 +338,9 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int NQ = 2 * KS;      // QK MFMAs per tile
   constexpr int NP = 4 * DB;      // PV MFMAs per tile
   constexpr int PF = 3;           // operand reads ahead
+  constexpr int EQ = 32 / NQ;     // scores per lane exponentiated per QK MFMA
   constexpr int EP = 32 / NP;     // scores per lane scaled per PV MFMA
-  constexpr int XP = 16;          // scores per lane exponentiated during PV (the rest during QK)
-  constexpr int XPM = XP / NP;    // ... per PV MFMA
-  constexpr int XQM = (32 - XP) / NQ;   // ... per QK MFMA
-  static_assert(PF <= NQ && PF <= NP && XPM * NP == XP && XQM * NQ == 32 - XP && XPM <= EP,
-                "pipeline shape");
+  static_assert(PF <= NQ && PF <= NP && EQ % 2 == 0, "pipeline shape");
   char* const kst[4] = {lds, lds + TILE, lds + 2 * TILE, lds + 3 * TILE};
   char* const vst[4] = {lds + 4 * TILE, lds + 5 * TILE, lds + 6 * TILE, lds + 7 * TILE};
 
@@ -360,8 +349,7 @@ void prefill_kernel(PrefillArgs a) {
   // kb), so each frees as soon as it is used; S^T of the next tile is the pair
   // of MFMA accumulators sn
   float sc[32];
-  // weights e, e+1 as a bf16 pair in pw[e / 2], two buffers (tile parity)
-  uint32_t pwA[16], pwB[16];
+  uint32_t pw[16];                // weights e, e+1 as a bf16 pair in pw[e / 2]
   f32x16 sn[2];
   bf16x8 kbuf[NQ], vbuf[NP];      // operands read ahead
   float rs = 0.f;                 // this lane's sum of the tile's rounded weights
@@ -384,38 +372,25 @@ void prefill_kernel(PrefillArgs a) {
                                    0, 1, 2, 3, 4, 5, 6, 7);
   };
   const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-  float ex[32];                   // exponentials waiting for their pair
-  // weight of score e (its pair e ^ 1 packed and summed with it when e is
-  // odd); pinned: the pair and the sum are held where they are formed (in the
-  // PV phase the mask branch follows, and the compiler would otherwise sink
-  // the exponentials past it, out of the MFMA stream)
-  auto exp_one = [&](uint32_t (&pw)[16], int e, bool pin) __attribute__((always_inline)) {
-    ex[e] = fast_exp2(sc[e]);
-    if (e & 1) {
-      bf16x2 pr;
-      pr[0] = to_bf16(ex[e - 1]);
-      pr[1] = to_bf16(ex[e]);
-      pw[e >> 1] = __builtin_bit_cast(uint32_t, pr);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rs, false);
-      if (pin) asm volatile("" : "+v"(pw[e >> 1]), "+v"(rs));
-    }
-  };
   // weights of scores e, e+1 into P^T and the row sum
-  auto exp_pair = [&](uint32_t (&pw)[16], int e) __attribute__((always_inline)) {
-    exp_one(pw, e, false);
-    exp_one(pw, e + 1, false);
+  auto exp_pair = [&](int e) __attribute__((always_inline)) {
+    bf16x2 pr;
+    pr[0] = to_bf16(fast_exp2(sc[e]));
+    pr[1] = to_bf16(fast_exp2(sc[e + 1]));
+    pw[e >> 1] = __builtin_bit_cast(uint32_t, pr);
+    rs = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rs, false);
   };
   // P^T operand of 16-key step ks (key block ks / 2, half ks % 2): weights
   // 8 ks .. 8 ks + 7
-  auto p_op = [&](const uint32_t (&pw)[16], int ks) __attribute__((always_inline)) {
+  auto p_op = [&](int ks) __attribute__((always_inline)) {
     const u32x4 w = {pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]};
     return __builtin_bit_cast(bf16x8, w);
   };
-  // QK of the next tile (K stage lk) with the weights of the current one's
-  // scores XP .. 31 (into pw); the reads past the QK operands fetch the first
-  // PF V operands of the current tile (V stage lv)
-  auto phase_qk = [&](const char* __restrict__ lk, const char* __restrict__ lv, uint32_t (&pw)[16])
-      __attribute__((always_inline)) {
+  // QK of the next tile (K stage lk) with the weights of the current one; the
+  // reads past the QK operands fetch the first PF V operands of the current
+  // tile (V stage lv)
+  auto phase_qk = [&](const char* __restrict__ lk, const char* __restrict__ lv) __attribute__((always_inline)) {
+    rs = 0.f;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
@@ -425,7 +400,7 @@ void prefill_kernel(PrefillArgs a) {
       if (j < NQ) kbuf[j] = rd_k(lk, j);
       else vbuf[j - NQ] = rd_v(lv, j - NQ);
 #pragma unroll
-      for (int e = XP + XQM * i; e < XP + XQM * (i + 1); ++e) exp_one(pw, e, false);
+      for (int e = EQ * i; e < EQ * (i + 1); e += 2) exp_pair(e);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -437,22 +412,17 @@ void prefill_kernel(PrefillArgs a) {
     const int kt = kv_lo + k * kKT;
     return (!wave_all_valid) | (kt + kKT - 1 > w_tmin + qo) | (kt < w_smax) | (kt + kKT > kend);
   };
-  // PV of the previous tile (V stage lv, its weights in pv) with the scale
-  // FMA of tile k's scores and the weights of its scores 0 .. XP-1 (into pw;
-  // MFMA i scales scores EP i .. EP i + EP-1 and exponentiates XPM i ..
-  // XPM i + XPM-1, already scaled since XPM <= EP);
-  // the reads past the PV operands fetch the first PF K operands of tile k+1
-  // (K stage lk2). Each FMA result is pinned where it is formed (an empty asm
-  // that takes it in a register), or the compiler would move all 32 FMAs out
-  // of the MFMA stream to where the scores are first used.
-  auto phase_pv = [&](const char* __restrict__ lv, const char* __restrict__ lk2, const uint32_t (&pv)[16],
-                      uint32_t (&pw)[16]) __attribute__((always_inline)) {
-    rs = 0.f;
+  // PV of the previous tile (V stage lv) with the scale FMA of tile k's
+  // scores; the reads past the PV operands fetch the first PF K operands of
+  // tile k+1 (K stage lk2). Each FMA result is pinned where it is formed (an
+  // empty asm that takes it in a register), or the compiler would move all 32
+  // FMAs out of the MFMA stream to where the scores are first used.
+  auto phase_pv = [&](const char* __restrict__ lv, const char* __restrict__ lk2) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int ks = i / DB, db = i % DB;
-      acc[db] = mfma32(vbuf[i], p_op(pv, ks), acc[db]);
+      acc[db] = mfma32(vbuf[i], p_op(ks), acc[db]);
       const int j = i + PF;
       if (j < NP) vbuf[j] = rd_v(lv, j);
       else kbuf[j - NP] = rd_k(lk2, j - NP);
@@ -461,8 +431,6 @@ void prefill_kernel(PrefillArgs a) {
         sc[e] = fmaf(sn[e >> 4][e & 15], a.scale_log2, negM);
         asm volatile("" : "+v"(sc[e]));
       }
-#pragma unroll
-      for (int e = XPM * i; e < XPM * (i + 1); ++e) exp_one(pw, e, true);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -471,8 +439,7 @@ void prefill_kernel(PrefillArgs a) {
   // 32 kb + 8 (j / 4) + 4 hi + j % 4, visible when in [st, min(tok + qo,
   // kend - 1)]; keys at or past kend (a ring step's key shard can end before
   // the rows' positions) are masked too
-  // (the weights of scores 0 .. nx-1, already formed, are formed again)
-  auto mask_tile = [&](int k, uint32_t (&pw)[16], int nx) __attribute__((always_inline)) {
+  auto mask_tile = [&](int k) __attribute__((always_inline)) {
     const int kt = kv_lo + k * kKT;
     const int lo4 = (valid[0] ? st[0] - kt : kKT) - 4 * hi;
     const int hi4 = (valid[0] ? min(tok[0] + qo, kend - 1) - kt : -1) - 4 * hi;
@@ -481,19 +448,15 @@ void prefill_kernel(PrefillArgs a) {
       const int r = 32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3);
       sc[e] = (r >= lo4 && r <= hi4) ? sc[e] : -INFINITY;
     }
-    rs = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; e += 2)
-      if (e < nx) exp_pair(pw, e);
   };
   // the last PV (tile n_tiles - 1, V stage lv): its first PF operands were
   // read by the last QK phase
-  auto phase_pv_last = [&](const char* lv, const uint32_t (&pv)[16]) __attribute__((always_inline)) {
+  auto phase_pv_last = [&](const char* lv) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int ks = i / DB, db = i % DB;
       if (i + PF < NP) vbuf[i + PF] = rd_v(lv, i + PF);
-      acc[db] = mfma32(vbuf[i], p_op(pv, ks), acc[db]);
+      acc[db] = mfma32(vbuf[i], p_op(ks), acc[db]);
     }
   };
   // After the weights of a tile: the reference must move only if a weight may
@@ -502,7 +465,7 @@ void prefill_kernel(PrefillArgs a) {
   // log2 units), the accumulator and row sum are scaled by 2^-d and the
   // weights are formed again; a column still without a visible key keeps
   // Mref = -inf. Softmax does not depend on the reference, so this is exact.
-  auto settle = [&](uint32_t (&pw)[16]) __attribute__((always_inline)) {
+  auto settle = [&]() __attribute__((always_inline)) {
     if (__any(Mref == -INFINITY || !(rs <= kLazyW))) {
       float mx = sc[0];
 #pragma unroll
@@ -520,7 +483,7 @@ void prefill_kernel(PrefillArgs a) {
       for (int e = 0; e < 32; ++e) sc[e] -= d;
       rs = 0.f;
 #pragma unroll
-      for (int e = 0; e < 32; e += 2) exp_pair(pw, e);
+      for (int e = 0; e < 32; e += 2) exp_pair(e);
     }
     l += rs;
   };
@@ -539,16 +502,16 @@ void prefill_kernel(PrefillArgs a) {
   // take the direct-to-LDS loads it issues as writers of what its reads fetch;
   // the waits and barriers order the stages.
   auto iter = [&](char* __restrict__ kdst, char* __restrict__ vdst, const char* __restrict__ vprev,
-                  const char* __restrict__ knext, const char* __restrict__ vcur, int k,
-                  const uint32_t (&pv)[16], uint32_t (&pw)[16]) __attribute__((always_inline)) {
+                  const char* __restrict__ knext, const char* __restrict__ vcur, int k)
+      __attribute__((always_inline)) {
     const bool masked = needs_mask(k);
-    phase_pv(vprev - 4 * TILE, knext, pv, pw);
-    if (masked) mask_tile(k, pw, XP);
+    phase_pv(vprev - 4 * TILE, knext);
+    if (masked) mask_tile(k);
     // (issued here rather than before the PV: the register allocator then
     // keeps every operand in registers; issued earlier they measured no faster)
     stage_kv(tile_kt(k + 3), kdst, false);
     stage_kv(tile_kt(k + 2), vdst, true);
-    phase_qk(knext, vcur - 4 * TILE, pw);
+    phase_qk(knext, vcur - 4 * TILE);
   };
   // Iteration 0: the loads of K3 and V2, QK of tile 0 (its operands read
   // here), the scale FMA and mask of tile 0, the first K1 operands, then QK(1)
@@ -562,20 +525,13 @@ void prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < NQ; ++i) kbuf[i] = rd_k(k0, i);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) sn[i / KS] = mfma32(kbuf[i], qreg[0][i % KS], i % KS == 0 ? f32x16{} : sn[i / KS]);
-    // (no PV precedes tile 0: its scale FMA, mask and first weights run on
-    // their own)
+    // (no PV precedes tile 0: its scale FMA and mask run on their own)
 #pragma unroll
     for (int e = 0; e < 32; ++e) sc[e] = fmaf(sn[e >> 4][e & 15], a.scale_log2, negM);
-    if (masked) {
-      mask_tile(0, pwA, XP);
-    } else {
-      rs = 0.f;
-#pragma unroll
-      for (int e = 0; e < XP; e += 2) exp_pair(pwA, e);
-    }
+    if (masked) mask_tile(0);
 #pragma unroll
     for (int i = 0; i < PF; ++i) kbuf[i] = rd_k(k1, i);
-    phase_qk(k1, v0 - 4 * TILE, pwA);
+    phase_qk(k1, v0 - 4 * TILE);
   };
 
   // ---- prologue loads: K0, K1, V0, K2, V1 (K and V stage 3 hold the RoPE table) --
@@ -694,7 +650,7 @@ void prefill_kernel(PrefillArgs a) {
   }
   sync_tiles();   // K0, K1, V0 landed; every wave is done with the RoPE table
   iter0(kst[3], vst[2], kst[0], kst[1], vst[0]);
-  settle(pwA);
+  settle();
   sync_tiles();   // B(0)
   // Unrolled over the four stage indices so every stage offset is a constant.
   // The loop has one exit: steps at or past the last tile are skipped by a
@@ -703,11 +659,8 @@ void prefill_kernel(PrefillArgs a) {
   auto step = [&](auto U, int k) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value;   // k % 4
     if (k < n_tiles) {
-      // tile k's weights go to buffer k % 2 (tile 0's to pwA)
-      uint32_t(&pw)[16] = (u & 1) ? pwB : pwA;
-      const uint32_t(&pv)[16] = (u & 1) ? pwA : pwB;
-      iter(kst[(u + 3) & 3], vst[(u + 2) & 3], vst[(u + 3) & 3], kst[(u + 1) & 3], vst[u], k, pv, pw);
-      settle(pw);
+      iter(kst[(u + 3) & 3], vst[(u + 2) & 3], vst[(u + 3) & 3], kst[(u + 1) & 3], vst[u], k);
+      settle();
       sync_tiles();   // B(k)
     }
   };
@@ -719,10 +672,10 @@ void prefill_kernel(PrefillArgs a) {
   }
   // PV of the last tile, from V stage (n_tiles - 1) % 4
   switch ((n_tiles - 1) & 3) {
-    case 0: phase_pv_last(vst[0] - 4 * TILE, pwA); break;
-    case 1: phase_pv_last(vst[1] - 4 * TILE, pwB); break;
-    case 2: phase_pv_last(vst[2] - 4 * TILE, pwA); break;
-    default: phase_pv_last(vst[3] - 4 * TILE, pwB); break;
+    case 0: phase_pv_last(vst[0] - 4 * TILE); break;
+    case 1: phase_pv_last(vst[1] - 4 * TILE); break;
+    case 2: phase_pv_last(vst[2] - 4 * TILE); break;
+    default: phase_pv_last(vst[3] - 4 * TILE); break;
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));          // loads past the last tile
 
