@@ -26,17 +26,22 @@
 //   moves with the tile and its size ends at the sequence end, so rows past
 //   the end read as zero. K operands are read with ds_read_b128; the V^T
 //   operand with the transposing ds_read_b64_tr_b16 from the row-major V tile.
+// * The query operand carries scale * log2(e) (multiplied in fp32 before its
+//   one rounding to bf16, after the rotation when the kernel rotates), and
+//   the score MFMA starts its accumulation from -Mref instead of 0, so it
+//   yields the exponent t = s * scale * log2(e) - Mref directly: no VALU
+//   operation per score before the exponential (the VALU time of a tile adds
+//   to its MFMA time on this part, so each operation removed counts).
 // * Software pipeline, one workgroup barrier per tile: between two barriers
-//   every wave runs the PV product of the previous tile with the score FMA of
-//   the current one interleaved, then the QK product of the next tile with the
-//   exponentials, bf16 rounding and row sums of the current one interleaved.
-//   Each piece (one MFMA, its operand read a few MFMAs ahead, two VALU or
-//   transcendental operations) is emitted in program order and fenced, so a
-//   wave keeps its matrix core and its VALU busy at the same time (on gfx950
-//   a wave's own independent VALU work issues while its MFMA runs); the two
-//   waves of a SIMD fill each other's waits. The loop is unrolled over the
-//   four stage indices, so every LDS operand address is a per-lane register
-//   plus a constant offset.
+//   every wave runs the PV product of the previous tile, then the QK product
+//   of the next tile with the exponentials, bf16 rounding and row sums of the
+//   current one interleaved. Each piece (one MFMA, its operand read a few
+//   MFMAs ahead, two transcendental and two VALU operations) is emitted in
+//   program order and fenced, so a wave keeps its matrix core and its VALU
+//   busy at the same time; the two waves of a SIMD fill each other's waits.
+//   The exponents of consecutive tiles alternate between two register
+//   buffers. The loop is unrolled over the four stage indices, so every LDS
+//   operand address is a per-lane register plus a constant offset.
 // * Online softmax in the base-2 domain with fp32 statistics; probabilities
 //   are rounded to bf16 once and the row sums accumulate those rounded values
 //   (v_dot2_f32_bf16), so numerator and denominator use the same weights. The
@@ -161,18 +166,23 @@ void prefill_kernel(PrefillArgs a) {
   // Columns past the sequence end load the last token's row (no branch, so
   // the wait for the offsets row does not also wait for Q); every key is
   // masked for them and their outputs are not stored.
+  // The operand holds q * scale * log2(e), rounded once to bf16 (after the
+  // rotation when the kernel rotates), so the score MFMA yields the exponent
+  // in log2 units directly.
   bf16x8 qreg[kCB][KS];
-  float qraw[kCB][KS][8];   // unrotated queries (RoPE in the kernel), else unused
+  float qraw[kCB][KS][8];   // the loaded queries in fp32
   const bool rope_q = a.rope_q != 0;
+  const float qscale = a.scale_log2;
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
     const T* qp = qbase + min(tok[cb], Sq - 1) * a.qs_s + head[cb] * a.qs_h + 8 * hi;
-    if (rope_q) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) load8_f32(qp + 16 * ks, qraw[cb][ks]);
-    } else {
+    for (int ks = 0; ks < KS; ++ks) load8_f32(qp + 16 * ks, qraw[cb][ks]);
+    if (!rope_q) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qreg[cb][ks] = load8(qp + 16 * ks);
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qreg[cb][ks][i] = to_bf16(qraw[cb][ks][i] * qscale);
     }
   }
 
@@ -248,13 +258,17 @@ void prefill_kernel(PrefillArgs a) {
   // ---- online-softmax state of this lane's column ------------------------------
   // Mref: the reference the exponents are taken against, in log2 units
   // (scale * log2(e) * score); -inf until the column has seen a visible key.
-  // negM: what the score FMA adds (-Mref, or 0 while Mref is -inf).
+  // negM: what the score MFMA starts its accumulation from (-Mref, or 0 while
+  // Mref is -inf), splat in negMv.
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[db][j] = 0.f;
   float Mref = -INFINITY, negM = 0.f, l = 0.f;
+  f32x16 negMv;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) negMv[j] = 0.f;
 
   // ---- tile staging: per-lane byte offsets of this wave's 1 KB loads --------
   int koff[NL], voff[NL];
@@ -320,12 +334,15 @@ void prefill_kernel(PrefillArgs a) {
   // K stage j % 4 (lds + (j % 4) TILE), V of tile j in V stage j % 4 (V region,
   // lds + (4 + j % 4) TILE). Barrier B(k) ends iteration k. Between B(k-1) and
   // B(k) every wave runs, for its 32 columns:
-  //   PV(k-1): 4 DB MFMAs O^T += V^T P^T of tile k-1, with the scale FMA
-  //            t = s * scale * log2(e) - Mref of tile k interleaved;
+  //   PV(k-1): 4 DB MFMAs O^T += V^T P^T of tile k-1;
   //   the causal/document mask of tile k (edge tiles only);
-  //   QK(k+1): 2 KS MFMAs S^T = K Q^T of tile k+1, with the exponentials,
-  //            bf16 rounding and row sums of tile k interleaved;
+  //   QK(k+1): 2 KS MFMAs t^T = K Q^T - Mref of tile k+1 (the queries carry
+  //            scale * log2(e) and the accumulation starts from -Mref, so t
+  //            is the exponent in log2 units), with the exponentials, bf16
+  //            rounding and row sums of tile k interleaved;
   //   the lazy reference check of tile k.
+  // The exponents of consecutive tiles are in two register buffers (tile
+  // parity): QK(k+1) writes one while the exponentials read the other.
   // Operand reads run PF MFMAs ahead of their use, across the phase boundary
   // and across the barrier. Each piece of work is emitted in program order and
   // fenced (sched_barrier), so every wave keeps its own matrix core and VALU
@@ -339,18 +356,14 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int NP = 4 * DB;      // PV MFMAs per tile
   constexpr int PF = 3;           // operand reads ahead
   constexpr int EQ = 32 / NQ;     // scores per lane exponentiated per QK MFMA
-  constexpr int EP = 32 / NP;     // scores per lane scaled per PV MFMA
   static_assert(PF <= NQ && PF <= NP && EQ % 2 == 0, "pipeline shape");
   char* const kst[4] = {lds, lds + TILE, lds + 2 * TILE, lds + 3 * TILE};
   char* const vst[4] = {lds + 4 * TILE, lds + 5 * TILE, lds + 6 * TILE, lds + 7 * TILE};
 
-  // t of the tile being exponentiated and its weights, one register per value
-  // (flat index e = 16 kb + j of the S^T accumulator element j of key block
-  // kb), so each frees as soon as it is used; S^T of the next tile is the pair
-  // of MFMA accumulators sn
-  float sc[32];
+  // exponents t of tile j in tA (j even) or tB (j odd): element e = 16 kb + i
+  // is element i of key block kb's t^T accumulator
+  f32x16 tA[2], tB[2];
   uint32_t pw[16];                // weights e, e+1 as a bf16 pair in pw[e / 2]
-  f32x16 sn[2];
   bf16x8 kbuf[NQ], vbuf[NP];      // operands read ahead
   float rs = 0.f;                 // this lane's sum of the tile's rounded weights
 
@@ -372,11 +385,11 @@ void prefill_kernel(PrefillArgs a) {
                                    0, 1, 2, 3, 4, 5, 6, 7);
   };
   const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-  // weights of scores e, e+1 into P^T and the row sum
-  auto exp_pair = [&](int e) __attribute__((always_inline)) {
+  // weights of exponents e, e+1 of tt into P^T and the row sum
+  auto exp_pair = [&](const f32x16 (&tt)[2], int e) __attribute__((always_inline)) {
     bf16x2 pr;
-    pr[0] = to_bf16(fast_exp2(sc[e]));
-    pr[1] = to_bf16(fast_exp2(sc[e + 1]));
+    pr[0] = to_bf16(fast_exp2(tt[e >> 4][e & 15]));
+    pr[1] = to_bf16(fast_exp2(tt[(e + 1) >> 4][(e + 1) & 15]));
     pw[e >> 1] = __builtin_bit_cast(uint32_t, pr);
     rs = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, rs, false);
   };
@@ -386,21 +399,22 @@ void prefill_kernel(PrefillArgs a) {
     const u32x4 w = {pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]};
     return __builtin_bit_cast(bf16x8, w);
   };
-  // QK of the next tile (K stage lk) with the weights of the current one; the
-  // reads past the QK operands fetch the first PF V operands of the current
-  // tile (V stage lv)
-  auto phase_qk = [&](const char* __restrict__ lk, const char* __restrict__ lv) __attribute__((always_inline)) {
+  // QK of the next tile (K stage lk) into tn with the weights of the current
+  // one (exponents tc); the reads past the QK operands fetch the first PF V
+  // operands of the current tile (V stage lv)
+  auto phase_qk = [&](const char* __restrict__ lk, const char* __restrict__ lv, f32x16 (&tn)[2],
+                      const f32x16 (&tc)[2]) __attribute__((always_inline)) {
     rs = 0.f;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int kb = i / KS, ks = i % KS;
-      sn[kb] = mfma32(kbuf[i], qreg[0][ks], ks == 0 ? f32x16{} : sn[kb]);
+      tn[kb] = mfma32(kbuf[i], qreg[0][ks], ks == 0 ? negMv : tn[kb]);
       const int j = i + PF;
       if (j < NQ) kbuf[j] = rd_k(lk, j);
       else vbuf[j - NQ] = rd_v(lv, j - NQ);
 #pragma unroll
-      for (int e = EQ * i; e < EQ * (i + 1); e += 2) exp_pair(e);
+      for (int e = EQ * i; e < EQ * (i + 1); e += 2) exp_pair(tc, e);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -412,11 +426,8 @@ void prefill_kernel(PrefillArgs a) {
     const int kt = kv_lo + k * kKT;
     return (!wave_all_valid) | (kt + kKT - 1 > w_tmin + qo) | (kt < w_smax) | (kt + kKT > kend);
   };
-  // PV of the previous tile (V stage lv) with the scale FMA of tile k's
-  // scores; the reads past the PV operands fetch the first PF K operands of
-  // tile k+1 (K stage lk2). Each FMA result is pinned where it is formed (an
-  // empty asm that takes it in a register), or the compiler would move all 32
-  // FMAs out of the MFMA stream to where the scores are first used.
+  // PV of the previous tile (V stage lv); the reads past the PV operands
+  // fetch the first PF K operands of tile k+1 (K stage lk2)
   auto phase_pv = [&](const char* __restrict__ lv, const char* __restrict__ lk2) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -426,11 +437,6 @@ void prefill_kernel(PrefillArgs a) {
       const int j = i + PF;
       if (j < NP) vbuf[j] = rd_v(lv, j);
       else kbuf[j - NP] = rd_k(lk2, j - NP);
-#pragma unroll
-      for (int e = EP * i; e < EP * (i + 1); ++e) {
-        sc[e] = fmaf(sn[e >> 4][e & 15], a.scale_log2, negM);
-        asm volatile("" : "+v"(sc[e]));
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -439,14 +445,14 @@ void prefill_kernel(PrefillArgs a) {
   // 32 kb + 8 (j / 4) + 4 hi + j % 4, visible when in [st, min(tok + qo,
   // kend - 1)]; keys at or past kend (a ring step's key shard can end before
   // the rows' positions) are masked too
-  auto mask_tile = [&](int k) __attribute__((always_inline)) {
+  auto mask_tile = [&](int k, f32x16 (&tt)[2]) __attribute__((always_inline)) {
     const int kt = kv_lo + k * kKT;
     const int lo4 = (valid[0] ? st[0] - kt : kKT) - 4 * hi;
     const int hi4 = (valid[0] ? min(tok[0] + qo, kend - 1) - kt : -1) - 4 * hi;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const int r = 32 * (e >> 4) + 8 * ((e & 15) >> 2) + (e & 3);
-      sc[e] = (r >= lo4 && r <= hi4) ? sc[e] : -INFINITY;
+      tt[e >> 4][e & 15] = (r >= lo4 && r <= hi4) ? tt[e >> 4][e & 15] : -INFINITY;
     }
   };
   // the last PV (tile n_tiles - 1, V stage lv): its first PF operands were
@@ -459,31 +465,38 @@ void prefill_kernel(PrefillArgs a) {
       acc[db] = mfma32(vbuf[i], p_op(ks), acc[db]);
     }
   };
-  // After the weights of a tile: the reference must move only if a weight may
-  // exceed kLazyW (some lane's sum of them does) or the column has no
-  // reference yet. It then moves up to the tile's column max (d = how far, in
-  // log2 units), the accumulator and row sum are scaled by 2^-d and the
-  // weights are formed again; a column still without a visible key keeps
-  // Mref = -inf. Softmax does not depend on the reference, so this is exact.
-  auto settle = [&]() __attribute__((always_inline)) {
+  // After the weights of a tile (exponents tc): the reference must move only
+  // if a weight may exceed kLazyW (some lane's sum of them does) or the column
+  // has no reference yet. It then moves up to the tile's column max (d = how
+  // far, in log2 units), the accumulator and row sum are scaled by 2^-d and
+  // the weights are formed again; the next tile's exponents (tn, formed from
+  // the old reference) move by d too. A column still without a visible key
+  // keeps Mref = -inf. Softmax does not depend on the reference, so this is
+  // exact.
+  auto settle = [&](f32x16 (&tc)[2], f32x16 (&tn)[2]) __attribute__((always_inline)) {
     if (__any(Mref == -INFINITY || !(rs <= kLazyW))) {
-      float mx = sc[0];
+      float mx = tc[0][0];
 #pragma unroll
-      for (int e = 1; e < 32; ++e) mx = fmaxf(mx, sc[e]);
+      for (int e = 1; e < 32; ++e) mx = fmaxf(mx, tc[e >> 4][e & 15]);
       mx = max_xor32(mx);
       const bool none = Mref == -INFINITY;
       const float d = none ? (mx > -INFINITY ? mx : 0.f) : fmaxf(mx, 0.f);
       const float al = none ? 1.f : fast_exp2(-d);
       Mref = none ? (mx > -INFINITY ? mx : -INFINITY) : Mref + d;
       negM = Mref == -INFINITY ? 0.f : -Mref;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) negMv[j] = negM;
       l *= al;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= al;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) sc[e] -= d;
+      for (int kb = 0; kb < 2; ++kb) {
+        tc[kb] -= d;
+        tn[kb] -= d;
+      }
       rs = 0.f;
 #pragma unroll
-      for (int e = 0; e < 32; e += 2) exp_pair(e);
+      for (int e = 0; e < 32; e += 2) exp_pair(tc, e);
     }
     l += rs;
   };
@@ -502,16 +515,16 @@ void prefill_kernel(PrefillArgs a) {
   // take the direct-to-LDS loads it issues as writers of what its reads fetch;
   // the waits and barriers order the stages.
   auto iter = [&](char* __restrict__ kdst, char* __restrict__ vdst, const char* __restrict__ vprev,
-                  const char* __restrict__ knext, const char* __restrict__ vcur, int k)
-      __attribute__((always_inline)) {
+                  const char* __restrict__ knext, const char* __restrict__ vcur, int k, f32x16 (&tc)[2],
+                  f32x16 (&tn)[2]) __attribute__((always_inline)) {
     const bool masked = needs_mask(k);
     phase_pv(vprev - 4 * TILE, knext);
-    if (masked) mask_tile(k);
+    if (masked) mask_tile(k, tc);
     // (issued here rather than before the PV: the register allocator then
     // keeps every operand in registers; issued earlier they measured no faster)
     stage_kv(tile_kt(k + 3), kdst, false);
     stage_kv(tile_kt(k + 2), vdst, true);
-    phase_qk(knext, vcur - 4 * TILE);
+    phase_qk(knext, vcur - 4 * TILE, tn, tc);
   };
   // Iteration 0: the loads of K3 and V2, QK of tile 0 (its operands read
   // here), the scale FMA and mask of tile 0, the first K1 operands, then QK(1)
@@ -524,14 +537,12 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < NQ; ++i) kbuf[i] = rd_k(k0, i);
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) sn[i / KS] = mfma32(kbuf[i], qreg[0][i % KS], i % KS == 0 ? f32x16{} : sn[i / KS]);
-    // (no PV precedes tile 0: its scale FMA and mask run on their own)
-#pragma unroll
-    for (int e = 0; e < 32; ++e) sc[e] = fmaf(sn[e >> 4][e & 15], a.scale_log2, negM);
-    if (masked) mask_tile(0);
+    for (int i = 0; i < NQ; ++i) tA[i / KS] = mfma32(kbuf[i], qreg[0][i % KS], i % KS == 0 ? negMv : tA[i / KS]);
+    // (no PV precedes tile 0: its mask runs on its own)
+    if (masked) mask_tile(0, tA);
 #pragma unroll
     for (int i = 0; i < PF; ++i) kbuf[i] = rd_k(k1, i);
-    phase_qk(k1, v0 - 4 * TILE);
+    phase_qk(k1, v0 - 4 * TILE, tB, tA);
   };
 
   // ---- prologue loads: K0, K1, V0, K2, V1 (K and V stage 3 hold the RoPE table) --
@@ -552,8 +563,8 @@ void prefill_kernel(PrefillArgs a) {
       bf16x8 r;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        r[2 * p] = to_bf16(fmaf(x[2 * p], cv[p], -x[2 * p + 1] * sv[p]));
-        r[2 * p + 1] = to_bf16(fmaf(x[2 * p], sv[p], x[2 * p + 1] * cv[p]));
+        r[2 * p] = to_bf16(fmaf(x[2 * p], cv[p], -x[2 * p + 1] * sv[p]) * qscale);
+        r[2 * p + 1] = to_bf16(fmaf(x[2 * p], sv[p], x[2 * p + 1] * cv[p]) * qscale);
       }
       return r;
     };
@@ -563,8 +574,8 @@ void prefill_kernel(PrefillArgs a) {
                            bf16x8& r, bf16x8& t) __attribute__((always_inline)) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        r[e0 + p] = to_bf16(fmaf(x[e0 + p], cv[p], -y[e0 + p] * sv[p]));
-        t[e0 + p] = to_bf16(fmaf(x[e0 + p], sv[p], y[e0 + p] * cv[p]));
+        r[e0 + p] = to_bf16(fmaf(x[e0 + p], cv[p], -y[e0 + p] * sv[p]) * qscale);
+        t[e0 + p] = to_bf16(fmaf(x[e0 + p], sv[p], y[e0 + p] * cv[p]) * qscale);
       }
     };
     if constexpr (TQ * (D / 2) * 4 <= TILE) {
@@ -650,7 +661,7 @@ void prefill_kernel(PrefillArgs a) {
   }
   sync_tiles();   // K0, K1, V0 landed; every wave is done with the RoPE table
   iter0(kst[3], vst[2], kst[0], kst[1], vst[0]);
-  settle();
+  settle(tA, tB);
   sync_tiles();   // B(0)
   // Unrolled over the four stage indices so every stage offset is a constant.
   // The loop has one exit: steps at or past the last tile are skipped by a
@@ -659,8 +670,11 @@ void prefill_kernel(PrefillArgs a) {
   auto step = [&](auto U, int k) __attribute__((always_inline)) {
     constexpr int u = decltype(U)::value;   // k % 4
     if (k < n_tiles) {
-      iter(kst[(u + 3) & 3], vst[(u + 2) & 3], vst[(u + 3) & 3], kst[(u + 1) & 3], vst[u], k);
-      settle();
+      // exponents of tile k in tA (k even) or tB; tile k+1's go to the other
+      f32x16(&tc)[2] = (u & 1) ? tB : tA;
+      f32x16(&tn)[2] = (u & 1) ? tA : tB;
+      iter(kst[(u + 3) & 3], vst[(u + 2) & 3], vst[(u + 3) & 3], kst[(u + 1) & 3], vst[u], k, tc, tn);
+      settle(tc, tn);
       sync_tiles();   // B(k)
     }
   };
