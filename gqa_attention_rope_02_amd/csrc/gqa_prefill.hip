@@ -88,7 +88,12 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <typename T, int D, int G>
+// QS: the query operand carries scale * log2(e) (queries rotated in the
+// kernel, or fp32 queries: either way rounded once to bf16 from fp32). For
+// queries that arrive rotated in bf16 (QS false) the operand is the query
+// itself, since scaling it would round it a second time, and the exponents
+// are formed from the scores by one FMA each.
+template <typename T, int D, int G, bool QS>
 __global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int TQ = kCols / G;          // tokens per workgroup
@@ -166,23 +171,28 @@ void prefill_kernel(PrefillArgs a) {
   // Columns past the sequence end load the last token's row (no branch, so
   // the wait for the offsets row does not also wait for Q); every key is
   // masked for them and their outputs are not stored.
-  // The operand holds q * scale * log2(e), rounded once to bf16 (after the
-  // rotation when the kernel rotates), so the score MFMA yields the exponent
-  // in log2 units directly.
+  // With QS the operand holds q * scale * log2(e), rounded once to bf16
+  // (after the rotation when the kernel rotates), so the score MFMA yields
+  // the exponent in log2 units directly.
   bf16x8 qreg[kCB][KS];
-  float qraw[kCB][KS][8];   // the loaded queries in fp32
+  float qraw[kCB][KS][8];   // the loaded queries in fp32 (QS)
   const bool rope_q = a.rope_q != 0;
-  const float qscale = a.scale_log2;
+  const float qscale = QS ? a.scale_log2 : 1.f;
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
     const T* qp = qbase + min(tok[cb], Sq - 1) * a.qs_s + head[cb] * a.qs_h + 8 * hi;
+    if constexpr (QS) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load8_f32(qp + 16 * ks, qraw[cb][ks]);
-    if (!rope_q) {
+      for (int ks = 0; ks < KS; ++ks) load8_f32(qp + 16 * ks, qraw[cb][ks]);
+      if (!rope_q) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qreg[cb][ks][i] = to_bf16(qraw[cb][ks][i] * qscale);
+          for (int i = 0; i < 8; ++i) qreg[cb][ks][i] = to_bf16(qraw[cb][ks][i] * qscale);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qreg[cb][ks] = load8(qp + 16 * ks);
     }
   }
 
@@ -427,8 +437,13 @@ void prefill_kernel(PrefillArgs a) {
     return (!wave_all_valid) | (kt + kKT - 1 > w_tmin + qo) | (kt < w_smax) | (kt + kKT > kend);
   };
   // PV of the previous tile (V stage lv); the reads past the PV operands
-  // fetch the first PF K operands of tile k+1 (K stage lk2)
-  auto phase_pv = [&](const char* __restrict__ lv, const char* __restrict__ lk2) __attribute__((always_inline)) {
+  // fetch the first PF K operands of tile k+1 (K stage lk2). Without QS the
+  // scale FMA of tile k's scores (tc) is interleaved, each result pinned
+  // where it is formed (an empty asm that takes it in a register), or the
+  // compiler would move the FMAs out of the MFMA stream.
+  constexpr int EP = 32 / NP;     // scores per lane scaled per PV MFMA (without QS)
+  auto phase_pv = [&](const char* __restrict__ lv, const char* __restrict__ lk2, f32x16 (&tc)[2])
+      __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -437,6 +452,13 @@ void prefill_kernel(PrefillArgs a) {
       const int j = i + PF;
       if (j < NP) vbuf[j] = rd_v(lv, j);
       else kbuf[j - NP] = rd_k(lk2, j - NP);
+      if constexpr (!QS) {
+#pragma unroll
+        for (int e = EP * i; e < EP * (i + 1); ++e) {
+          tc[e >> 4][e & 15] = fmaf(tc[e >> 4][e & 15], a.scale_log2, negM);
+          asm volatile("" : "+v"(tc[e >> 4][e & 15]));
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -484,15 +506,17 @@ void prefill_kernel(PrefillArgs a) {
       const float al = none ? 1.f : fast_exp2(-d);
       Mref = none ? (mx > -INFINITY ? mx : -INFINITY) : Mref + d;
       negM = Mref == -INFINITY ? 0.f : -Mref;
+      if constexpr (QS) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) negMv[j] = negM;
+        for (int j = 0; j < 16; ++j) negMv[j] = negM;
+      }
       l *= al;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= al;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         tc[kb] -= d;
-        tn[kb] -= d;
+        if constexpr (QS) tn[kb] -= d;   // (without QS tn holds raw scores)
       }
       rs = 0.f;
 #pragma unroll
@@ -518,7 +542,7 @@ void prefill_kernel(PrefillArgs a) {
                   const char* __restrict__ knext, const char* __restrict__ vcur, int k, f32x16 (&tc)[2],
                   f32x16 (&tn)[2]) __attribute__((always_inline)) {
     const bool masked = needs_mask(k);
-    phase_pv(vprev - 4 * TILE, knext);
+    phase_pv(vprev - 4 * TILE, knext, tc);
     if (masked) mask_tile(k, tc);
     // (issued here rather than before the PV: the register allocator then
     // keeps every operand in registers; issued earlier they measured no faster)
@@ -538,7 +562,12 @@ void prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < NQ; ++i) kbuf[i] = rd_k(k0, i);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) tA[i / KS] = mfma32(kbuf[i], qreg[0][i % KS], i % KS == 0 ? negMv : tA[i / KS]);
-    // (no PV precedes tile 0: its mask runs on its own)
+    // (no PV precedes tile 0: its scale FMA (without QS) and mask run on
+    // their own)
+    if constexpr (!QS) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) tA[e >> 4][e & 15] = fmaf(tA[e >> 4][e & 15], a.scale_log2, negM);
+    }
     if (masked) mask_tile(0, tA);
 #pragma unroll
     for (int i = 0; i < PF; ++i) kbuf[i] = rd_k(k1, i);
@@ -551,7 +580,7 @@ void prefill_kernel(PrefillArgs a) {
   stage_kv(tile_kt(0), vst[0], true);
   stage_kv(tile_kt(2), kst[2], false);
   stage_kv(tile_kt(1), vst[1], true);
-  if (rope_q) {
+  if (QS && rope_q) {
     // RoPE of this lane's query channels 16ks + 8hi + 0..7, i.e. the pairs
     // k = 8ks + 4hi + p (adjacent pairs (2k, 2k+1)) or, for half-split pairs
     // (k, k + D/2), k = 16ks + 8hi + i for ks < KS/2 with the same channels of
@@ -831,7 +860,15 @@ template <typename T, int D, int G>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)a.B * a.Hkv * a.n_qtiles;
   const unsigned splits = a.split_tiles > 0 ? (unsigned)a.max_splits : 1u;
-  hipLaunchKernelGGL((prefill_kernel<T, D, G>), dim3(grid, splits), dim3(64 * kNW), 0, st, a);
+  // bf16 queries that arrive rotated keep their exact values (no QS); fp32
+  // queries and queries the kernel rotates are scaled before their rounding
+  if constexpr (std::is_same<T, __bf16>::value) {
+    if (!a.rope_q) {
+      hipLaunchKernelGGL((prefill_kernel<T, D, G, false>), dim3(grid, splits), dim3(64 * kNW), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((prefill_kernel<T, D, G, true>), dim3(grid, splits), dim3(64 * kNW), 0, st, a);
   return hipGetLastError();
 }
 

@@ -77,7 +77,10 @@ def test_prefill_rope_agrees_with_the_two_call_path():
 
 def test_prefill_rope_position_zero_leaves_queries_unrotated():
     """At position 0 every angle is 0: with all positions 0 the fused path
-    equals gqa_prefill on the unrotated queries, bit for bit."""
+    equals gqa_prefill on the unrotated queries given in fp32, bit for bit.
+    (Both round q * scale * log2(e) once to bf16 from the same fp32 value; the
+    fp32 call rounds K and V to bf16 on their way into LDS, exactly here since
+    they are bf16 values, and writes O in fp32, which rounds to the bf16 O.)"""
     import gqa_attention_rope_02_amd as la
     B, S, Hq, Hkv, D = 1, 130, 16, 2, 128
     H.say("prefill_rope position 0")
@@ -85,12 +88,12 @@ def test_prefill_rope_position_zero_leaves_queries_unrotated():
     dev = torch.device("cuda")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     pos = torch.zeros(B, S, dtype=torch.int32, device=dev)
-    o1 = torch.empty_like(qd)
+    o1 = torch.empty(B, S, Hq, D, dtype=torch.float32, device=dev)
     o2 = torch.empty_like(qd)
-    la.gqa_prefill(qd, kd, vd, o1)
+    la.gqa_prefill(qd.float(), kd.float(), vd.float(), o1)
     la.gqa_prefill_rope(qd, kd, vd, o2, positions=pos)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2)
+    assert torch.equal(o1.bfloat16(), o2)
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,D,seed,positions", [
