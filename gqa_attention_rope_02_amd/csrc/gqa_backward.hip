@@ -241,16 +241,34 @@ void dkdv_kernel(BwdArgs a) {
     f32x16 sd[NCB];
     if (!skip) {
       const char* src = st + role * QT;
+      // role 1 starts dP from the columns' staged -delta, so its MFMAs yield
+      // dP - delta directly; role 0 starts S from 0
+      auto products = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
+        for (int ks = 0; ks < KS; ++ks) {
+          const int ch = 16 * t_chunk<CH>(2 * ks + hi, lc);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sd[cb][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int ch = 16 * t_chunk<CH>(2 * ks + hi, lc);
+          for (int cb = 0; cb < NCB; ++cb)
+            sd[cb] = mfma32(*reinterpret_cast<const bf16x8*>(src + (32 * cb + lc) * ROW + ch), kv[ks], sd[cb]);
+        }
+      };
+      if (role == 0) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
-          sd[cb] = mfma32(*reinterpret_cast<const bf16x8*>(src + (32 * cb + lc) * ROW + ch), kv[ks], sd[cb]);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sd[cb][i] = 0.f;
+        products();
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int c0 = 32 * cb + 8 * q4 + 4 * hi;
+            const f32x4 e4 = *reinterpret_cast<const f32x4*>(st + 2 * QT + kNC * 4 + 4 * c0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sd[cb][4 * q4 + u] = e4[u];
+          }
+        products();
       }
       if (role == 0) {
         // P = exp(s scale - lse) on visible pairs, to LDS for role 1
@@ -285,16 +303,14 @@ void dkdv_kernel(BwdArgs a) {
     __syncthreads();   // role 0's P is in LDS
     if (!skip) {
       if (role == 1) {
-        // dS = P (dP - delta)
+        // dS = P (dP - delta), sd holding dP - delta
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const int c0 = 32 * cb + 8 * q4 + 4 * hi;
-            const f32x4 e4 = *reinterpret_cast<const f32x4*>(st + 2 * QT + kNC * 4 + 4 * c0);
             const f32x4 pv = *reinterpret_cast<const f32x4*>(pbuf + ((cb * 4 + q4) * 64 + lane) * 16);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) sd[cb][4 * q4 + u] = pv[u] * (sd[cb][4 * q4 + u] - e4[u]);
+            for (int u = 0; u < 4; ++u) sd[cb][4 * q4 + u] = pv[u] * sd[cb][4 * q4 + u];
           }
       }
       // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1), the A operand read
@@ -380,8 +396,9 @@ void dq_kernel(BwdArgs a, int n_qtiles) {
   const int64_t li = ((int64_t)b * a.Hq + head) * S + tc;
   const float lse2 = a.lse[li] * kLog2e;
   // delta of the column, dO . O: this lane's half of the row (the d of its
-  // operand registers) plus the other half from lane l ^ 32; written for the
-  // dk/dv kernel, which runs after this one
+  // operand registers) plus the other half from lane l ^ 32; written negated
+  // for the dk/dv kernel, which runs after this one and starts its dP
+  // accumulation from it
   float dlt = 0.f;
   {
     const __bf16* op = static_cast<const __bf16*>(a.o) + b * a.os_b + tc * a.os_s + head * a.os_h + 8 * hi;
@@ -394,7 +411,7 @@ void dq_kernel(BwdArgs a, int n_qtiles) {
     }
     const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(dlt), __float_as_uint(dlt), false, false);
     dlt = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-    if (valid && hi == 0) a.delta[li] = dlt;
+    if (valid && hi == 0) a.delta[li] = -dlt;
   }
   const int dstart = cu ? doc_start(cu, a.n_docs, tc) : 0;
   // keys dstart .. t are visible: 0 <= key - dstart < lim

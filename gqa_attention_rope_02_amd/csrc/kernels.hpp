@@ -99,7 +99,7 @@ struct CombineArgs {
 };
 
 // Gradient pass (bf16 tensors): q, k rotated; o, lse from the forward; dout
-// the output gradient; delta fp32 [B, Hq, S] a workspace (rowsum(dout o)).
+// the output gradient; delta fp32 [B, Hq, S] a workspace (-rowsum(dout o)).
 struct BwdArgs {
   const void* q;
   const void* k;

@@ -353,7 +353,7 @@ la_status rope_qk_backward(const void* dq_in, void* dq_out, const int64_t dq_in_
  * Hq times their head stride, which is at least D (each token's heads lie in
  * its row). o and lse are the forward's outputs for these q, k, v (lse fp32
  * [B, Hq, S] contiguous, natural log). delta: caller-owned fp32 workspace
- * [B, Hq, S] (contiguous), overwritten with dout_i . o_i. cu_docs, n_docs,
+ * [B, Hq, S] (contiguous), overwritten with -(dout_i . o_i). cu_docs, n_docs,
  * softmax_scale as gqa_prefill. dq, dk, dv are written, not accumulated.
  * dkv_workspace: optional caller-owned fp32 buffer of
  * LA_BWD_PIECES * B * S * Hkv * 2 * D elements (16-byte aligned; contents
