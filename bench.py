@@ -238,7 +238,7 @@ def chunk_pairs(cu_docs: np.ndarray, S: int, Sq: int) -> int:
     return int(np.sum(rows - start + 1))
 
 
-CHUNK_SPLIT_TILES = 24   # key tiles per piece for the chunked prefill (gqa_prefill_split)
+CHUNK_SPLIT_TILES = 16   # key tiles per piece for the chunked prefill (gqa_prefill_split; 16 measured best of 8-32)
 
 
 def time_chunk(st, Sq: int, steps: int, warmup: int, settle_s: float = 0.0, split_tiles: int = 0):
