@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "GQA prefill TFLOP/s (% MFMA peak) + decode KV-read GB/s (% HBM peak), 1 GPU"
-KV_CHUNK = 256
+KV_CHUNK = int(os.environ.get("LLAMA_ATTN_KV_CHUNK") or 256)   # decode keys per split (LLAMA_ATTN_KV_CHUNK overrides)
 
 
 def log(*a):
@@ -489,12 +489,31 @@ def blas_threads() -> int:
         return os.cpu_count() or 1
 
 
-def cpu_prefill_rate(host_inputs, w, cu, budget_s: float):
+class _ErrStats:
+    """max and mean absolute difference of the GPU's values from the oracle's
+    over the elements compared so far."""
+
+    def __init__(self):
+        self.mx, self.sum, self.n = 0.0, 0.0, 0
+
+    def add(self, got, want):
+        d = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(want, dtype=np.float64))
+        self.mx = max(self.mx, float(d.max()))
+        self.sum += float(d.sum())
+        self.n += d.size
+
+    def out(self):
+        return {"max_abs": self.mx, "mean_abs": self.sum / max(self.n, 1), "elements": self.n}
+
+
+def cpu_prefill_rate(host_inputs, w, cu, budget_s: float, gpu_out=None):
     """The fp64 row oracle (incl. RoPE), as it stands, on 64-row blocks of
     consecutive query rows (all heads) drawn uniformly, one oracle call per
     block, for about budget_s seconds: TFLOP/s counting 4 D per visible
     (query head, key) pair of the rows done, and the whole workload's oracle
-    time extrapolated linearly in visible pairs."""
+    time extrapolated linearly in visible pairs. With gpu_out = (O, LSE) of
+    the timed path on the device, its rows are compared with the oracle's
+    (max and mean absolute difference)."""
     from oracle import reference as orc
     q, k, v = host_inputs
     rng = np.random.default_rng(w.seed + 7)
@@ -503,15 +522,21 @@ def cpu_prefill_rate(host_inputs, w, cu, budget_s: float):
     blk = 64
     order = rng.permutation(-(-w.S // blk))
     done_rows, done_blocks, flops, t_used = 0, 0, 0.0, 0.0
+    eo, el = _ErrStats(), _ErrStats()
     t0 = time.perf_counter()
     for b in order:
         rows = np.arange(b * blk, min((b + 1) * blk, w.S))
-        orc.rope_attention_rows(q[0], k[0], v[0], rows, cu, w.rope_base, block=blk)
+        t1 = time.perf_counter()
+        Ow, Lw = orc.rope_attention_rows(q[0], k[0], v[0], rows, cu, w.rope_base, block=blk)
+        t_used += time.perf_counter() - t1
         done_rows += rows.size
         done_blocks += 1
         flops += 4.0 * w.D * w.Hq * float(np.sum(rows - start[rows] + 1))
-        t_used = time.perf_counter() - t0
-        if t_used >= budget_s:
+        if gpu_out is not None:
+            ri = torch_index(rows)
+            eo.add(gpu_out[0][0, ri].float().cpu().numpy(), Ow)
+            el.add(gpu_out[1][0][:, ri].cpu().numpy(), Lw)
+        if t_used >= budget_s or time.perf_counter() - t0 > 3 * budget_s:
             break
     rate = flops / t_used
     whole = prefill_flops(w, cu)
@@ -524,7 +549,14 @@ def cpu_prefill_rate(host_inputs, w, cu, budget_s: float):
                        f" x all {w.Hq} heads of the {w.name} prefill (fp64 NumPy row oracle incl. RoPE, "
                        f"one call per block), {t_used:.1f}s",
                 oracle_s_whole_workload=round(whole / rate, 1),
-                extrapolated=not full)
+                extrapolated=not full,
+                parity=None if gpu_out is None else {"O": eo.out(), "LSE": el.out(),
+                                                     "rows": "the oracle's rows above"})
+
+
+def torch_index(rows):
+    import torch
+    return torch.as_tensor(rows, dtype=torch.long)
 
 
 def cpu_decode_rate(st, budget_s: float):
@@ -538,34 +570,44 @@ def cpu_decode_rate(st, budget_s: float):
     rng = np.random.default_rng(w.seed + 7)
     pairs = [(int(b), int(h)) for b in rng.permutation(w.B) for h in rng.permutation(w.Hkv)]
     done, nbytes, t_used = 0, 0.0, 0.0
-    t0 = time.perf_counter()
+    eo = _ErrStats()
     for b, h in pairs:
         L = int(lens[b])
         qb = st["q"][b:b + 1, h * g:(h + 1) * g].cpu()
         kb = [st["kc"][b, h:h + 1, :L].cpu()]
         vb = [st["vc"][b, h:h + 1, :L].cpu()]
-        orc.decode(qb, kb, vb, [L])
+        t1 = time.perf_counter()
+        Ow, _ = orc.decode(qb, kb, vb, [L])
+        t_used += time.perf_counter() - t1
+        eo.add(st["o"][b:b + 1, h * g:(h + 1) * g].float().cpu().numpy(), Ow)
         done += 1
         nbytes += L * w.D * 2 * 2
-        t_used = time.perf_counter() - t0
         if t_used >= budget_s:
             break
     rate = nbytes / t_used
     return dict(value=rate / 1e9, unit="GB/s", cores=blas_threads(), kind="oracle", cpu_model=cpu_model(),
                 sample=f"{done} of {len(pairs)} (sequence, KV head) caches of the decode405b workload "
                        f"(fp64 NumPy decode oracle), {t_used:.1f}s",
-                oracle_s_whole_workload=round(decode_bytes(st) / rate, 1), extrapolated=done < len(pairs))
+                oracle_s_whole_workload=round(decode_bytes(st) / rate, 1), extrapolated=done < len(pairs),
+                parity={"O": eo.out(), "heads": "the (sequence, KV head) caches above, after the timed decode"})
 
 
-def cpu_tiny_rate(host_inputs, w, cu):
+def cpu_tiny_rate(host_inputs, w, cu, gpu_out=None):
     """The whole tiny workload through the fp64 oracle (incl. RoPE)."""
     from oracle import reference as orc
     q, k, v = host_inputs
     t0 = time.perf_counter()
-    orc.rope_attention(q, k, v, cu, w.rope_base)
+    Ow, Lw = orc.rope_attention(q, k, v, cu, w.rope_base)
     t = time.perf_counter() - t0
+    par = None
+    if gpu_out is not None:
+        eo, el = _ErrStats(), _ErrStats()
+        eo.add(gpu_out[0].float().cpu().numpy(), Ow)
+        el.add(gpu_out[1].cpu().numpy(), Lw)
+        par = {"O": eo.out(), "LSE": el.out(), "rows": "all"}
     return dict(value=prefill_flops(w, cu) / t / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
-                cpu_model=cpu_model(), sample=f"the whole tiny workload, {t * 1e3:.1f} ms", extrapolated=False)
+                cpu_model=cpu_model(), sample=f"the whole tiny workload, {t * 1e3:.1f} ms", extrapolated=False,
+                parity=par)
 
 
 # ------------------------------------------------------------------------ main
@@ -648,7 +690,7 @@ def main():
         out["timing"] = {k: (round(x, 4) if isinstance(x, float) else x) for k, x in t.items()}
         if cpu:
             log("timing the fp64 oracle on a row sample of the 128K prefill ...")
-            out["cpu_baseline"] = cpu_prefill_rate(host, w, cu, 15.0)
+            out["cpu_baseline"] = cpu_prefill_rate(host, w, cu, 15.0, (st["o"], st["lse"]))
         del st, host
         torch.cuda.empty_cache()
 
@@ -662,6 +704,9 @@ def main():
                 st, t, "llama-3.1-8b attention layer prefill S=8192, 32 q / 8 kv heads: rope_qk (keys) + "
                        "gqa_prefill_rope")
             out["prefill_8b"]["traffic"] = measured_traffic("gqa_prefill", "llama8b", phash)
+            if cpu and only != "backward":
+                log("timing the fp64 oracle on a row sample of the 8B prefill ...")
+                cpu_cfg["llama8b"] = cpu_prefill_rate(host, w, cu, 8.0, (st["o"], st["lse"]))
             Sq = 2048
             tc = time_chunk(st, Sq, args.steps, args.warmup, args.settle, CHUNK_SPLIT_TILES)
             tu = time_chunk(st, Sq, args.steps, args.warmup, 0.0)
@@ -691,9 +736,6 @@ def main():
             out.update(value=out["backward_8b"]["tflops"], unit="TFLOP/s",
                        ms_per_step=out["backward_8b"]["backward_ms"],
                        config={"workload": out["backward_8b"]["workload"]})
-        elif cpu:
-            log("timing the fp64 oracle on a row sample of the 8B prefill ...")
-            cpu_cfg["llama8b"] = cpu_prefill_rate(host, w, cu, 8.0)
         del st, host
 
     # ---- 405B at S=32768: prefill, context-parallel ring ----------------------------
@@ -704,6 +746,9 @@ def main():
             st3, t3, "llama-3.1-405b attention layer prefill S=32768, 128 q / 8 kv heads: rope_qk (keys) + "
                      "gqa_prefill_rope")
         out["prefill_405b"]["traffic"] = measured_traffic("gqa_prefill", "llama405b", phash)
+        if cpu:
+            log("timing the fp64 oracle on a row sample of the 405B prefill ...")
+            cpu_cfg["llama405b"] = cpu_prefill_rate(host3, st3["w"], st3["cu"], 8.0, (st3["o"], st3["lse"]))
         P = 8
         fl3 = prefill_flops(st3["w"], st3["cu"])
         tr = time_ring(st3, P, 2)
@@ -713,9 +758,6 @@ def main():
             "tflops": round(fl3 / (tr * 1e-3) / 1e12, 2),
             "frac": round(fl3 / (tr * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "ms_per_ring": round(tr, 3)}
-        if cpu:
-            log("timing the fp64 oracle on a row sample of the 405B prefill ...")
-            cpu_cfg["llama405b"] = cpu_prefill_rate(host3, st3["w"], st3["cu"], 8.0)
         del st3, host3
         torch.cuda.empty_cache()
 
@@ -726,7 +768,7 @@ def main():
         out["tiny"] = prefill_record(st1, t1, "tiny prefill S=128, 8 q / 2 kv heads, head_dim 64, fp32 "
                                               "(launch-bound: absolute time only)")
         if cpu:
-            cpu_cfg["tiny"] = cpu_tiny_rate(host1, st1["w"], st1["cu"])
+            cpu_cfg["tiny"] = cpu_tiny_rate(host1, st1["w"], st1["cu"], (st1["o"], st1["lse"]))
         del st1, host1
 
     # ---- 405B-shape decode ---------------------------------------------------------

@@ -40,6 +40,8 @@ contiguous):
   [B,S,Hq,D]; k, v, dk, dv [B,S,Hkv,D]; lse fp32 [B,Hq,S] from the forward; delta fp32
   [B,Hq,S] workspace (allocated when None); workspace: ``backward_workspace(B, S, Hkv, D)``
   (allocated when "auto"; None runs without cutting long query ranges).
+* kv_chunk (keys per split of the decode calls) may be None: the
+  LLAMA_ATTN_KV_CHUNK environment variable, else 256 (``default_kv_chunk()``).
 * ``gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk, o_part, lse_part,
   softmax_scale=0.0)``: q [B,Hq,D], caches [B,Hkv,Lmax,D], seq_lens int32 [B],
   o_part fp32 [B,Hq,max_splits,D], lse_part fp32 [B,Hq,max_splits].
@@ -55,6 +57,8 @@ contiguous):
 
 from __future__ import annotations
 
+import os
+
 import torch
 
 from . import _lib
@@ -62,7 +66,7 @@ from . import _lib
 __all__ = ["LlamaAttnError", "rope_qk", "rope_qk_backward", "gqa_attention_backward", "backward_workspace", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk",
            "gqa_prefill_split", "prefill_split_workspace", "gqa_prefill_ring_step",
            "gqa_prefill_ring_finalize", "gqa_decode", "gqa_decode_paged",
-           "gqa_decode_combine", "gqa_decode_noalloc", "version", "LA_BF16", "LA_FP32"]
+           "gqa_decode_combine", "gqa_decode_noalloc", "default_kv_chunk", "version", "LA_BF16", "LA_FP32"]
 
 LA_BF16, LA_FP32 = 0, 1
 _DT = {torch.bfloat16: LA_BF16, torch.float32: LA_FP32}
@@ -375,6 +379,20 @@ def gqa_prefill_ring_finalize(o_acc, lse_acc, o, lse=None):
     _check(st, "gqa_prefill_ring_finalize")
 
 
+def default_kv_chunk() -> int:
+    """The decode's keys per split when a call passes kv_chunk=None: the
+    LLAMA_ATTN_KV_CHUNK environment variable if set, else 256."""
+    v = os.environ.get("LLAMA_ATTN_KV_CHUNK")
+    kv = int(v) if v else 256
+    if kv < 1:
+        raise ValueError("LLAMA_ATTN_KV_CHUNK must be a positive integer")
+    return kv
+
+
+def _kv_chunk(kv_chunk):
+    return default_kv_chunk() if kv_chunk is None else int(kv_chunk)
+
+
 def gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk: int, o_part, lse_part,
                softmax_scale: float = 0.0):
     B, Hq, D = q.shape
@@ -390,7 +408,7 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, kv_chunk: int, o_part, lse_part,
     op, lp = _f32c(o_part), _f32c(lse_part)
     st = _lib.load().gqa_decode(
         _dev(q), _strides(q, 2), _dev(k_cache), _dev(v_cache), _strides(k_cache, 3),
-        _i32(seq_lens), B, Hq, Hkv, D, Lmax, int(kv_chunk), max_splits, float(softmax_scale),
+        _i32(seq_lens), B, Hq, Hkv, D, Lmax, _kv_chunk(kv_chunk), max_splits, float(softmax_scale),
         op, lp, _stream())
     _check(st, "gqa_decode")
 
@@ -415,7 +433,7 @@ def gqa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, kv_chunk: int, 
     st = _lib.load().gqa_decode_paged(
         _dev(q), _strides(q, 2), _dev(k_pages), _dev(v_pages), page_strides, page_size,
         _i32(block_table), block_table.stride(0), _i32(seq_lens), B, Hq, Hkv, D, int(Lmax),
-        int(kv_chunk), max_splits, float(softmax_scale), op, lp, _stream())
+        _kv_chunk(kv_chunk), max_splits, float(softmax_scale), op, lp, _stream())
     _check(st, "gqa_decode_paged")
 
 
@@ -425,7 +443,7 @@ def gqa_decode_combine(o_part, lse_part, seq_lens, kv_chunk: int, o, lse=None):
             or tuple(seq_lens.shape) != (B,) or (lse is not None and tuple(lse.shape) != (B, Hq)):
         raise ValueError("gqa_decode_combine: inconsistent shapes")
     st = _lib.load().gqa_decode_combine(
-        _f32c(o_part), _f32c(lse_part), _i32(seq_lens), B, Hq, D, int(kv_chunk), max_splits,
+        _f32c(o_part), _f32c(lse_part), _i32(seq_lens), B, Hq, D, _kv_chunk(kv_chunk), max_splits,
         _dev(o), _strides(o, 2), _f32c(lse), _dtype(o), _stream())
     _check(st, "gqa_decode_combine")
 
@@ -444,6 +462,6 @@ def gqa_decode_noalloc(q, k_cache, v_cache, seq_lens, kv_chunk: int, o, lse=None
     lp = _f32c(lse)
     st = _lib.load().gqa_decode_noalloc(
         _dev(q), _strides(q, 2), _dev(k_cache), _dev(v_cache), _strides(k_cache, 3), _i32(seq_lens),
-        B, Hq, Hkv, D, Lmax, int(kv_chunk), float(softmax_scale), _dev(o), _strides(o, 2), lp,
+        B, Hq, Hkv, D, Lmax, _kv_chunk(kv_chunk), float(softmax_scale), _dev(o), _strides(o, 2), lp,
         _dtype(o), _stream())
     _check(st, "gqa_decode_noalloc")

@@ -60,3 +60,15 @@ def test_sample_rows_contains_document_edges():
     for x in (0, 4, 5, 299, 300, 999, 63, 64, 127, 128):
         assert x in r
     assert np.all(np.diff(r) > 0) and r.min() >= 0 and r.max() < 1000
+
+
+def test_kv_chunk_override(monkeypatch):
+    """kv_chunk=None takes LLAMA_ATTN_KV_CHUNK, else 256; non-positive values are rejected."""
+    import gqa_attention_rope_02_amd as la
+    monkeypatch.delenv("LLAMA_ATTN_KV_CHUNK", raising=False)
+    assert la.default_kv_chunk() == 256
+    monkeypatch.setenv("LLAMA_ATTN_KV_CHUNK", "128")
+    assert la.default_kv_chunk() == 128
+    monkeypatch.setenv("LLAMA_ATTN_KV_CHUNK", "0")
+    with pytest.raises(ValueError):
+        la.default_kv_chunk()
