@@ -43,6 +43,8 @@
 // P and dS are rounded to bf16 for the products that use them, fp32
 // accumulation throughout; masks are evaluated only where a block straddles
 // a causal or document edge.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -191,9 +193,9 @@ void dkdv_kernel(BwdArgs a) {
   }
   const int loff = ((lane % G) * S + lane / G) * 4;
   // block m (of the key block's range) into stage (m - blk0) & 1
-  auto issue = [&](int m) __attribute__((always_inline)) {
+  // block m of the key block's range into the stage at dst
+  auto issue = [&](int m, char* dst) __attribute__((always_inline)) {
     const int tb0 = k0 + m * TB;
-    char* dst = lds + ((m - blk0) & 1) * STAGE;
     const int rows = min(S - tb0, TB);        // >= 1: tb0 < q_end <= S
     // byte ranges end at the last valid token's last head row: rows past the
     // sequence end read as zero
@@ -223,12 +225,14 @@ void dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  if (n_blk > 0) issue(blk0);
-  for (int n = 0; n < n_blk; ++n) {
+  // Block n of the piece from stage stg = n % 2; the loop below is unrolled
+  // over the two stages so that every LDS offset is a constant.
+  auto block = [&](int n, auto STG) __attribute__((always_inline)) {
+    constexpr int stg = decltype(STG)::value;
     wait_all();
     __syncthreads();
-    if (n + 1 < n_blk) issue(blk0 + n + 1);
-    const char* st = lds + (n & 1) * STAGE;
+    if (n + 1 < n_blk) issue(blk0 + n + 1, lds + (1 - stg) * STAGE);
+    const char* st = lds + stg * STAGE;
     const int tb0 = k0 + (blk0 + n) * TB;
     // nothing of this block visible to the group's keys: both roles skip the
     // work (never the barriers)
@@ -326,6 +330,11 @@ void dkdv_kernel(BwdArgs a) {
           for (int db = 0; db < DB; ++db) acc[db] = mfma32(read_tr_rows(tsrc + roff, tr1[db], tr2[db]), x, acc[db]);
         }
     }
+  };
+  if (n_blk > 0) issue(blk0, lds);
+  for (int n = 0; n < n_blk; n += 2) {
+    block(n, std::integral_constant<int, 0>{});
+    if (n + 1 < n_blk) block(n + 1, std::integral_constant<int, 1>{});
   }
 
   // lane = key j, element i of block db is d = 32db + 8(i/4) + 4hi + i%4;
@@ -443,9 +452,9 @@ void dq_kernel(BwdArgs a, int n_qtiles) {
     koff[p] = (int)(row * a.ks_s * 2 + 16 * t_chunk<CH>(lane % CH, row));
     voff[p] = (int)(row * a.vs_s * 2 + 16 * k_chunk<CH>(lane % CH, row));
   }
-  auto issue = [&](int n) __attribute__((always_inline)) {
+  // tile n's K and V into the stage at dst
+  auto issue = [&](int n, char* dst) __attribute__((always_inline)) {
     const int kt = kv_lo + n * kKT;
-    char* dst = lds + (n & 1) * 2 * TILE;
     const int rows = min(S - kt, kKT);         // >= 1: kt <= t_last < S
     const int kbytes = (int)(((rows - 1) * a.ks_s + D) * 2);
     const int vbytes = (int)(((rows - 1) * a.vs_s + D) * 2);
@@ -469,15 +478,18 @@ void dq_kernel(BwdArgs a, int n_qtiles) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
 
-  issue(0);
-  for (int n = 0; n < n_tiles; ++n) {
+  // Tile n from stage stg = n % 2; the loop below is unrolled over the two
+  // stages so that every LDS operand offset is a constant (with a run-time
+  // stage each read's address took VALU adds).
+  auto tile = [&](int n, auto STG) __attribute__((always_inline)) {
+    constexpr int stg = decltype(STG)::value;
     wait_all();
     __syncthreads();
-    if (n + 1 < n_tiles) issue(n + 1);
-    const char* lk = lds + (n & 1) * 2 * TILE;
+    if (n + 1 < n_tiles) issue(n + 1, lds + (1 - stg) * 2 * TILE);
+    const char* lk = lds + stg * 2 * TILE;
     const char* lv = lk + TILE;
     const int kt = kv_lo + n * kKT;
-    if (kt > w_tmax || kt + kKT - 1 < w_smin) continue;   // no key of the tile visible to the wave
+    if (kt > w_tmax || kt + kKT - 1 < w_smin) return;   // no key of the tile visible to the wave
     const bool full = wave_all_valid && kt + kKT - 1 <= w_tmin && kt >= w_smax;
 
     f32x16 s[2], dp[2];
@@ -526,6 +538,11 @@ void dq_kernel(BwdArgs a, int n_qtiles) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         dq[db] = mfma32(read_tr_rows(lk + 16 * ks * ROW, tr1[db], tr2[db]), sb[ks >> 1][ks & 1], dq[db]);
+  };
+  issue(0, lds);
+  for (int n = 0; n < n_tiles; n += 2) {
+    tile(n, std::integral_constant<int, 0>{});
+    if (n + 1 < n_tiles) tile(n + 1, std::integral_constant<int, 1>{});
   }
 
   // lane = column, element i of block db is d = 32db + 8(i/4) + 4hi + i%4
