@@ -64,6 +64,15 @@
 // * Workgroups are issued longest-first (last token tiles first), and the KV
 //   head is the fastest-varying index so the workgroups of one KV head land on
 //   one XCD (blockIdx % 8) and share its L2.
+// * Long prefills run on a persistent grid instead (one workgroup per compute
+//   unit, the same items drawn from one queue per XCD, other XCDs' queues
+//   once its own is empty): the eight XCDs of one part run at different
+//   clocks under the power limit, a few percent apart, and a fixed split of
+//   the items leaves the faster ones idle at the end. While an item runs its
+//   last key tiles, the next item's first tiles load into the rings, its
+//   queries into registers.
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -93,7 +102,12 @@ __device__ __forceinline__ float max_xor32(float x) {
 // queries that arrive rotated in bf16 (QS false) the operand is the query
 // itself, since scaling it would round it a second time, and the exponents
 // are formed from the scores by one FMA each.
-template <typename T, int D, int G, bool QS>
+//
+// PERS: a persistent grid (one workgroup per compute unit) that takes its
+// items, one (sequence, KV head, query tile) each, from the work queues in
+// a.sched; while an item runs its last key tiles, the first tiles of the next
+// item already load into the rings (bf16 only).
+template <typename T, int D, int G, bool QS, bool PERS>
 __global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int TQ = kCols / G;          // tokens per workgroup
@@ -106,13 +120,72 @@ void prefill_kernel(PrefillArgs a) {
 
   // four stages: K of stage s at s TILE, V of stage s at (4 + s) TILE, so
   // every operand address is one per-lane register plus an offset below 64 KB
-  __shared__ __attribute__((aligned(1024))) char lds[8 * TILE];
+  // (persistent: a ninth tile at 8 TILE for the output, and the next item's
+  // index after it)
+  static_assert(!PERS || std::is_same<T, __bf16>::value, "persistent grid: bf16 only");
+  __shared__ __attribute__((aligned(1024))) char lds[PERS ? 9 * TILE + 512 : 8 * TILE];
+  int* const sh_next = reinterpret_cast<int*>(lds + 9 * TILE);
+  // (persistent) per wave, the next item's K and V bases, first key and tile
+  // count: kept in LDS rather than in scalar registers through the key loop,
+  // and read back by the iterations that load the next item's tiles
+  struct NextItem {
+    const T* kb;
+    const T* vb;
+    int kvlo, nt;
+  };
+  auto uniform_ptr = [](const T* p) __attribute__((always_inline)) {
+    const uint64_t x = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+  };
 
-  const int tid = threadIdx.x;
+  // Work items: item = (qtiles from the last, sequence, KV head), KV head
+  // fastest, so that longer items come first. Without PERS workgroup i runs
+  // item i. With PERS workgroup i runs item i first; the items congruent to x
+  // mod 8 form queue x, and a workgroup draws further items from queue
+  // blockIdx % 8 (the workgroups of one XCD, sharing one L2), then from the
+  // other queues once its own is empty. Counter x of a.sched counts the draws
+  // on queue x past the items the grid started with; counter 8 counts the
+  // workgroups that found every queue empty, and the last of them sets all
+  // nine back to zero for the next launch on the stream.
+  const int n_items = a.B * a.Hkv * a.n_qtiles;
+  int item = blockIdx.x;
+  int ph_c = 0;              // ring stage of the item's tile 0 (PERS)
+  int kpf_c = 3, vpf_c = 2;  // the item's own start loads K tiles j < kpf_c and V tiles j < vpf_c
+  // the item's offsets row (one entry per lane) and raw queries, loaded
+  // before the item starts (PERS)
+  int cu_n = 0;
+  bf16x8 qn[D / 16];
+  // offsets row of sequence bb, one entry per lane
+  auto load_cu = [&](int bb) __attribute__((always_inline)) {
+    return a.cu_docs[(int64_t)bb * (a.n_docs + 1) + min((int)threadIdx.x & 63, a.n_docs)];
+  };
+  // raw queries of this lane's column of item (bb, hh, qt)
+  auto load_q = [&](int bb, int hh, int qt) __attribute__((always_inline)) {
+    const int lc = threadIdx.x & 31, hi = (threadIdx.x >> 5) & 1;
+    const int col = (int)(threadIdx.x >> 6) * 32 + lc;
+    const int t = min(qt * TQ + col / G, a.Sq - 1);
+    const T* qp = static_cast<const T*>(a.q) + bb * a.qs_b + t * a.qs_s + (hh * G + col % G) * a.qs_h + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qn[ks] = load8(qp + 16 * ks);
+  };
+  if constexpr (PERS) {
+    const int h0 = item % a.Hkv, r0 = item / a.Hkv;
+    if (a.cu_docs && a.n_docs < 64) cu_n = load_cu(r0 % a.B);
+    load_q(r0 % a.B, h0, a.n_qtiles - 1 - r0 / a.B);
+  }
+
+  for (;;) {
+  // (persistent) the thread index passes through an empty asm at the top of
+  // every item, so that what is derived from it is formed inside the item
+  // instead of hoisted out of the loop and held, or spilled, across it
+  int zz = 0;
+  if constexpr (PERS) asm volatile("" : "+v"(zz));
+  const int tid = (int)threadIdx.x + zz;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lc = lane & 31, hi = lane >> 5;
-
-  const int bid = blockIdx.x;
+  const int bid = item;
   const int kvh = bid % a.Hkv;
   const int r = bid / a.Hkv;
   const int b = r % a.B;
@@ -165,7 +238,8 @@ void prefill_kernel(PrefillArgs a) {
     w_smax = doc_start(cu, n_docs, w_tmax + qo);
   }
   int cu_l = 0;
-  if (docs_in_lanes) cu_l = cu[min(lane, n_docs)];
+  if constexpr (PERS) cu_l = cu_n;
+  else if (docs_in_lanes) cu_l = cu[min(lane, n_docs)];
 
   // ---- Q operand (B of S^T = K Q^T): Q[col][16ks + 8hi + i] ----------------
   // Columns past the sequence end load the last token's row (no branch, so
@@ -181,7 +255,22 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
     const T* qp = qbase + min(tok[cb], Sq - 1) * a.qs_s + head[cb] * a.qs_h + 8 * hi;
-    if constexpr (QS) {
+    if constexpr (PERS) {
+      // loaded before the item started
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (QS) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qraw[cb][ks][i] = (float)qn[ks][i];
+          if (!rope_q) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qreg[cb][ks][i] = to_bf16(qraw[cb][ks][i] * qscale);
+          }
+        } else {
+          qreg[cb][ks] = qn[ks];
+        }
+      }
+    } else if constexpr (QS) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) load8_f32(qp + 16 * ks, qraw[cb][ks]);
       if (!rope_q) {
@@ -220,7 +309,7 @@ void prefill_kernel(PrefillArgs a) {
   // [0, t0 + qo]
   int kv_lo = max(k_off, max(0, min(kv_start, t0 + qo)));
   const int kv_hi = min(kend - 1, t_end - 1 + qo);
-  if (kv_lo > kv_hi) {
+  if (!PERS && kv_lo > kv_hi) {
     // no key of this shard is visible to any of the tile's rows (ring step):
     // the first step of an accumulation still starts the rows at o = 0,
     // lse = -inf
@@ -250,7 +339,7 @@ void prefill_kernel(PrefillArgs a) {
   // its unused slots mark them lse_part = -inf. Nothing has touched LDS yet.
   const int sp = blockIdx.y;
   int n_split = 1;
-  if (a.split_tiles > 0) {
+  if (!PERS && a.split_tiles > 0) {
     n_split = (n_tiles + a.split_tiles - 1) / a.split_tiles;
     if (sp >= n_split) {
       if (n_split > 1 && hi == 0)
@@ -293,8 +382,7 @@ void prefill_kernel(PrefillArgs a) {
   // at or past kend read as zero. bf16: this wave's NL direct-to-LDS loads,
   // tracked by vmcnt; fp32: converted to bf16 through registers and written
   // with ds_write (complete once lgkmcnt drains).
-  auto stage_kv = [&](int kt, char* dst, bool is_v) __attribute__((always_inline)) {
-    const T* base = is_v ? vbase : kbase;
+  auto stage_kv_b = [&](const T* base, int kt, char* dst, bool is_v) __attribute__((always_inline)) {
     const int64_t ss = is_v ? a.vs_s : a.ks_s;
     if constexpr (std::is_same<T, __bf16>::value) {
       const int64_t rows = max(kend - kt, 0);
@@ -313,9 +401,128 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
   };
+  auto stage_kv = [&](int kt, char* dst, bool is_v) __attribute__((always_inline)) {
+    stage_kv_b(is_v ? vbase : kbase, kt, dst, is_v);
+  };
   // tile k's key position; tiles past the last one load nothing (zero rows),
   // so every wave has the same loads in flight at every wait
   auto tile_kt = [&](int k) __attribute__((always_inline)) { return k < n_tiles ? kv_lo + k * kKT : kend; };
+  // The next item (PERS): its index nx (-1: none), and once nx_ok its key
+  // range (nkvlo, nnt tiles) and K/V bases. Tile k >= n_tiles of this item's
+  // stream is then the next item's tile k - n_tiles: the loads past this
+  // item's last tile fetch the next item's first tiles, into the ring stages
+  // that item will read them from.
+  // (nt = 0 until the next item is known)
+  NextItem* const nxi = reinterpret_cast<NextItem*>(lds + 9 * TILE + 64) + wave;
+  if (PERS && lane == 0) nxi->nt = 0;
+
+  // ---- the next item (PERS) ------------------------------------------------------
+  // A workgroup draws its next item when the current one starts, settles the
+  // draw at the item's first barrier (once its start loads have landed),
+  // loads the next item's offsets row before iteration 0 issues its tiles,
+  // and forms the next item's key range after B(0): from tile 1 on, the loads
+  // past this item's last tile fetch the next item's first tiles. (Drawing
+  // at the start holds one item ahead; the host takes the persistent grid
+  // only where the items are many per workgroup, so that this costs little
+  // balance.) These steps read the kernel arguments through a pointer the
+  // compiler cannot follow, so that it loads them where they are used
+  // instead of holding them in scalar registers through the key loop.
+  unsigned tk = 0;
+  auto kargs = []() __attribute__((always_inline)) {
+    auto p = (const __attribute__((address_space(4))) PrefillArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(p));
+    return p;
+  };
+  auto draw = [&]() __attribute__((always_inline)) {
+    if (wave == 0 && lane == 0)
+      tk = __hip_atomic_fetch_add((__attribute__((address_space(1))) unsigned*)(kargs()->sched + (blockIdx.x & 7)), 1u,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // (wave 0) the draw's item, or one taken from another queue once this
+  // queue is empty, or -1, into sh_next; a barrier must follow
+  auto resolve = [&]() __attribute__((always_inline)) {
+    if (wave == 0) {
+      if (lane == 0) {
+        const auto A = kargs();
+        unsigned* const sched = A->sched;
+        auto ctr = [&](int y) __attribute__((always_inline)) {
+          return (__attribute__((address_space(1))) unsigned*)(sched + y);
+        };
+        const int n_it = A->B * A->Hkv * A->n_qtiles;
+        const int grid = min(n_it, A->pgrid), home = (int)(blockIdx.x & 7);
+        auto started = [&](int y) __attribute__((always_inline)) { return (unsigned)((grid - y + 7) >> 3); };
+        auto queued = [&](int y) __attribute__((always_inline)) { return (unsigned)((n_it - y + 7) >> 3); };
+        int nxt = -1;
+        const unsigned v = tk + started(home);
+        if (v < queued(home)) {
+          nxt = (int)(v * 8 + home);
+        } else {
+          for (int s2 = 1; s2 < 8 && nxt < 0; ++s2) {
+            const int y = (home + s2) & 7;
+            const unsigned w = __hip_atomic_fetch_add(ctr(y), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + started(y);
+            if (w < queued(y)) nxt = (int)(w * 8 + y);
+          }
+          if (nxt < 0 &&
+              __hip_atomic_fetch_add(ctr(8), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)grid - 1) {
+            for (int y = 0; y < 9; ++y) __hip_atomic_store(ctr(y), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        *sh_next = nxt;
+      }
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+    }
+  };
+  // (after that barrier) the next item's offsets row
+  auto fetch_next = [&]() __attribute__((always_inline)) {
+    const auto A = kargs();
+    const int nx = __builtin_amdgcn_readfirstlane(*sh_next);
+    if (A->cu_docs && A->n_docs < 64)
+      cu_n = A->cu_docs[(int64_t)(max(nx, 0) / A->Hkv % A->B) * (A->n_docs + 1) + min(lane, A->n_docs)];
+  };
+  // (once the row has landed) the next item's key range and K/V bases, into
+  // this wave's slot: the loads past this item's last tile fetch its first
+  // tiles from here on
+  auto publish_next = [&]() __attribute__((always_inline)) {
+    const auto A = kargs();
+    const int nx = __builtin_amdgcn_readfirstlane(*sh_next);
+    if (nx >= 0) {
+      const int nkv = nx % A->Hkv, nr = nx / A->Hkv, nbb = nr % A->B;
+      const int q0 = A->q_off, nd = A->n_docs;
+      const int nt0 = (A->n_qtiles - 1 - nr / A->B) * TQ;
+      int nst = 0;
+      if (A->cu_docs && nd < 64) {
+        const unsigned long long mk = __ballot(lane < nd && cu_n <= nt0 + q0);
+        nst = __builtin_amdgcn_readlane(cu_n, mk ? 63 - __clzll(mk) : 0);
+      } else if (A->cu_docs) {
+        nst = doc_start(A->cu_docs + (int64_t)nbb * (nd + 1), nd, nt0 + q0);
+      }
+      const int nkvlo = max(0, min(nst, nt0 + q0));
+      if (lane == 0) {
+        nxi->kb = static_cast<const T*>(A->k) + nbb * A->ks_b + nkv * A->ks_h;
+        nxi->vb = static_cast<const T*>(A->v) + nbb * A->vs_b + nkv * A->vs_h;
+        nxi->kvlo = nkvlo;
+        nxi->nt = (min(A->k_off + A->S - 1, min(nt0 + TQ, A->Sq) - 1 + q0) - nkvlo) / kKT + 1;
+      }
+    }
+  };
+  if (PERS) draw();
+  auto stage_c = [&](int k, char* dst, bool is_v) __attribute__((always_inline)) {
+    if constexpr (PERS) {
+      if (k >= n_tiles) {
+        const int nnt = __builtin_amdgcn_readfirstlane(nxi->nt);
+        const int j = k - n_tiles;
+        if (j < nnt)
+          stage_kv_b(uniform_ptr(is_v ? nxi->vb : nxi->kb), __builtin_amdgcn_readfirstlane(nxi->kvlo) + j * kKT, dst,
+                     is_v);
+        else
+          stage_kv(kend, dst, is_v);
+      } else {
+        stage_kv(tile_kt(k), dst, is_v);
+      }
+    } else {
+      stage_kv(tile_kt(k), dst, is_v);
+    }
+  };
 
   // ---- per-lane LDS operand offsets ------------------------------------------
   // K operand: row 32kb + lc, logical chunk 2ks + hi.
@@ -369,6 +576,11 @@ void prefill_kernel(PrefillArgs a) {
   static_assert(PF <= NQ && PF <= NP && EQ % 2 == 0, "pipeline shape");
   char* const kst[4] = {lds, lds + TILE, lds + 2 * TILE, lds + 3 * TILE};
   char* const vst[4] = {lds + 4 * TILE, lds + 5 * TILE, lds + 6 * TILE, lds + 7 * TILE};
+  // stages of the item's tile j (the ring position of tile 0 rotates from
+  // item to item in a persistent workgroup)
+  const int ph = PERS ? ph_c : 0;
+  auto kst_at = [&](int j) __attribute__((always_inline)) { return lds + ((ph + j) & 3) * TILE; };
+  auto vst_at = [&](int j) __attribute__((always_inline)) { return lds + (4 + ((ph + j) & 3)) * TILE; };
 
   // exponents t of tile j in tA (j even) or tB (j odd): element e = 16 kb + i
   // is element i of key block kb's t^T accumulator
@@ -546,40 +758,46 @@ void prefill_kernel(PrefillArgs a) {
     if (masked) mask_tile(k, tc);
     // (issued here rather than before the PV: the register allocator then
     // keeps every operand in registers; issued earlier they measured no faster)
-    stage_kv(tile_kt(k + 3), kdst, false);
-    stage_kv(tile_kt(k + 2), vdst, true);
+    stage_c(k + 3, kdst, false);
+    stage_c(k + 2, vdst, true);
     phase_qk(knext, vcur - 4 * TILE, tn, tc);
   };
   // Iteration 0: the loads of K3 and V2, QK of tile 0 (its operands read
   // here), the scale FMA and mask of tile 0, the first K1 operands, then QK(1)
   // with the weights of tile 0.
-  auto iter0 = [&](char* __restrict__ kdst, char* __restrict__ vdst, const char* __restrict__ k0,
+  // (P: tile 0's exponents go to tB instead of tA, for a ring position of odd
+  // parity)
+  auto iter0 = [&](auto P, char* __restrict__ kdst, char* __restrict__ vdst, const char* __restrict__ k0,
                    const char* __restrict__ k1, const char* __restrict__ v0) __attribute__((always_inline)) {
+    f32x16(&t0)[2] = decltype(P)::value ? tB : tA;
+    f32x16(&t1)[2] = decltype(P)::value ? tA : tB;
     const bool masked = needs_mask(0);
-    stage_kv(tile_kt(3), kdst, false);
-    stage_kv(tile_kt(2), vdst, true);
+    stage_c(3, kdst, false);
+    stage_c(2, vdst, true);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) kbuf[i] = rd_k(k0, i);
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) tA[i / KS] = mfma32(kbuf[i], qreg[0][i % KS], i % KS == 0 ? negMv : tA[i / KS]);
+    for (int i = 0; i < NQ; ++i) t0[i / KS] = mfma32(kbuf[i], qreg[0][i % KS], i % KS == 0 ? negMv : t0[i / KS]);
     // (no PV precedes tile 0: its scale FMA (without QS) and mask run on
     // their own)
     if constexpr (!QS) {
 #pragma unroll
-      for (int e = 0; e < 32; ++e) tA[e >> 4][e & 15] = fmaf(tA[e >> 4][e & 15], a.scale_log2, negM);
+      for (int e = 0; e < 32; ++e) t0[e >> 4][e & 15] = fmaf(t0[e >> 4][e & 15], a.scale_log2, negM);
     }
-    if (masked) mask_tile(0, tA);
+    if (masked) mask_tile(0, t0);
 #pragma unroll
     for (int i = 0; i < PF; ++i) kbuf[i] = rd_k(k1, i);
-    phase_qk(k1, v0 - 4 * TILE, tB, tA);
+    phase_qk(k1, v0 - 4 * TILE, t1, t0);
   };
 
   // ---- prologue loads: K0, K1, V0, K2, V1 (K and V stage 3 hold the RoPE table) --
-  stage_kv(tile_kt(0), kst[0], false);
-  stage_kv(tile_kt(1), kst[1], false);
-  stage_kv(tile_kt(0), vst[0], true);
-  stage_kv(tile_kt(2), kst[2], false);
-  stage_kv(tile_kt(1), vst[1], true);
+  // (those the previous item of a persistent workgroup has not loaded)
+  const int kpf = PERS ? kpf_c : 3, vpf = PERS ? vpf_c : 2;
+  if (kpf > 0) stage_c(0, kst_at(0), false);
+  if (kpf > 1) stage_c(1, kst_at(1), false);
+  if (vpf > 0) stage_c(0, vst_at(0), true);
+  if (kpf > 2) stage_c(2, kst_at(2), false);
+  if (vpf > 1) stage_c(1, vst_at(1), true);
   if (QS && rope_q) {
     // RoPE of this lane's query channels 16ks + 8hi + 0..7, i.e. the pairs
     // k = 8ks + 4hi + p (adjacent pairs (2k, 2k+1)) or, for half-split pairs
@@ -625,15 +843,18 @@ void prefill_kernel(PrefillArgs a) {
           sv[p] = __builtin_amdgcn_sinf(fr);
         }
         const int off = tt * ROW + 16 * (c ^ (tt & (CH - 1)));
-        *reinterpret_cast<f32x4*>(lds + 3 * TILE + off) = cv;
-        *reinterpret_cast<f32x4*>(lds + 7 * TILE + off) = sv;
+        *reinterpret_cast<f32x4*>(kst_at(3) + off) = cv;
+        *reinterpret_cast<f32x4*>(vst_at(3) + off) = sv;
       }
-      __syncthreads();
+      // the table's writes are LDS only: the barrier waits for them, not for
+      // the tile loads in flight (__syncthreads would wait for those too)
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
         const int tt = (wave * 32 * kCB + cb * 32 + lc) / G;
         auto tab = [&](int c, int which) __attribute__((always_inline)) {   // 4 pairs from chunk c
-          return *reinterpret_cast<const f32x4*>(lds + (which ? 7 : 3) * TILE + tt * ROW +
+          return *reinterpret_cast<const f32x4*>((which ? vst_at(3) : kst_at(3)) + tt * ROW +
                                                   16 * (c ^ (tt & (CH - 1))));
         };
         if (a.rope_half) {
@@ -688,17 +909,33 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
   }
-  sync_tiles();   // K0, K1, V0 landed; every wave is done with the RoPE table
-  iter0(kst[3], vst[2], kst[0], kst[1], vst[0]);
-  settle(tA, tB);
+  if constexpr (PERS) {
+    // every load of the item's start has landed (and the previous item's
+    // stores, and the draw); the next item's offsets row is loaded before
+    // iteration 0 issues its tiles, so that B(0) covers it
+    __builtin_amdgcn_s_waitcnt(0);
+    resolve();
+    __builtin_amdgcn_s_barrier();
+    fetch_next();
+  } else {
+    sync_tiles();   // K0, K1, V0 landed; every wave is done with the RoPE table
+  }
+  if (!PERS || (ph & 1) == 0) {
+    iter0(std::integral_constant<int, 0>{}, kst_at(3), vst_at(2), kst_at(0), kst_at(1), vst_at(0));
+    settle(tA, tB);
+  } else {
+    iter0(std::integral_constant<int, 1>{}, kst_at(3), vst_at(2), kst_at(0), kst_at(1), vst_at(0));
+    settle(tB, tA);
+  }
   sync_tiles();   // B(0)
+  if (PERS) publish_next();
   // Unrolled over the four stage indices so every stage offset is a constant.
   // The loop has one exit: steps at or past the last tile are skipped by a
   // uniform branch that rejoins (an exit after every unrolled step keeps the
   // register allocator from merging the accumulators' copies).
   auto step = [&](auto U, int k) __attribute__((always_inline)) {
-    constexpr int u = decltype(U)::value;   // k % 4
-    if (k < n_tiles) {
+    constexpr int u = decltype(U)::value;   // ring stage of tile k: (ph + k) % 4
+    if (k < n_tiles && (!PERS || k >= 1)) {
       // exponents of tile k in tA (k even) or tB; tile k+1's go to the other
       f32x16(&tc)[2] = (u & 1) ? tB : tA;
       f32x16(&tn)[2] = (u & 1) ? tA : tB;
@@ -707,20 +944,30 @@ void prefill_kernel(PrefillArgs a) {
       sync_tiles();   // B(k)
     }
   };
-  for (int k = 1; k < n_tiles; k += 4) {
+  for (int k = 1 - ph; k < n_tiles; k += 4) {
     step(std::integral_constant<int, 1>{}, k);
     step(std::integral_constant<int, 2>{}, k + 1);
     step(std::integral_constant<int, 3>{}, k + 2);
     step(std::integral_constant<int, 0>{}, k + 3);
   }
-  // PV of the last tile, from V stage (n_tiles - 1) % 4
-  switch ((n_tiles - 1) & 3) {
+  // PV of the last tile, from V stage (ph + n_tiles - 1) % 4
+  switch ((ph + n_tiles - 1) & 3) {
     case 0: phase_pv_last(vst[0] - 4 * TILE); break;
     case 1: phase_pv_last(vst[1] - 4 * TILE); break;
     case 2: phase_pv_last(vst[2] - 4 * TILE); break;
     default: phase_pv_last(vst[3] - 4 * TILE); break;
   }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));          // loads past the last tile
+  if constexpr (PERS) {
+    // the next item's queries, while this one's output is written (the
+    // loads past the last tile, the next item's first tiles, stay in flight)
+    // (unconditional, so that the registers are not live across the item:
+    // with no next item this item's queries are fetched again, unused)
+    const int nx = __builtin_amdgcn_readfirstlane(*sh_next);
+    const int nr = nx / a.Hkv;
+    load_q(nx >= 0 ? nr % a.B : b, nx >= 0 ? nx % a.Hkv : kvh, nx >= 0 ? a.n_qtiles - 1 - nr / a.B : qtile);
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));          // loads past the last tile
+  }
 
   // ---- epilogue --------------------------------------------------------------
   // o = acc / lt as the reciprocal's product plus one residual step
@@ -742,7 +989,7 @@ void prefill_kernel(PrefillArgs a) {
   auto row_lse = [&](int cb) __attribute__((always_inline)) {
     return lt[cb] > 0.f ? (Mref + fast_log2(lt[cb])) * kLn2 : -INFINITY;
   };
-  if (a.acc_mode) {
+  if (!PERS && a.acc_mode) {
     // ring step: this shard's (o, lse) of every row, written (first step) or
     // merged by log-sum-exp weight into the fp32 accumulators (o_acc, lse_acc);
     // a workgroup owns its rows, so the read-merge-write needs no atomics
@@ -783,7 +1030,7 @@ void prefill_kernel(PrefillArgs a) {
     }
     return;
   }
-  if (n_split > 1) {
+  if (!PERS && n_split > 1) {
     // partial result of this split: fp32 o (normalised by its own row sum)
     // and lse, slot sp
 #pragma unroll
@@ -810,8 +1057,23 @@ void prefill_kernel(PrefillArgs a) {
     // back 16 contiguous bytes per lane, D/8 lanes per row. The barrier
     // orders every wave's last operand reads and LDS-direct loads before the
     // stage memory is reused; each wave then only touches its own rows.
-    __syncthreads();
     char* ow = lds + wave * 32 * ROW;
+    if constexpr (PERS) {
+      // Only the stages the next item's first tiles do not use: K stage of
+      // its tile 3, V stages of its tiles 2 and 3, and the ninth tile, two
+      // waves to a tile. The barrier orders every wave's last operand reads.
+      const int nph = (ph + n_tiles) & 3;
+      const int rg = wave >> 1;
+      char* const base = rg == 0 ? lds + ((nph + 3) & 3) * TILE
+                         : rg == 1 ? lds + (4 + ((nph + 2) & 3)) * TILE
+                         : rg == 2 ? lds + (4 + ((nph + 3) & 3)) * TILE
+                                   : lds + 8 * TILE;
+      ow = base + (wave & 1) * 32 * ROW;
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
+    } else {
+      __syncthreads();
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -854,6 +1116,27 @@ void prefill_kernel(PrefillArgs a) {
     if (a.lse) a.lse[((int64_t)b * a.Hq + head[cb]) * Sq + tok[cb]] = row_lse(cb);
     if (a.split_tiles > 0) a.lse_part[((int64_t)b * a.Hq + head[cb]) * Sq + tok[cb]] = INFINITY;
   }
+  if constexpr (PERS) {
+    const int nx = __builtin_amdgcn_readfirstlane(*sh_next);
+    if (nx < 0) {
+      __builtin_amdgcn_s_waitcnt(0);   // the loads past the last tile
+      return;
+    }
+    // every wave's output reads are done before the next item's RoPE table
+    // reuses those stages
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    __builtin_amdgcn_s_barrier();
+    // The next item starts at ring stage ph + n_tiles. The loads of
+    // iterations 1 .. n_tiles - 1 fetched its K tiles j >= 4 - n_tiles and V
+    // tiles j >= 3 - n_tiles; its start loads the others.
+    item = nx;
+    ph_c = (ph + n_tiles) & 3;
+    kpf_c = n_tiles >= 2 ? max(0, 4 - n_tiles) : 3;
+    vpf_c = n_tiles >= 2 ? max(0, 3 - n_tiles) : 2;
+  } else {
+    return;
+  }
+  }   // items
 }
 
 template <typename T, int D, int G>
@@ -863,12 +1146,22 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   // bf16 queries that arrive rotated keep their exact values (no QS); fp32
   // queries and queries the kernel rotates are scaled before their rounding
   if constexpr (std::is_same<T, __bf16>::value) {
+    if (a.sched) {
+      // persistent grid: one workgroup per compute unit (the LDS use allows
+      // no more), items drawn from the queues in a.sched
+      const unsigned pg = std::min(grid, (unsigned)a.pgrid);
+      if (!a.rope_q)
+        hipLaunchKernelGGL((prefill_kernel<T, D, G, false, true>), dim3(pg), dim3(64 * kNW), 0, st, a);
+      else
+        hipLaunchKernelGGL((prefill_kernel<T, D, G, true, true>), dim3(pg), dim3(64 * kNW), 0, st, a);
+      return hipGetLastError();
+    }
     if (!a.rope_q) {
-      hipLaunchKernelGGL((prefill_kernel<T, D, G, false>), dim3(grid, splits), dim3(64 * kNW), 0, st, a);
+      hipLaunchKernelGGL((prefill_kernel<T, D, G, false, false>), dim3(grid, splits), dim3(64 * kNW), 0, st, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((prefill_kernel<T, D, G, true>), dim3(grid, splits), dim3(64 * kNW), 0, st, a);
+  hipLaunchKernelGGL((prefill_kernel<T, D, G, true, false>), dim3(grid, splits), dim3(64 * kNW), 0, st, a);
   return hipGetLastError();
 }
 
@@ -933,6 +1226,57 @@ hipError_t launch_g(const PrefillArgs& a, int G, hipStream_t st) {
 }
 
 }  // namespace
+
+// ---- work-queue counters of the persistent grid --------------------------------
+// A file-scope device array: each device holds its own copy, zero from module
+// load. A stream gets one 128-byte slot of it on first use and keeps it:
+// launches on one stream run one after another, and each launch leaves its
+// counters at zero, so the slot needs no clearing. A stream under graph
+// capture gets none (the launch then takes one workgroup per item), so a
+// captured graph never shares a slot with calls made outside it.
+constexpr int kSchedSlots = 64;
+constexpr int kSchedWords = 32;
+static __device__ __align__(256) unsigned prefill_queues[kSchedSlots * kSchedWords];
+
+namespace {
+constexpr int kMaxSchedDevices = 64;
+std::mutex g_sched_mu;
+unsigned* g_sched_base[kMaxSchedDevices];
+hipStream_t g_sched_stream[kMaxSchedDevices][kSchedSlots];
+int g_sched_used[kMaxSchedDevices];
+}  // namespace
+
+hipError_t prefill_sched(hipStream_t st, unsigned** out) {
+  *out = nullptr;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return hipSuccess;
+  }
+  if (cs != hipStreamCaptureStatusNone) return hipSuccess;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxSchedDevices) return hipSuccess;
+  std::lock_guard<std::mutex> lock(g_sched_mu);
+  if (g_sched_base[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(prefill_queues));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_sched_base[dev] = static_cast<unsigned*>(p);
+  }
+  int slot = -1;
+  for (int i = 0; i < g_sched_used[dev]; ++i)
+    if (g_sched_stream[dev][i] == st) slot = i;
+  if (slot < 0) {
+    if (g_sched_used[dev] == kSchedSlots) return hipSuccess;   // out of slots: no persistent grid
+    slot = g_sched_used[dev]++;
+    g_sched_stream[dev][slot] = st;
+  }
+  *out = g_sched_base[dev] + slot * kSchedWords;
+  return hipSuccess;
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, int D, int G, int dt, hipStream_t st) {
   if (dt == 0) return D == 64 ? launch_g<__bf16, 64>(a, G, st) : launch_g<__bf16, 128>(a, G, st);

@@ -58,6 +58,11 @@ struct PrefillArgs {
   int k_off, acc_mode;
   float* o_acc;
   float* lse_acc;
+  // persistent grid (bf16, no split, no ring step): nine work-queue counters
+  // (zero between launches; the kernel leaves them zero) and the grid size;
+  // sched = null: one workgroup per work item
+  unsigned* sched;
+  int pgrid;
 };
 
 struct DecodeArgs {
@@ -134,6 +139,9 @@ hipError_t launch_rope_pair(const RopeArgs& q, const RopeArgs& k, const RopeAngl
                             hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int D, int G, int dt, hipStream_t st);
 hipError_t launch_prefill_merge(const PrefillArgs& a, int D, int dt, hipStream_t st);
+// The work-queue counters of the persistent prefill grid for launches on
+// stream st (null: launch one workgroup per item instead).
+hipError_t prefill_sched(hipStream_t st, unsigned** sched);
 // Sequences per gqa_decode call (the kernel keeps per-sequence tables in LDS).
 constexpr int kDecodeMaxBatch = 1024;
 // Waves per workgroup of the persistent decode grid (one workgroup per CU).

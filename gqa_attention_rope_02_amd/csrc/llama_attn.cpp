@@ -70,6 +70,26 @@ bool debug_mode() {
   return e != nullptr && e[0] == '1' && e[1] == '\0';
 }
 
+// The persistent prefill grid for n_items work items: one workgroup per
+// compute unit where the items number at least kPersistentItemsPerCu per
+// compute unit (a persistent workgroup draws its next item when the current
+// one starts, which costs balance where each workgroup runs only a few
+// items), else 0 (one workgroup per item). LLAMA_ATTN_PERSISTENT, when it
+// holds a number, overrides this: 0 turns the persistent grid off, n > 0 sets
+// it to n workgroups wherever the items outnumber them (so that small
+// problems run many items per workgroup).
+constexpr long long kPersistentItemsPerCu = 16;
+int persistent_grid(long long n_items) {
+  const char* e = std::getenv("LLAMA_ATTN_PERSISTENT");
+  if (e != nullptr && e[0] != '\0') {
+    char* end = nullptr;
+    const long n = std::strtol(e, &end, 10);
+    if (end != e && *end == '\0' && n >= 0 && n <= 65535) return n_items > n ? (int)n : 0;
+  }
+  const int ncu = current_cu_count();
+  return n_items >= kPersistentItemsPerCu * ncu ? ncu : 0;
+}
+
 bool fetch_i32(const int32_t* d, int64_t n, hipStream_t st, std::vector<int32_t>& h) {
   h.assign((size_t)std::max<int64_t>(n, 0), 0);
   if (n <= 0) return true;
@@ -317,6 +337,20 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
   a.max_splits = split_tiles ? max_splits : 1;
   a.o_part = o_part;
   a.lse_part = lse_part;
+  // bf16 without split key ranges or a ring step, with at most 63 documents
+  // per sequence, and many items per compute unit: a persistent grid that
+  // balances the items over the XCDs as they finish (the XCDs of one part
+  // run at different clocks) and loads each item's first tiles while the
+  // previous one ends
+  if (dt == LA_BF16 && split_tiles == 0 && !ring && (!cu_docs || n_docs < 64)) {
+    const int pg = persistent_grid((long long)B * Hkv * n_qtiles);
+    if (pg > 0) {
+      unsigned* sched = nullptr;
+      if (la::prefill_sched(stream, &sched) != hipSuccess) return LA_ERR_LAUNCH;
+      a.sched = sched;
+      a.pgrid = pg;
+    }
+  }
   const int dti = dt == LA_BF16 ? 0 : 1;
   const la_status st = launched(la::launch_prefill(a, D, G, dti, stream));
   if (st != LA_OK || split_tiles == 0) return st;

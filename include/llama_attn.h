@@ -26,6 +26,16 @@
  *     16 bytes' worth of elements (8 for bf16, 4 for fp32).
  *   - All work is enqueued on `stream` (0 = the null stream) and is
  *     asynchronous: no call synchronises.
+ *   - A bf16 gqa_prefill, gqa_prefill_rope or gqa_prefill_chunk with at least
+ *     16 work items (sequence x KV head x query tile) per compute unit runs
+ *     on a persistent grid: one workgroup per compute unit, taking its items
+ *     from work-queue counters the library keeps in device memory, one set
+ *     per stream for the first 64 streams of a device (any other stream, and
+ *     a stream under graph capture, gets one workgroup per item). Calls on one
+ *     stream run in order and leave the counters at zero; calls on different
+ *     streams use different counters. The environment variable
+ *     LLAMA_ATTN_PERSISTENT=0 turns the persistent grid off; a positive
+ *     number n sets it to n workgroups wherever the items outnumber them.
  *   - All argument checks are made on the host before anything is enqueued;
  *     on any error nothing is launched. Device-resident CONTENTS (document
  *     offsets, sequence lengths, positions) are the caller's contract and are

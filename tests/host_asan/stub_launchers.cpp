@@ -61,6 +61,10 @@ hipError_t launch_backward(const BwdArgs& a, int D, int G, hipStream_t) {
 namespace la {
 
 // no device: the scratch lookup fails like a runtime without a GPU would
+hipError_t prefill_sched(hipStream_t, unsigned** sched) {
+  *sched = nullptr;   // no queue counters: one workgroup per item
+  return hipSuccess;
+}
 hipError_t decode_scratch(void** ptr, size_t* bytes) {
   *ptr = nullptr;
   *bytes = 0;
