@@ -118,3 +118,43 @@ def test_persistent_grid_matches_oracle():
     Ow, Lw = orc.rope_attention(q, k, v, cu, 500000.0, None)
     H.assert_close(o, Ow)
     H.assert_lse_close(lse, Lw, "LSE")
+
+
+def test_persistent_grid_under_graph_capture():
+    """A prefill captured into a HIP graph runs one workgroup per item (a
+    stream under capture gets no queue counters); its replays equal the eager
+    persistent launch bit for bit. Eager persistent launches and
+    synchronisations run between the replays, and the output is refilled
+    outside the graph before each replay."""
+    import gqa_attention_rope_02_amd as la
+    B, S, Hq, Hkv, D = 1, 1100, 32, 8, 128
+    H.say("persistent grid and graph capture", dict(S=S))
+    dev = torch.device("cuda")
+    q, k, v = draw_prefill_inputs(B, S, Hq, Hkv, D, "bf16", 98)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    cu = torch.as_tensor(draw_cu_docs(S, 98, 5, 1), dtype=torch.int32, device=dev).reshape(1, -1)
+    _grid(13)
+    o_e, l_e = _run(_calls()["rope"], q, k, v, cu)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, S, dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        la.gqa_prefill_rope(q, k, v, o, lse, cu)   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        la.gqa_prefill_rope(q, k, v, o, lse, cu)
+    for rep in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        H.say("  replay", dict(run=rep))
+        assert torch.equal(o.cpu().view(torch.int16), o_e.view(torch.int16)), f"O differs at replay {rep}"
+        assert torch.equal(lse.cpu().view(torch.int32), l_e.view(torch.int32)), f"LSE differs at replay {rep}"
+        o2, l2 = _run(_calls()["rope"], q, k, v, cu)   # eager persistent launch between replays
+        assert torch.equal(o2.view(torch.int16), o_e.view(torch.int16))
+        assert torch.equal(l2.view(torch.int32), l_e.view(torch.int32))
