@@ -51,11 +51,19 @@ def _run(call, q, k, v, cu, Sq=None, stream=None):
     return o.cpu(), lse.cpu()
 
 
+def _positions(B, S, seed):
+    from workloads import draw_positions
+    return torch.as_tensor(draw_positions(B, S, 131071 - S, seed), dtype=torch.int32, device="cuda")
+
+
 def _calls():
     import gqa_attention_rope_02_amd as la
     return {
         # queries rotated in the kernel (the query operand carries the scale)
         "rope": lambda q, k, v, o, lse, cu: la.gqa_prefill_rope(q, k, v, o, lse, cu),
+        # the same with explicit positions and half-split pairs, no LSE output
+        "rope_pos_half": lambda q, k, v, o, lse, cu: la.gqa_prefill_rope(
+            q, k, v, o, None, cu, positions=_positions(q.shape[0], q.shape[1], 5), rope_pairing="half"),
         # queries given rotated (one FMA per score)
         "plain": lambda q, k, v, o, lse, cu: la.gqa_prefill(q, k, v, o, lse, cu),
         # the last rows of the sequence over its whole key range
@@ -71,6 +79,8 @@ CASES = [
     ("rotated queries, g=2", 1, 900, 16, 8, 128, 4, "plain", None, (7, 30)),
     ("no documents, g=4", 1, 640, 32, 8, 128, None, "rope", None, (9,)),
     ("chunk after a prefix", 1, 1300, 32, 8, 128, 3, "chunk", 500, (11,)),
+    ("g=8, positions, half pairs", 2, 600, 64, 8, 128, 4, "rope_pos_half", None, (10,)),
+    ("rotated queries, g=16, D=64", 1, 400, 128, 8, 64, 2, "plain", None, (12,)),
 ]
 
 
