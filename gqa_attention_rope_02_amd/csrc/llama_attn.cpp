@@ -309,6 +309,11 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
     if (rope_base > 0.0 && !positions_ok(positions, (int64_t)B * Sq, stream)) return LA_ERR_INVALID_ARG;
   }
 
+  // a ring step that merges (acc_mode 2) keys that all lie after the block's
+  // queries: the causal mask hides every key from every row, and the
+  // accumulators stay as they are, so nothing is launched
+  if (ring && acc_mode == 2 && (long long)k_off >= (long long)q_off + Sq) return LA_OK;
+
   la::PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.qs_b = q_strides[0]; a.qs_s = q_strides[1]; a.qs_h = q_strides[2];

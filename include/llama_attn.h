@@ -221,7 +221,10 @@ la_status gqa_prefill_split(const void* q, const void* k, const void* v, void* o
  * keys, and its log-sum-exp; o = 0 and lse = -inf where it has none) is
  * written (first != 0) or merged by log-sum-exp weight into the fp32
  * accumulators, so that after the steps over all shards they hold the
- * attention over all keys; gqa_prefill_ring_finalize turns them into o.
+ * attention over all keys; gqa_prefill_ring_finalize turns them into o. A
+ * merging step (first == 0) whose keys all lie after the block's queries
+ * (k_off >= q_off + Sq: no row sees any key) leaves the accumulators as they
+ * are and launches nothing (after the argument checks).
  *
  * q: [B, Sq, Hq, D] (rows of the query shard); k, v: [B, Skv, Hkv, D] (rows
  *   of the key shard, keys rotated at their positions); strides as in

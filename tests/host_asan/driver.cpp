@@ -81,6 +81,21 @@ int main() {
   CHECK(gqa_prefill_ring_step(fake(), fake(), fake(), (float*)fake(), (float*)fake(), LA_BF16, B, 64, 128, 64,
                               64, Hq, Hkv, D, qs, ks, ks, cu, 3, 0.f, nullptr, 0.0, 0, 0, nullptr) == LA_OK);
   CHECK(g_stub.pre.acc_mode == 2 && g_stub.pre.k_off == 64);
+  // a merging step whose keys all lie after the block's queries launches nothing
+  {
+    const int before = g_stub.prefill;
+    CHECK(gqa_prefill_ring_step(fake(), fake(), fake(), (float*)fake(), (float*)fake(), LA_BF16, B, 64, 128, 64,
+                                192, Hq, Hkv, D, qs, ks, ks, cu, 3, 0.f, nullptr, 0.0, 0, 0, nullptr) == LA_OK);
+    CHECK(g_stub.prefill == before);
+    // (the same shard as the first step still writes the accumulators)
+    CHECK(gqa_prefill_ring_step(fake(), fake(), fake(), (float*)fake(), (float*)fake(), LA_BF16, B, 64, 128, 64,
+                                192, Hq, Hkv, D, qs, ks, ks, cu, 3, 0.f, nullptr, 0.0, 0, 1, nullptr) == LA_OK);
+    CHECK(g_stub.prefill == before + 1 && g_stub.pre.acc_mode == 1);
+    // keys starting inside the block are launched
+    CHECK(gqa_prefill_ring_step(fake(), fake(), fake(), (float*)fake(), (float*)fake(), LA_BF16, B, 64, 128, 64,
+                                191, Hq, Hkv, D, qs, ks, ks, cu, 3, 0.f, nullptr, 0.0, 0, 0, nullptr) == LA_OK);
+    CHECK(g_stub.prefill == before + 2);
+  }
   CHECK(gqa_prefill_ring_finalize((float*)fake(), (float*)fake(), fake(), qs, nullptr, LA_BF16, B, 64, Hq, D,
                                   nullptr) == LA_OK);
 
