@@ -1205,6 +1205,42 @@ __global__ __launch_bounds__(256) void merge_kernel(PrefillArgs a) {
   if (a.lse && lane == 0) a.lse[((int64_t)b * a.Hq + h) * a.Sq + tok] = W > 0.f ? M + __logf(W) : -INFINITY;
 }
 
+// The ring's finalize: one fp32 accumulator slot, already normalised, so the
+// merge above reduces to o = o_acc where lse_acc > -inf (else 0) and lse =
+// lse_acc (its weight is exp(0) = 1, the same values bit for bit). D/8 lanes
+// per (sequence, query row, head), 8 values per lane; the row's lse and its o
+// are loaded together, not one after the other.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void finalize_kernel(PrefillArgs a) {
+  constexpr int LPR = D / 8;             // lanes per row
+  constexpr int RPB = 256 / LPR;         // rows per block
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;   // (b, tok, head), head fastest
+  const int lane = threadIdx.x % LPR;
+  const int64_t rows = (int64_t)a.B * a.Sq * a.Hq;
+  if (r >= rows) return;
+  const int h = (int)(r % a.Hq);
+  const int64_t bt = r / a.Hq;
+  const int tok = (int)(bt % a.Sq), b = (int)(bt / a.Sq);
+  const int64_t li = ((int64_t)b * a.Hq + h) * a.Sq + tok;
+  const float* src = a.o_part + r * D + 8 * lane;
+  const float ls = a.lse_part[li];
+  const f32x4 o0 = *reinterpret_cast<const f32x4*>(src);
+  const f32x4 o1 = *reinterpret_cast<const f32x4*>(src + 4);
+  const float keep = ls > -INFINITY ? 1.f : 0.f;
+  T* op = static_cast<T*>(a.o) + b * a.os_b + tok * a.os_s + h * a.os_h + 8 * lane;
+  store4(op, o0[0] * keep, o0[1] * keep, o0[2] * keep, o0[3] * keep);
+  store4(op + 4, o1[0] * keep, o1[1] * keep, o1[2] * keep, o1[3] * keep);
+  if (a.lse && lane == 0) a.lse[li] = ls > -INFINITY ? ls : -INFINITY;
+}
+
+template <typename T, int D>
+hipError_t launch_finalize_t(const PrefillArgs& a, hipStream_t st) {
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t rows = (int64_t)a.B * a.Sq * a.Hq;
+  hipLaunchKernelGGL((finalize_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_merge_t(const PrefillArgs& a, hipStream_t st) {
   constexpr int RPB = 256 / (D / 4);
@@ -1281,6 +1317,11 @@ hipError_t prefill_sched(hipStream_t st, unsigned** out) {
 hipError_t launch_prefill(const PrefillArgs& a, int D, int G, int dt, hipStream_t st) {
   if (dt == 0) return D == 64 ? launch_g<__bf16, 64>(a, G, st) : launch_g<__bf16, 128>(a, G, st);
   return D == 64 ? launch_g<float, 64>(a, G, st) : launch_g<float, 128>(a, G, st);
+}
+
+hipError_t launch_ring_finalize(const PrefillArgs& a, int D, int dt, hipStream_t st) {
+  if (dt == 0) return D == 64 ? launch_finalize_t<__bf16, 64>(a, st) : launch_finalize_t<__bf16, 128>(a, st);
+  return D == 64 ? launch_finalize_t<float, 64>(a, st) : launch_finalize_t<float, 128>(a, st);
 }
 
 hipError_t launch_prefill_merge(const PrefillArgs& a, int D, int dt, hipStream_t st) {

@@ -139,6 +139,8 @@ hipError_t launch_rope_pair(const RopeArgs& q, const RopeArgs& k, const RopeAngl
                             hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int D, int G, int dt, hipStream_t st);
 hipError_t launch_prefill_merge(const PrefillArgs& a, int D, int dt, hipStream_t st);
+// The ring's finalize: the fp32 accumulators (o_part, lse_part, one slot) to o and lse.
+hipError_t launch_ring_finalize(const PrefillArgs& a, int D, int dt, hipStream_t st);
 // The work-queue counters of the persistent prefill grid for launches on
 // stream st (null: launch one workgroup per item instead).
 hipError_t prefill_sched(hipStream_t st, unsigned** sched);

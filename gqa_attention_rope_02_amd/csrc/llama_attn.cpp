@@ -444,11 +444,11 @@ la_status gqa_prefill_ring_finalize(const float* o_acc, const float* lse_acc, vo
   a.o = o; a.lse = lse;
   a.os_b = o_strides[0]; a.os_s = o_strides[1]; a.os_h = o_strides[2];
   a.B = B; a.Sq = Sq; a.Hq = Hq;
-  // the accumulators are the merge's single slot
+  // the accumulators are a merge's single slot
   a.max_splits = 1;
   a.o_part = const_cast<float*>(o_acc);
   a.lse_part = const_cast<float*>(lse_acc);
-  return launched(la::launch_prefill_merge(a, D, dt == LA_BF16 ? 0 : 1, stream));
+  return launched(la::launch_ring_finalize(a, D, dt == LA_BF16 ? 0 : 1, stream));
 }
 
 }  // extern "C"
