@@ -1170,6 +1170,8 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
 // the prefill kernel; the others take M = max_s lse_s, w_s = exp(lse_s - M),
 // o = sum_s w_s o_s / sum_s w_s, lse = M + ln(sum_s w_s) over the slots with
 // lse_s > -inf.
+constexpr int kMergeSlots = 8;   // slots merged with all loads issued at once
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(PrefillArgs a) {
   constexpr int LPR = D / 4;             // lanes per row
@@ -1185,18 +1187,43 @@ __global__ __launch_bounds__(256) void merge_kernel(PrefillArgs a) {
   const float* lp = a.lse_part + ((int64_t)b * a.Hq + h) * a.Sq + tok;
   if (lp[0] == INFINITY) return;
   float M = -INFINITY;
-  for (int s = 0; s < a.max_splits; ++s) M = fmaxf(M, lp[s * slot_stride]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
-  if (M > -INFINITY) {
-    for (int s = 0; s < a.max_splits; ++s) {
-      const float ls = lp[s * slot_stride];
-      if (!(ls > -INFINITY)) continue;
-      const float w = __expf(ls - M);
-      const f32x4 o = *reinterpret_cast<const f32x4*>(
-          a.o_part + ((((int64_t)s * a.B + b) * a.Sq + tok) * a.Hq + h) * D + 4 * lane);
-      acc += w * o;
-      W += w;
+  auto o_of = [&](int s) __attribute__((always_inline)) {
+    return *reinterpret_cast<const f32x4*>(a.o_part + ((((int64_t)s * a.B + b) * a.Sq + tok) * a.Hq + h) * D +
+                                           4 * lane);
+  };
+  if (a.max_splits <= kMergeSlots) {
+    // every slot's lse and o loaded at once (an unused slot's o is whatever
+    // the workspace holds: it is selected away, never multiplied)
+    float ls[kMergeSlots];
+    f32x4 o[kMergeSlots];
+#pragma unroll
+    for (int s = 0; s < kMergeSlots; ++s) {
+      ls[s] = s < a.max_splits ? lp[s * slot_stride] : -INFINITY;
+      if (s < a.max_splits) o[s] = o_of(s);
+      M = fmaxf(M, ls[s]);
+    }
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int s = 0; s < kMergeSlots; ++s) {
+        const bool live = ls[s] > -INFINITY;
+        const float w = live ? __expf(ls[s] - M) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = live ? acc[i] + w * o[s][i] : acc[i];
+        W += w;
+      }
+    }
+  } else {
+    for (int s = 0; s < a.max_splits; ++s) M = fmaxf(M, lp[s * slot_stride]);
+    if (M > -INFINITY) {
+      for (int s = 0; s < a.max_splits; ++s) {
+        const float ls = lp[s * slot_stride];
+        if (!(ls > -INFINITY)) continue;
+        const float w = __expf(ls - M);
+        acc += w * o_of(s);
+        W += w;
+      }
     }
   }
   const float rw = W > 0.f ? 1.f / W : 0.f;
