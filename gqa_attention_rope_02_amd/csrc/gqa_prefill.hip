@@ -252,9 +252,31 @@ void prefill_kernel(PrefillArgs a) {
   float qraw[kCB][KS][8];   // the loaded queries in fp32 (QS)
   const bool rope_q = a.rope_q != 0;
   const float qscale = QS ? a.scale_log2 : 1.f;
+  auto load_queries = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const T* qp = qbase + min(tok[cb], Sq - 1) * a.qs_s + head[cb] * a.qs_h + 8 * hi;
+      if constexpr (QS) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) load8_f32(qp + 16 * ks, qraw[cb][ks]);
+        if (!rope_q) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qreg[cb][ks][i] = to_bf16(qraw[cb][ks][i] * qscale);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qreg[cb][ks] = load8(qp + 16 * ks);
+      }
+    }
+  };
+  // The pieces after the first of a split key range load their queries only
+  // once they know they have keys: most of them have none (short documents)
+  // and exit right after the document search.
+  const bool q_after_split = !PERS && a.split_tiles > 0 && blockIdx.y > 0;
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
-    const T* qp = qbase + min(tok[cb], Sq - 1) * a.qs_s + head[cb] * a.qs_h + 8 * hi;
     if constexpr (PERS) {
       // loaded before the item started
 #pragma unroll
@@ -270,20 +292,9 @@ void prefill_kernel(PrefillArgs a) {
           qreg[cb][ks] = qn[ks];
         }
       }
-    } else if constexpr (QS) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) load8_f32(qp + 16 * ks, qraw[cb][ks]);
-      if (!rope_q) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) qreg[cb][ks][i] = to_bf16(qraw[cb][ks][i] * qscale);
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qreg[cb][ks] = load8(qp + 16 * ks);
     }
   }
+  if (!PERS && !q_after_split) load_queries();
 
   if (docs_in_lanes) {
     // index of the document holding position t (the same t in every lane):
@@ -347,12 +358,13 @@ void prefill_kernel(PrefillArgs a) {
         for (int cb = 0; cb < kCB; ++cb)
           if (valid[cb])
             a.lse_part[(((int64_t)sp * a.B + b) * a.Hq + head[cb]) * Sq + tok[cb]] = -INFINITY;
-      __builtin_amdgcn_s_waitcnt(0);   // the Q loads already issued
+      __builtin_amdgcn_s_waitcnt(0);   // the Q loads already issued (first piece)
       return;
     }
     kv_lo += sp * a.split_tiles * kKT;
     n_tiles = min(a.split_tiles, n_tiles - sp * a.split_tiles);
   }
+  if (q_after_split) load_queries();
 
   // ---- online-softmax state of this lane's column ------------------------------
   // Mref: the reference the exponents are taken against, in log2 units
