@@ -59,8 +59,10 @@ constexpr int kQWaves = 8;
 constexpr int kQCols = 32 * kQWaves;     // columns per workgroup (dq kernel)
 constexpr int kKT = 64;                  // keys per tile (dq kernel)
 // key blocks with more query blocks than this are split (when a workspace
-// is given): below it the split's extra traffic outweighs the balance
-constexpr int kSplitMin = 48;
+// is given): below it the split's extra traffic and merge outweigh the
+// balance it buys (the 8B backward measured 128-256 alike, 1.5-2% faster
+// than 48, 8% faster than no split)
+constexpr int kSplitMin = 128;
 static_assert(kKvKeys == kBwdKeysPerBlock, "host and kernel disagree on the key block");
 
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }

@@ -77,8 +77,8 @@ def _check_case(B, S, Hq, Hkv, D, seed, cus, softmax_scale=0.0, workspace="nan")
     (1, 257, 8, 2, 128, 204, None),   # one document, one token past a block
     (1, 450, 128, 8, 128, 205, 4),    # 405B heads (g = 16)
     (1, 390, 16, 4, 128, 206, 6),     # many short documents
-    (1, 1500, 32, 8, 128, 210, 1),    # long query ranges cut into pieces (g = 4)
-    (1, 600, 16, 2, 64, 213, 2),      # g = 8, D = 64, cut into pieces
+    (1, 2200, 32, 8, 128, 210, 1),    # long query ranges cut into pieces (g = 4: 137 query blocks)
+    (1, 1300, 16, 2, 64, 213, 1),     # g = 8, D = 64, cut into pieces (162 query blocks)
     (1, 400, 4, 2, 128, 214, 3),      # g = 2
 ])
 def test_backward_matches_oracle(B, S, Hq, Hkv, D, seed, nd):
@@ -91,7 +91,7 @@ def test_backward_without_workspace():
     """No workspace: every key block's whole query range on one workgroup
     (the ranges here are long enough to be cut when a workspace is given)."""
     H.say("backward without workspace")
-    _check_case(1, 520, 16, 1, 128, 211, [draw_cu_docs(520, 211, 2, 6)], workspace=None)
+    _check_case(1, 1100, 16, 1, 128, 211, [draw_cu_docs(1100, 211, 2, 6)], workspace=None)
 
 
 def test_backward_empty_documents_and_explicit_scale():
