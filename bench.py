@@ -287,12 +287,26 @@ def time_chunk(st, Sq: int, steps: int, warmup: int, settle_s: float = 0.0, spli
                 gpu_ms_per_step=float(np.mean([e[0].elapsed_time(e[2]) for e in evs])))
 
 
+def ring_schedule(cu: np.ndarray, S: int, P: int, i: int):
+    """The key shards query shard i of a P-shard ring computes against, in
+    ring order (its own first, then i-1, i-2, ...). The runtime that packs the
+    documents holds their offsets cu on the host. A key shard after the query
+    shard is never seen (causal). One wholly before it is seen only by rows of
+    a document that starts before the key shard ends, and the earliest such
+    start is that of the document holding the shard's first row. The steps
+    left out would change nothing and are not launched."""
+    L = S // P
+    start = int(cu[np.searchsorted(cu, i * L, side="right") - 1])
+    return [j for j in ((i - step) % P for step in range(P)) if j == i or (j < i and start < (j + 1) * L)]
+
+
 def time_ring(st, P: int, reps: int):
     """Context-parallel attention as P devices of a ring would run it, all on
-    this GPU: the sequence in P equal shards; every query shard against every
-    key shard (its own first, then the ring order), partials merged into fp32
-    accumulators, then finalized. Queries rotated in the kernel, keys rotated
-    once beforehand (outside the timed region). Returns ms per whole ring."""
+    this GPU: the sequence in P equal shards; every query shard against the
+    key shards its rows can see (its own first, then the ring order; see
+    ring_schedule), partials merged into fp32 accumulators, then finalized.
+    Queries rotated in the kernel, keys rotated once beforehand (outside the
+    timed region). Returns ms per whole ring."""
     import torch
     import gqa_attention_rope_02_amd as la
     w = st["w"]
@@ -303,14 +317,15 @@ def time_ring(st, P: int, reps: int):
     lsa = torch.empty(w.B, w.Hq, L, dtype=torch.float32, device=dev)
     lse_blk = torch.empty(w.B, w.Hq, L, dtype=torch.float32, device=dev)
 
+    sched = [ring_schedule(st["cu"], S, P, i) for i in range(P)]
+
     def ring():
         for i in range(P):
             q0 = i * L
-            for step in range(P):
-                j = (i - step) % P
+            for n, j in enumerate(sched[i]):
                 la.gqa_prefill_ring_step(st["q"][:, q0:q0 + L], st["kr"][:, j * L:(j + 1) * L],
                                          st["v"][:, j * L:(j + 1) * L], q0, j * L, oa, lsa,
-                                         first=(step == 0), cu_docs=st["cu_d"], rope_base=w.rope_base)
+                                         first=(n == 0), cu_docs=st["cu_d"], rope_base=w.rope_base)
             la.gqa_prefill_ring_finalize(oa, lsa, st["o"][:, q0:q0 + L], lse_blk)
 
     ring()

@@ -367,9 +367,10 @@ def test_full_size_paged_decode_equals_contiguous():
 def test_full_size_ring_sampled_rows():
     """bench.py's ring: the llama405b workload as 8 devices of a context-
     parallel ring would run it (8 shards of 4096 tokens, every query shard
-    against every key shard in ring order, fp32 partials merged, then
-    finalized), all on this GPU; sampled rows (and their LSE) against the fp64
-    row oracle."""
+    against the key shards its rows can see in ring order, fp32 partials
+    merged, then finalized), all on this GPU; sampled rows (and their LSE)
+    against the fp64 row oracle."""
+    import bench
     import gqa_attention_rope_02_amd as la
     w = CONFIGS["llama405b"]
     P = 8
@@ -389,10 +390,9 @@ def test_full_size_ring_sampled_rows():
     lb = torch.empty(w.B, w.Hq, L, dtype=torch.float32, device=dev)
     for i in range(P):
         q0 = i * L
-        for step in range(P):
-            j = (i - step) % P
+        for n, j in enumerate(bench.ring_schedule(cu, S, P, i)):
             la.gqa_prefill_ring_step(qd[:, q0:q0 + L], kr[:, j * L:(j + 1) * L], vd[:, j * L:(j + 1) * L],
-                                     q0, j * L, oa, lsa, first=(step == 0), cu_docs=cu_d,
+                                     q0, j * L, oa, lsa, first=(n == 0), cu_docs=cu_d,
                                      rope_base=w.rope_base)
         la.gqa_prefill_ring_finalize(oa, lsa, o[:, q0:q0 + L], lb)
         lse[:, :, q0:q0 + L] = lb
