@@ -304,9 +304,10 @@ def time_ring(st, P: int, reps: int):
     """Context-parallel attention as P devices of a ring would run it, all on
     this GPU: the sequence in P equal shards; every query shard against the
     key shards its rows can see (its own first, then the ring order; see
-    ring_schedule), partials merged into fp32 accumulators, then finalized.
-    Queries rotated in the kernel, keys rotated once beforehand (outside the
-    timed region). Returns ms per whole ring."""
+    ring_schedule), partials merged into fp32 accumulators, the last step
+    writing the shard's output (gqa_prefill_ring_step_final). Queries rotated
+    in the kernel, keys rotated once beforehand (outside the timed region).
+    Returns ms per whole ring."""
     import torch
     import gqa_attention_rope_02_amd as la
     w = st["w"]
@@ -323,10 +324,13 @@ def time_ring(st, P: int, reps: int):
         for i in range(P):
             q0 = i * L
             for n, j in enumerate(sched[i]):
-                la.gqa_prefill_ring_step(st["q"][:, q0:q0 + L], st["kr"][:, j * L:(j + 1) * L],
-                                         st["v"][:, j * L:(j + 1) * L], q0, j * L, oa, lsa,
-                                         first=(n == 0), cu_docs=st["cu_d"], rope_base=w.rope_base)
-            la.gqa_prefill_ring_finalize(oa, lsa, st["o"][:, q0:q0 + L], lse_blk)
+                args = (st["q"][:, q0:q0 + L], st["kr"][:, j * L:(j + 1) * L], st["v"][:, j * L:(j + 1) * L],
+                        q0, j * L, oa, lsa)
+                if n == len(sched[i]) - 1:
+                    la.gqa_prefill_ring_step_final(*args, st["o"][:, q0:q0 + L], lse_blk, first=(n == 0),
+                                                   cu_docs=st["cu_d"], rope_base=w.rope_base)
+                else:
+                    la.gqa_prefill_ring_step(*args, first=(n == 0), cu_docs=st["cu_d"], rope_base=w.rope_base)
 
     ring()
     torch.cuda.synchronize()
@@ -769,7 +773,8 @@ def main():
         tr = time_ring(st3, P, 2)
         out["ring_405b"] = {
             "workload": f"405b-shape context-parallel attention, S=32768 in {P} shards of {32768 // P}: "
-                        f"all {P * P} ring steps (gqa_prefill_ring_step) and {P} finalizes on one GPU",
+                        f"each query shard's ring steps over the key shards its rows can see "
+                        f"(gqa_prefill_ring_step, the last gqa_prefill_ring_step_final) on one GPU",
             "tflops": round(fl3 / (tr * 1e-3) / 1e12, 2),
             "frac": round(fl3 / (tr * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "ms_per_ring": round(tr, 3)}

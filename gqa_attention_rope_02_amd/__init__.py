@@ -367,6 +367,41 @@ def gqa_prefill_ring_step(q, k, v, q_off: int, k_off: int, o_acc, lse_acc, first
     _check(st, "gqa_prefill_ring_step")
 
 
+def gqa_prefill_ring_step_final(q, k, v, q_off: int, k_off: int, o_acc, lse_acc, o, lse=None,
+                                first: bool = False, cu_docs=None, softmax_scale: float = 0.0,
+                                positions=None, rope_base: float = 0.0, rope_pairing: str = "adjacent"):
+    """The last step of a query shard's ring: gqa_prefill_ring_step, then the
+    final o (and lse) written directly instead of into the accumulators (as
+    gqa_prefill_ring_finalize would write them). With first=True the
+    accumulators are not used and may be None."""
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    n_docs = cu_docs.shape[-1] - 1 if cu_docs is not None else 1
+    _same_shape("gqa_prefill_ring_step_final", (k, v), (q, o))
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("gqa_prefill_ring_step_final: k/v must be [B, Skv, Hkv, D]")
+    if not first:
+        if o_acc is None or lse_acc is None or tuple(o_acc.shape) != (B, Sq, Hq, D) \
+                or tuple(lse_acc.shape) != (B, Hq, Sq) or o_acc.dtype != torch.float32 \
+                or lse_acc.dtype != torch.float32 or not o_acc.is_contiguous() \
+                or not lse_acc.is_contiguous():
+            raise ValueError("gqa_prefill_ring_step_final: accumulators must be contiguous fp32 "
+                             "[B, Sq, Hq, D] and [B, Hq, Sq]")
+    if lse is not None and tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("gqa_prefill_ring_step_final: lse must be [B, Hq, Sq]")
+    if cu_docs is not None and (cu_docs.dim() != 2 or cu_docs.shape[0] != B):
+        raise ValueError("gqa_prefill_ring_step_final: cu_docs must be [B, n_docs + 1]")
+    if positions is not None and tuple(positions.shape) != (B, Sq):
+        raise ValueError("gqa_prefill_ring_step_final: positions must be [B, Sq]")
+    _same_dtype("gqa_prefill_ring_step_final", q.dtype, k=k, v=v, o=o)
+    st = _lib.load().gqa_prefill_ring_step_final(
+        _dev(q), _dev(k), _dev(v), None if first else _dev(o_acc), None if first else _dev(lse_acc),
+        _dev(o), _strides(o, 3), _f32c(lse), _dtype(q), B, Sq, int(q_off), Skv, int(k_off), Hq, Hkv, D,
+        _strides(q, 3), _strides(k, 3), _strides(v, 3), _i32(cu_docs), n_docs, float(softmax_scale),
+        _i32(positions), float(rope_base), _pairing(rope_pairing), int(bool(first)), _stream())
+    _check(st, "gqa_prefill_ring_step_final")
+
+
 def gqa_prefill_ring_finalize(o_acc, lse_acc, o, lse=None):
     B, Sq, Hq, D = o.shape
     if tuple(o_acc.shape) != (B, Sq, Hq, D) or tuple(lse_acc.shape) != (B, Hq, Sq):

@@ -40,6 +40,9 @@ SIGNATURES = {
     "gqa_prefill_ring_step": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                                _c_i64_p, _c_i64_p, _c_i64_p, _vp, _i, ctypes.c_float, _vp,
                                ctypes.c_double, _i, _i, _vp], _i),
+    "gqa_prefill_ring_step_final": ([_vp, _vp, _vp, _vp, _vp, _vp, _c_i64_p, _vp, _i, _i, _i, _i, _i,
+                                     _i, _i, _i, _i, _c_i64_p, _c_i64_p, _c_i64_p, _vp, _i,
+                                     ctypes.c_float, _vp, ctypes.c_double, _i, _i, _vp], _i),
     "gqa_prefill_ring_finalize": ([_vp, _vp, _vp, _c_i64_p, _vp, _i, _i, _i, _i, _i, _vp], _i),
     "gqa_decode": ([_vp, _c_i64_p, _vp, _vp, _c_i64_p, _vp, _i, _i, _i, _i, _i, _i, _i,
                     ctypes.c_float, _vp, _vp, _vp], _i),

@@ -323,8 +323,28 @@ void prefill_kernel(PrefillArgs a) {
   if (!PERS && kv_lo > kv_hi) {
     // no key of this shard is visible to any of the tile's rows (ring step):
     // the first step of an accumulation still starts the rows at o = 0,
-    // lse = -inf
-    if (a.acc_mode == 1) {
+    // lse = -inf; a last step writes the rows' final o and lse from the
+    // accumulators (or, also the first, o = 0 and lse = -inf)
+    if (a.ring_out) {
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) {
+        if (!valid[cb]) continue;
+        const float* ap = a.o_acc + (((int64_t)b * Sq + tok[cb]) * a.Hq + head[cb]) * D;
+        T* op = static_cast<T*>(a.o) + b * a.os_b + tok[cb] * a.os_s + head[cb] * a.os_h;
+        const int64_t li = ((int64_t)b * a.Hq + head[cb]) * Sq + tok[cb];
+        const float ls = a.acc_mode == 3 ? a.lse_acc[li] : -INFINITY;
+        const float keep = ls > -INFINITY ? 1.f : 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) {
+            const int d = db * 32 + 8 * jq + 4 * hi;
+            const f32x4 x = a.acc_mode == 3 ? *reinterpret_cast<const f32x4*>(ap + d) : f32x4{0.f, 0.f, 0.f, 0.f};
+            store4(op + d, x[0] * keep, x[1] * keep, x[2] * keep, x[3] * keep);
+          }
+        if (hi == 0 && a.lse) a.lse[li] = ls;
+      }
+    } else if (a.acc_mode == 1) {
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb) {
         if (!valid[cb]) continue;
@@ -1004,7 +1024,10 @@ void prefill_kernel(PrefillArgs a) {
   if (!PERS && a.acc_mode) {
     // ring step: this shard's (o, lse) of every row, written (first step) or
     // merged by log-sum-exp weight into the fp32 accumulators (o_acc, lse_acc);
-    // a workgroup owns its rows, so the read-merge-write needs no atomics
+    // a workgroup owns its rows, so the read-merge-write needs no atomics.
+    // A last merging step (acc_mode 3) writes the merged rows as the final o
+    // and lse instead, the values the finalize would take from the
+    // accumulators (o = 0 where lse = -inf)
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
       if (!valid[cb]) continue;
@@ -1012,7 +1035,7 @@ void prefill_kernel(PrefillArgs a) {
       float* lp = a.lse_acc + ((int64_t)b * a.Hq + head[cb]) * Sq + tok[cb];
       const float ln = row_lse(cb);
       float wo = 0.f, wn = 1.f, rw = 1.f, lout = ln;
-      if (a.acc_mode == 2) {
+      if (a.acc_mode >= 2) {
         const float lo_ = *lp;
         const float mx = fmaxf(lo_, ln);
         if (mx > -INFINITY) {
@@ -1026,6 +1049,30 @@ void prefill_kernel(PrefillArgs a) {
           lout = -INFINITY;
         }
       }
+      // the accumulated row x merged with this shard's v, in one fixed order of
+      // operations for both forms of the merging step
+      auto merge4 = [&](const f32x4& x, const f32x4& v) __attribute__((always_inline)) {
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = fmaf(wo, x[e], wn * v[e]) * rw;
+        return r;
+      };
+      if (a.acc_mode == 3) {
+        T* fo = static_cast<T*>(a.o) + b * a.os_b + tok[cb] * a.os_s + head[cb] * a.os_h;
+        const float keep = lout > -INFINITY ? 1.f : 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) {
+            const int d = db * 32 + 8 * jq + 4 * hi;
+            f32x4 v = {quot(acc[db][4 * jq], cb), quot(acc[db][4 * jq + 1], cb),
+                       quot(acc[db][4 * jq + 2], cb), quot(acc[db][4 * jq + 3], cb)};
+            v = merge4(*reinterpret_cast<const f32x4*>(op + d), v);
+            store4(fo + d, v[0] * keep, v[1] * keep, v[2] * keep, v[3] * keep);
+          }
+        if (hi == 0 && a.lse) a.lse[((int64_t)b * a.Hq + head[cb]) * Sq + tok[cb]] = lout;
+        continue;
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -1033,7 +1080,7 @@ void prefill_kernel(PrefillArgs a) {
           f32x4* dst = reinterpret_cast<f32x4*>(op + db * 32 + 8 * jq + 4 * hi);
           f32x4 v = {quot(acc[db][4 * jq], cb), quot(acc[db][4 * jq + 1], cb),
                      quot(acc[db][4 * jq + 2], cb), quot(acc[db][4 * jq + 3], cb)};
-          if (a.acc_mode == 2) v = (wo * (*dst) + wn * v) * rw;
+          if (a.acc_mode == 2) v = merge4(*dst, v);
           *dst = v;
         }
       __builtin_amdgcn_s_waitcnt(0);   // both halves of the row have read lse before it changes

@@ -54,8 +54,11 @@ struct PrefillArgs {
   float* lse_part;
   // context-parallel ring step: keys at positions k_off .. k_off + S - 1;
   // acc_mode 1 writes, 2 merges this shard's (o, lse) into the fp32
-  // accumulators o_acc [B, Sq, Hq, D] and lse_acc [B, Hq, Sq]
-  int k_off, acc_mode;
+  // accumulators o_acc [B, Sq, Hq, D] and lse_acc [B, Hq, Sq]; 3 merges
+  // them and writes the final o and lse instead (the ring's last step).
+  // ring_out: the step writes the final o and lse (acc_mode 0: a first and
+  // last step, the plain prefill of the shard; acc_mode 3)
+  int k_off, acc_mode, ring_out;
   float* o_acc;
   float* lse_acc;
   // persistent grid (bf16, no split, no ring step): nine work-queue counters

@@ -261,9 +261,12 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
                        const int32_t* positions, double rope_base, int rope_pairing,
                        hipStream_t stream, int split_tiles = 0, int max_splits = 0, float* o_part = nullptr,
                        float* lse_part = nullptr, bool ring = false, int q_off = 0, int k_off = 0,
-                       int acc_mode = 0, float* o_acc = nullptr, float* lse_acc = nullptr) {
+                       int acc_mode = 0, float* o_acc = nullptr, float* lse_acc = nullptr,
+                       bool ring_out = false) {
   if (!known_dtype(dt)) return LA_ERR_UNSUPPORTED;
-  if (!q || !k || !v || (!o && !ring)) return LA_ERR_INVALID_ARG;
+  // (a ring step writes o only as the ring's last step)
+  const bool has_o = !ring || ring_out;
+  if (!q || !k || !v || (!o && has_o)) return LA_ERR_INVALID_ARG;
   if (rope_pairing != 0 && rope_pairing != 1) return LA_ERR_INVALID_ARG;
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1) return LA_ERR_INVALID_ARG;
   if (Sq < 1 || (!ring && Sq > S)) return LA_ERR_INVALID_ARG;
@@ -271,15 +274,15 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
     if (q_off < 0 || k_off < 0 || (long long)q_off + Sq > 0x7fffffffLL ||
         (long long)k_off + S > 0x7fffffffLL)
       return LA_ERR_INVALID_ARG;
-    if (!o_acc || !lse_acc || !aligned16(o_acc)) return LA_ERR_INVALID_ARG;
+    if (acc_mode != 0 && (!o_acc || !lse_acc || !aligned16(o_acc))) return LA_ERR_INVALID_ARG;
   }
   if (cu_docs && n_docs < 1) return LA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return LA_ERR_INVALID_ARG;
   if (!supported_d(D) || !supported_g(Hq / Hkv)) return LA_ERR_UNSUPPORTED;
   const int es = elem_size(dt);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (!ring && !aligned16(o))) return LA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (has_o && !aligned16(o))) return LA_ERR_INVALID_ARG;
   if (!strides_ok(q_strides, 3, es) || !strides_ok(k_strides, 3, es) ||
-      !strides_ok(v_strides, 3, es) || (!ring && !strides_ok(o_strides, 3, es)))
+      !strides_ok(v_strides, 3, es) || (has_o && !strides_ok(o_strides, 3, es)))
     return LA_ERR_INVALID_ARG;
   // key/value rows of consecutive tokens may not overlap (tiles are fetched
   // with a byte range that ends at the last token's row)
@@ -313,13 +316,24 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
   // queries: the causal mask hides every key from every row, and the
   // accumulators stay as they are, so nothing is launched
   if (ring && acc_mode == 2 && (long long)k_off >= (long long)q_off + Sq) return LA_OK;
+  // the same as the ring's last step: the accumulators are the result
+  if (ring && acc_mode == 3 && (long long)k_off >= (long long)q_off + Sq) {
+    la::PrefillArgs f{};
+    f.o = o; f.lse = lse;
+    f.os_b = o_strides[0]; f.os_s = o_strides[1]; f.os_h = o_strides[2];
+    f.B = B; f.Sq = Sq; f.Hq = Hq;
+    f.max_splits = 1;
+    f.o_part = o_acc;
+    f.lse_part = lse_acc;
+    return launched(la::launch_ring_finalize(f, D, dt == LA_BF16 ? 0 : 1, stream));
+  }
 
   la::PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.qs_b = q_strides[0]; a.qs_s = q_strides[1]; a.qs_h = q_strides[2];
   a.ks_b = k_strides[0]; a.ks_s = k_strides[1]; a.ks_h = k_strides[2];
   a.vs_b = v_strides[0]; a.vs_s = v_strides[1]; a.vs_h = v_strides[2];
-  if (!ring) {
+  if (has_o) {
     a.os_b = o_strides[0]; a.os_s = o_strides[1]; a.os_h = o_strides[2];
   }
   a.cu_docs = cu_docs; a.n_docs = cu_docs ? n_docs : 1;
@@ -327,6 +341,7 @@ la_status prefill_impl(const void* q, const void* k, const void* v, void* o, flo
   a.Sq = Sq; a.q_off = ring ? q_off : S - Sq;
   a.k_off = ring ? k_off : 0;
   a.acc_mode = ring ? acc_mode : 0;
+  a.ring_out = ring && ring_out;
   a.o_acc = o_acc;
   a.lse_acc = lse_acc;
   a.n_qtiles = (int)n_qtiles;
@@ -429,6 +444,21 @@ la_status gqa_prefill_ring_step(const void* q, const void* k, const void* v, flo
                       v_strides, nullptr, cu_docs, n_docs, softmax_scale, positions, rope_base,
                       rope_pairing, stream, 0, 0, nullptr, nullptr, true, q_off, k_off,
                       first ? 1 : 2, o_acc, lse_acc);
+}
+
+la_status gqa_prefill_ring_step_final(const void* q, const void* k, const void* v, float* o_acc,
+                                      float* lse_acc, void* o, const int64_t o_strides[3], float* lse,
+                                      la_dtype dt, int B, int Sq, int q_off, int Skv, int k_off, int Hq,
+                                      int Hkv, int D, const int64_t q_strides[3],
+                                      const int64_t k_strides[3], const int64_t v_strides[3],
+                                      const int32_t* cu_docs, int n_docs, float softmax_scale,
+                                      const int32_t* positions, double rope_base, int rope_pairing,
+                                      int first, hipStream_t stream) {
+  if (!(rope_base >= 0.0) || !std::isfinite(rope_base)) return LA_ERR_INVALID_ARG;
+  return prefill_impl(q, k, v, o, lse, dt, B, Sq, Skv, Hq, Hkv, D, q_strides, k_strides,
+                      v_strides, o_strides, cu_docs, n_docs, softmax_scale, positions, rope_base,
+                      rope_pairing, stream, 0, 0, nullptr, nullptr, true, q_off, k_off,
+                      first ? 0 : 3, o_acc, lse_acc, true);
 }
 
 la_status gqa_prefill_ring_finalize(const float* o_acc, const float* lse_acc, void* o,

@@ -247,6 +247,30 @@ la_status gqa_prefill_ring_step(const void* q, const void* k, const void* v, flo
                                 hipStream_t stream);
 
 /*
+ * gqa_prefill_ring_step_final — the last step of a query shard's ring: as
+ * gqa_prefill_ring_step, but instead of updating the accumulators it writes
+ * the rows' final o (type dt, [B, Sq, Hq, D], strides o_strides) and
+ * optional lse (fp32 [B, Hq, Sq]), the values gqa_prefill_ring_step followed
+ * by gqa_prefill_ring_finalize would give, bit for bit ([P1] "4D
+ * Parallelism": context parallelism; the merge is the log-sum-exp rule of the
+ * ring steps). With first != 0 (a ring of one step) it is the shard's plain
+ * prefill and the accumulators are not touched (they may be NULL); otherwise
+ * they are read and left unspecified. A row that saw no key gets o = 0 and
+ * lse = -inf. Keys that all lie after the block's queries make it the
+ * finalize alone.
+ * Errors: those of gqa_prefill_ring_step, and those of gqa_prefill for o and
+ * its strides.
+ */
+la_status gqa_prefill_ring_step_final(const void* q, const void* k, const void* v, float* o_acc,
+                                      float* lse_acc, void* o, const int64_t o_strides[3], float* lse,
+                                      la_dtype dt, int B, int Sq, int q_off, int Skv, int k_off, int Hq,
+                                      int Hkv, int D, const int64_t q_strides[3],
+                                      const int64_t k_strides[3], const int64_t v_strides[3],
+                                      const int32_t* cu_docs, int n_docs, float softmax_scale,
+                                      const int32_t* positions, double rope_base, int rope_pairing,
+                                      int first, hipStream_t stream);
+
+/*
  * gqa_prefill_ring_finalize — o (type dt, [B, Sq, Hq, D], strides o_strides)
  * and optional lse (fp32 [B, Hq, Sq]) from the ring accumulators; a row that
  * saw no key gets o = 0 and lse = -inf.

@@ -98,6 +98,28 @@ int main() {
   }
   CHECK(gqa_prefill_ring_finalize((float*)fake(), (float*)fake(), fake(), qs, nullptr, LA_BF16, B, 64, Hq, D,
                                   nullptr) == LA_OK);
+  // the ring's last step: merges and writes o (acc_mode 3), or, also the first,
+  // is the shard's plain prefill without accumulators; keys after the block's
+  // queries make it the finalize alone
+  {
+    CHECK(gqa_prefill_ring_step_final(fake(), fake(), fake(), (float*)fake(), (float*)fake(), fake(), qs, nullptr,
+                                      LA_BF16, B, 64, 128, 64, 64, Hq, Hkv, D, qs, ks, ks, cu, 3, 0.f, nullptr,
+                                      0.0, 0, 0, nullptr) == LA_OK);
+    CHECK(g_stub.pre.acc_mode == 3 && g_stub.pre.ring_out == 1 && g_stub.pre.o != nullptr &&
+          g_stub.pre.os_s == qs[1]);
+    CHECK(gqa_prefill_ring_step_final(fake(), fake(), fake(), nullptr, nullptr, fake(), qs, nullptr, LA_BF16, B,
+                                      64, 128, 64, 128, Hq, Hkv, D, qs, ks, ks, cu, 3, 0.f, nullptr, 0.0, 0, 1,
+                                      nullptr) == LA_OK);
+    CHECK(g_stub.pre.acc_mode == 0 && g_stub.pre.ring_out == 1);
+    CHECK(gqa_prefill_ring_step_final(fake(), fake(), fake(), nullptr, nullptr, fake(), qs, nullptr, LA_BF16, B,
+                                      64, 128, 64, 64, Hq, Hkv, D, qs, ks, ks, cu, 3, 0.f, nullptr, 0.0, 0, 0,
+                                      nullptr) == LA_ERR_INVALID_ARG);
+    const int before = g_stub.prefill, merges = g_stub.merge;
+    CHECK(gqa_prefill_ring_step_final(fake(), fake(), fake(), (float*)fake(), (float*)fake(), fake(), qs, nullptr,
+                                      LA_BF16, B, 64, 128, 64, 192, Hq, Hkv, D, qs, ks, ks, cu, 3, 0.f, nullptr,
+                                      0.0, 0, 0, nullptr) == LA_OK);
+    CHECK(g_stub.prefill == before && g_stub.merge == merges + 1 && g_stub.pre_merge.max_splits == 1);
+  }
 
   // decode, paged decode, combine
   const int64_t q2[2] = {Hq * D, D};

@@ -32,7 +32,8 @@ def lib():
 def test_header_declares_every_call():
     names = declared_functions()
     for n in ("rope_qk", "gqa_prefill", "gqa_prefill_rope", "gqa_prefill_chunk", "gqa_prefill_split",
-              "gqa_prefill_ring_step", "gqa_prefill_ring_finalize", "gqa_decode", "gqa_decode_paged",
+              "gqa_prefill_ring_step", "gqa_prefill_ring_step_final", "gqa_prefill_ring_finalize",
+              "gqa_decode", "gqa_decode_paged",
               "gqa_decode_combine", "la_status_str", "la_version"):
         assert n in names
 
@@ -164,6 +165,32 @@ def ring_step(lib, base=0.0, pairing=0, **kw):
 ])
 def test_ring_step_rejects(lib, kw, status):
     assert ring_step(lib, **kw) == status
+
+
+def ring_step_final(lib, base=0.0, pairing=0, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, oa=FAKE, la=FAKE, o=FAKE, os_=S3, lse=None, dt=0, B=1, Sq=64,
+                qo=128, Skv=64, ko=0, Hq=16, Hkv=1, D=128, qs=S3, ks=S3, vs=S3, cu=None, nd=1, scale=0.0,
+                first=0)
+    args.update(kw)
+    return lib.gqa_prefill_ring_step_final(args["q"], args["k"], args["v"], args["oa"], args["la"], args["o"],
+                                           args["os_"], args["lse"], args["dt"], args["B"], args["Sq"],
+                                           args["qo"], args["Skv"], args["ko"], args["Hq"], args["Hkv"],
+                                           args["D"], args["qs"], args["ks"], args["vs"], args["cu"],
+                                           args["nd"], args["scale"], None, base, pairing, args["first"],
+                                           None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Sq=0), INVALID), (dict(Skv=0), INVALID), (dict(qo=-1), INVALID), (dict(ko=-5), INVALID),
+    (dict(oa=None), INVALID), (dict(la=None), INVALID), (dict(oa=FAKE + 4), INVALID),
+    (dict(o=None), INVALID), (dict(o=FAKE + 2), INVALID), (dict(os_=S3_BAD), INVALID),
+    (dict(o=None, first=1), INVALID), (dict(base=-1.0), INVALID), (dict(D=96), UNSUPPORTED),
+    (dict(dt=9), UNSUPPORTED), (dict(pairing=2), INVALID),
+])
+def test_ring_step_final_rejects(lib, kw, status):
+    """Host-side rejections of the ring's last step (nothing is launched):
+    the accumulators are required unless the step is also the first, o always."""
+    assert ring_step_final(lib, **kw) == status
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -368,8 +368,8 @@ def test_full_size_ring_sampled_rows():
     """bench.py's ring: the llama405b workload as 8 devices of a context-
     parallel ring would run it (8 shards of 4096 tokens, every query shard
     against the key shards its rows can see in ring order, fp32 partials
-    merged, then finalized), all on this GPU; sampled rows (and their LSE)
-    against the fp64 row oracle."""
+    merged, the last step writing the output), all on this GPU; sampled rows
+    (and their LSE) against the fp64 row oracle."""
     import bench
     import gqa_attention_rope_02_amd as la
     w = CONFIGS["llama405b"]
@@ -390,11 +390,14 @@ def test_full_size_ring_sampled_rows():
     lb = torch.empty(w.B, w.Hq, L, dtype=torch.float32, device=dev)
     for i in range(P):
         q0 = i * L
-        for n, j in enumerate(bench.ring_schedule(cu, S, P, i)):
-            la.gqa_prefill_ring_step(qd[:, q0:q0 + L], kr[:, j * L:(j + 1) * L], vd[:, j * L:(j + 1) * L],
-                                     q0, j * L, oa, lsa, first=(n == 0), cu_docs=cu_d,
-                                     rope_base=w.rope_base)
-        la.gqa_prefill_ring_finalize(oa, lsa, o[:, q0:q0 + L], lb)
+        sched = bench.ring_schedule(cu, S, P, i)
+        for n, j in enumerate(sched):
+            args = (qd[:, q0:q0 + L], kr[:, j * L:(j + 1) * L], vd[:, j * L:(j + 1) * L], q0, j * L, oa, lsa)
+            if n == len(sched) - 1:
+                la.gqa_prefill_ring_step_final(*args, o[:, q0:q0 + L], lb, first=(n == 0), cu_docs=cu_d,
+                                               rope_base=w.rope_base)
+            else:
+                la.gqa_prefill_ring_step(*args, first=(n == 0), cu_docs=cu_d, rope_base=w.rope_base)
         lse[:, :, q0:q0 + L] = lb
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()

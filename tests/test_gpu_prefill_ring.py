@@ -25,10 +25,12 @@ def _cu(cu, B=1):
     return None if cu is None else _dev(torch.as_tensor(np.asarray(cu), dtype=torch.int32).reshape(B, -1))
 
 
-def _ring(q, kr, v, cu, bounds, rope_base):
+def _ring(q, kr, v, cu, bounds, rope_base, fused=False):
     """Every query shard against every key shard (ring order starting at its
-    own shard), then finalize; q, kr, v are the whole sequence on the device,
-    bounds the shard edges. Returns O, LSE of the whole sequence on the CPU."""
+    own shard), then finalize (fused: the last step writes o and lse itself,
+    gqa_prefill_ring_step_final); q, kr, v are the whole sequence on the
+    device, bounds the shard edges. Returns O, LSE of the whole sequence on
+    the CPU."""
     import gqa_attention_rope_02_amd as la
     B, S, Hq, D = q.shape
     O = torch.full_like(q, float("nan"))
@@ -40,14 +42,19 @@ def _ring(q, kr, v, cu, bounds, rope_base):
         Sq = q1 - q0
         oa = torch.full((B, Sq, Hq, D), float("nan"), dtype=torch.float32, device=q.device)
         lsa = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=q.device)
+        o_blk = torch.full((B, Sq, Hq, D), float("nan"), dtype=q.dtype, device=q.device)
+        l_blk = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=q.device)
         for step in range(P):
             j = (i - step) % P
             k0, k1 = bounds[j], bounds[j + 1]
-            la.gqa_prefill_ring_step(q[:, q0:q1], kr[:, k0:k1], v[:, k0:k1], q0, k0, oa, lsa,
-                                     first=(step == 0), cu_docs=cud, rope_base=rope_base)
-        o_blk = torch.empty(B, Sq, Hq, D, dtype=q.dtype, device=q.device)
-        l_blk = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
-        la.gqa_prefill_ring_finalize(oa, lsa, o_blk, l_blk)
+            if fused and step == P - 1:
+                la.gqa_prefill_ring_step_final(q[:, q0:q1], kr[:, k0:k1], v[:, k0:k1], q0, k0, oa, lsa, o_blk,
+                                               l_blk, first=(step == 0), cu_docs=cud, rope_base=rope_base)
+            else:
+                la.gqa_prefill_ring_step(q[:, q0:q1], kr[:, k0:k1], v[:, k0:k1], q0, k0, oa, lsa,
+                                         first=(step == 0), cu_docs=cud, rope_base=rope_base)
+        if not fused:
+            la.gqa_prefill_ring_finalize(oa, lsa, o_blk, l_blk)
         O[:, q0:q1] = o_blk
         L[:, :, q0:q1] = l_blk
     torch.cuda.synchronize()
@@ -84,6 +91,95 @@ def test_ring_matches_oracle(S, bounds, Hq, Hkv, D, dtype, seed, nd, fused):
     Ow, Lw = orc.rope_attention(q, k, v, cu, BASE)
     H.assert_close(O, Ow)
     H.assert_lse_close(L, Lw, "LSE")
+
+
+@pytest.mark.parametrize("S,bounds,Hq,Hkv,D,dtype,seed,nd,fused", [
+    (512, [0, 128, 256, 384, 512], 32, 8, 128, "bf16", 101, 3, True),
+    (700, [0, 250, 450, 700], 16, 1, 128, "bf16", 102, 4, True),
+    (600, [0, 100, 333, 600], 8, 8, 64, "bf16", 103, 2, False),
+    (400, [0, 200, 400], 32, 2, 128, "fp32", 104, 2, True),
+    (900, [0, 300, 600, 900], 128, 8, 128, "bf16", 108, 6, True),
+])
+def test_ring_last_step_fused_equals_step_and_finalize(S, bounds, Hq, Hkv, D, dtype, seed, nd, fused):
+    """gqa_prefill_ring_step_final as each query shard's last step (a real
+    merge for the last shard, keys after the queries, so the finalize alone,
+    for the others) writes the same o and lse as the step followed by
+    gqa_prefill_ring_finalize, bit for bit."""
+    import gqa_attention_rope_02_amd as la
+    H.say("ring last step fused", dict(S=S, bounds=bounds, Hq=Hq, D=D, dtype=dtype))
+    q, k, v = draw_prefill_inputs(1, S, Hq, Hkv, D, dtype, seed)
+    cu = draw_cu_docs(S, seed, nd, 1)
+    kr = _rot(k)
+    if fused:
+        qd, rb = _dev(q), BASE
+    else:
+        qd = torch.empty_like(_dev(q))
+        la.rope_qk(_dev(q), qd, None, None, rope_base=BASE)
+        rb = 0.0
+    O0, L0 = _ring(qd, kr, _dev(v), cu, bounds, rb)
+    O1, L1 = _ring(qd, kr, _dev(v), cu, bounds, rb, fused=True)
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(O1.view(iv), O0.view(iv))
+    assert torch.equal(L1.view(torch.int32), L0.view(torch.int32))
+
+
+def test_ring_last_step_merging_a_visible_shard_equals_step_and_finalize():
+    """A last step over an earlier key shard the block's rows see (documents
+    crossing the shard edge, some rows seeing none of its keys): bit for bit
+    the step followed by the finalize, and the oracle's attention over both
+    shards."""
+    import gqa_attention_rope_02_amd as la
+    S, Hq, Hkv, D = 768, 32, 8, 128
+    H.say("ring last step over a visible shard")
+    q, k, v = draw_prefill_inputs(1, S, Hq, Hkv, D, "bf16", 109)
+    cu = np.array([0, 200, 450, 500, S], dtype=np.int32)
+    qd, kr, vd = _dev(q), _rot(k), _dev(v)
+    cud = _cu(cu)
+    outs = []
+    for fused in (False, True):
+        oa = torch.full((1, 384, Hq, D), float("nan"), dtype=torch.float32, device=qd.device)
+        lsa = torch.full((1, Hq, 384), float("nan"), dtype=torch.float32, device=qd.device)
+        o = torch.full((1, 384, Hq, D), float("nan"), dtype=qd.dtype, device=qd.device)
+        lse = torch.full((1, Hq, 384), float("nan"), dtype=torch.float32, device=qd.device)
+        la.gqa_prefill_ring_step(qd[:, 384:], kr[:, 384:], vd[:, 384:], 384, 384, oa, lsa, first=True,
+                                 cu_docs=cud, rope_base=BASE)
+        if fused:
+            la.gqa_prefill_ring_step_final(qd[:, 384:], kr[:, :384], vd[:, :384], 384, 0, oa, lsa, o, lse,
+                                           cu_docs=cud, rope_base=BASE)
+        else:
+            la.gqa_prefill_ring_step(qd[:, 384:], kr[:, :384], vd[:, :384], 384, 0, oa, lsa, first=False,
+                                     cu_docs=cud, rope_base=BASE)
+            la.gqa_prefill_ring_finalize(oa, lsa, o, lse)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    (O0, L0), (O1, L1) = outs
+    assert torch.equal(O1.view(torch.int16), O0.view(torch.int16))
+    assert torch.equal(L1.view(torch.int32), L0.view(torch.int32))
+    Ow, Lw = orc.rope_attention(q, k, v, cu, BASE, rows=np.arange(384, S))
+    H.assert_close(O1, Ow)
+    H.assert_lse_close(L1, Lw, "LSE")
+
+
+def test_ring_single_step_final_equals_gqa_prefill():
+    """A ring of one step (first and last): the shard's plain prefill, without
+    accumulators, bit for bit gqa_prefill's output."""
+    import gqa_attention_rope_02_amd as la
+    S, Hq, Hkv, D = 640, 32, 8, 128
+    H.say("ring single final step")
+    q, k, v = draw_prefill_inputs(1, S, Hq, Hkv, D, "bf16", 110)
+    cu = draw_cu_docs(S, 110, 3, 1)
+    qd, kd, vd = _dev(q), _dev(k), _dev(v)
+    qr, kr = torch.empty_like(qd), torch.empty_like(kd)
+    la.rope_qk(qd, qr, kd, kr)
+    o = torch.empty_like(qd)
+    lse = torch.empty(1, Hq, S, dtype=torch.float32, device=qd.device)
+    la.gqa_prefill(qr, kr, vd, o, lse, _cu(cu))
+    o1 = torch.full_like(qd, float("nan"))
+    l1 = torch.full((1, Hq, S), float("nan"), dtype=torch.float32, device=qd.device)
+    la.gqa_prefill_ring_step_final(qr, kr, vd, 0, 0, None, None, o1, l1, first=True, cu_docs=_cu(cu))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.cpu().view(torch.int16), o.cpu().view(torch.int16))
+    assert torch.equal(l1.cpu().view(torch.int32), lse.cpu().view(torch.int32))
 
 
 def test_ring_single_shard_equals_gqa_prefill():
